@@ -1,0 +1,158 @@
+/*
+ * EFLA reference oracle — TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, sequential fp64 CPU implementation of the Exact Flow Linear
+ * Attention recurrence. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load this library; the product path never does. It shares
+ * no code, header or constant with the GPU library.
+ *
+ * What it computes (papernotes.org note "Exact Flow Linear Attention: Exact
+ * Solution from Continuous-Time Dynamics", section 关键设计, items 1-2, and the
+ * flowchart of section 整体框架):
+ *
+ *   lambda_t = k_t . k_t                      (the only nonzero eigenvalue of k k^T)
+ *   alpha_t  = (1 - exp(-beta_t*lambda_t)) / lambda_t
+ *   S_t      = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T
+ *   o_t      = S_t^T q_t                      (read out after the update)
+ *
+ * Numerics follow the same note, section 损失函数 / 训练策略: the denominator is
+ * floored at 1e-12 and the numerator is formed as -expm1(-beta*lambda), never
+ * as 1 - exp(...). The floored lambda is used in both places (the plain reading
+ * that keeps alpha -> beta as lambda -> 0, section 关键设计 item 3).
+ *
+ * The state S is d_k x d_v, row index = key dimension (the write k v^T fixes
+ * that orientation). Heads are independent; each is run token by token.
+ *
+ * Also exposed, for tests only: the explicit-Euler coefficient (alpha = beta,
+ * the delta rule the note contrasts with, 关键设计 item 1) and the Frobenius
+ * norm of the state after every step.
+ *
+ * Parity pins live in the test suite: the worked example printed in the note
+ * (section 一个完整示例), scipy's matrix exponential of the augmented ODE
+ * matrix, a fine-step RK4 integration of dS/dt = -k k^T S + k v^T, a truncated
+ * Taylor series with scaling and squaring, mpmath alpha, limits, bounds,
+ * invariants and an independent chunked (WY/UT) evaluation.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define EFLA_ORACLE_EXACT 0
+#define EFLA_ORACLE_EULER 1
+
+/* Exact-flow coefficient with the 1e-12 floor on lambda (training-strategy
+ * section of the papernotes note; rank-1 collapse in 关键设计 item 2). */
+double efla_oracle_alpha(double beta, double lam) {
+  double lamc = lam > 1e-12 ? lam : 1e-12;
+  return -expm1(-beta * lamc) / lamc;
+}
+
+double efla_oracle_coef(int mode, double beta, double lam) {
+  if (mode == EFLA_ORACLE_EULER) return beta;
+  return efla_oracle_alpha(beta, lam);
+}
+
+/* One token on one head. S is d_k x d_v row-major, updated in place.
+ * o (length d_v) receives S_t^T q after the update. */
+void efla_oracle_step(int mode, const double* q, const double* k, const double* v,
+                      double beta, double* S, double* o, int dk, int dv) {
+  double lam = 0.0;
+  for (int i = 0; i < dk; ++i) lam += k[i] * k[i];
+  double a = efla_oracle_coef(mode, beta, lam);
+
+  /* p = S^T k, then S <- S - a k p^T + a k v^T  ==  (I - a k k^T) S + a k v^T */
+  double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (int j = 0; j < dv; ++j) p[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) p[j] += k[i] * S[(size_t)i * dv + j];
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += a * k[i] * (v[j] - p[j]);
+  free(p);
+
+  if (o) {
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * q[i];
+      o[j] = acc;
+    }
+  }
+}
+
+typedef struct {
+  int mode;
+  const double *q, *k, *v, *beta, *s0;
+  double *o, *s_final, *snorm;
+  long nh, T;
+  int dk, dv;
+  long h_begin, h_end;
+} oracle_job;
+
+static void run_head(const oracle_job* J, long h) {
+  const long T = J->T;
+  const int dk = J->dk, dv = J->dv;
+  const size_t ss = (size_t)dk * dv;
+  double* S = (double*)malloc(sizeof(double) * ss);
+  if (J->s0) memcpy(S, J->s0 + (size_t)h * ss, sizeof(double) * ss);
+  else memset(S, 0, sizeof(double) * ss);
+
+  for (long t = 0; t < T; ++t) {
+    const double* q = J->q + ((size_t)h * T + t) * dk;
+    const double* k = J->k + ((size_t)h * T + t) * dk;
+    const double* v = J->v + ((size_t)h * T + t) * dv;
+    double b = J->beta[(size_t)h * T + t];
+    double* o = J->o ? J->o + ((size_t)h * T + t) * dv : NULL;
+    efla_oracle_step(J->mode, q, k, v, b, S, o, dk, dv);
+    if (J->snorm) {
+      double n2 = 0.0;
+      for (size_t e = 0; e < ss; ++e) n2 += S[e] * S[e];
+      J->snorm[(size_t)h * T + t] = sqrt(n2);
+    }
+  }
+  if (J->s_final) memcpy(J->s_final + (size_t)h * ss, S, sizeof(double) * ss);
+  free(S);
+}
+
+static void* run_range(void* arg) {
+  const oracle_job* J = (const oracle_job*)arg;
+  for (long h = J->h_begin; h < J->h_end; ++h) run_head(J, h);
+  return NULL;
+}
+
+/*
+ * Sequential forward over nh independent heads.
+ *   q, k  [nh, T, dk]    v [nh, T, dv]    beta [nh, T]
+ *   s0    [nh, dk, dv] or NULL (zeros)
+ *   o     [nh, T, dv] or NULL          (out)
+ *   s_final [nh, dk, dv] or NULL       (out)
+ *   snorm [nh, T] or NULL              (out: ||S_t||_F after each token)
+ * nthreads <= 1 runs on the calling thread. Returns 0, or -1 on bad sizes.
+ */
+int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
+                    const double* beta, const double* s0, double* o, double* s_final,
+                    double* snorm, long nh, long T, int dk, int dv, int nthreads) {
+  if (nh < 0 || T < 0 || dk < 1 || dv < 1) return -1;
+  if (nh == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nh) nthreads = (int)nh;
+
+  oracle_job base = {mode, q, k, v, beta, s0, o, s_final, snorm, nh, T, dk, dv, 0, nh};
+  if (nthreads == 1) {
+    run_range(&base);
+    return 0;
+  }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  oracle_job* jobs = (oracle_job*)malloc(sizeof(oracle_job) * (size_t)nthreads);
+  long per = nh / nthreads, rem = nh % nthreads, h = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].h_begin = h;
+    h += per + (i < rem ? 1 : 0);
+    jobs[i].h_end = h;
+    pthread_create(&th[i], NULL, run_range, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
