@@ -1,0 +1,185 @@
+"""Exact Flow Linear Attention (EFLA) forward on MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/efla.h`` (library
+``libefla.so`` next to this file, built by ``build.py``). The functions carry
+the C entry points' names and only marshal arguments: torch provides device
+memory and the current HIP stream; every step of the computation runs in the
+library's HIP kernels. There is no fallback: if the library is missing the
+import of the binding functions raises.
+
+Method: papernotes.org note "Exact Flow Linear Attention: Exact Solution from
+Continuous-Time Dynamics" (关键设计 items 1-3; 整体框架 for the chunked WY/UT and
+recurrent forms; 损失函数 / 训练策略 for the 1e-12 floor and expm1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libefla.so")
+
+EFLA_DTYPE_F32 = 0
+EFLA_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: EFLA_DTYPE_F32, torch.bfloat16: EFLA_DTYPE_BF16}
+
+STATUS_NAMES = {
+    0: "EFLA_OK",
+    1: "EFLA_ERR_NULL_POINTER",
+    2: "EFLA_ERR_BAD_SHAPE",
+    3: "EFLA_ERR_UNSUPPORTED",
+    4: "EFLA_ERR_MISALIGNED",
+    5: "EFLA_ERR_WORKSPACE",
+    6: "EFLA_ERR_HIP",
+}
+
+SUPPORTED_HEAD_DIMS = (16, 32, 64, 128)
+SUPPORTED_CHUNKS = (16, 32, 64)
+
+
+class EflaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libefla.so`` and declare the C signatures. Raises if not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built; build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                " (hipcc, gfx950). There is no CPU fallback.")
+        lib = ctypes.CDLL(path)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.efla_fwd_chunked_workspace_bytes.restype = sz
+        lib.efla_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        lib.efla_fwd_chunked.restype = i
+        lib.efla_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         i, i, i, i, i, i, i, vp]
+        lib.efla_fwd_recurrent_step.restype = i
+        lib.efla_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        lib.efla_status_string.restype = ctypes.c_char_p
+        lib.efla_status_string.argtypes = [i]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().efla_status_string(int(status)).decode()
+
+
+def _raise(status: int):
+    if status != 0:
+        raise EflaError(status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def efla_fwd_chunked_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int, chunk: int,
+                                     dtype: torch.dtype) -> int:
+    return int(load_library().efla_fwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk,
+                                                               _DTYPES[dtype]))
+
+
+def efla_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                     s0: Optional[torch.Tensor] = None, chunk: int = 64,
+                     o: Optional[torch.Tensor] = None, s_final: Optional[torch.Tensor] = None,
+                     return_state: bool = True, stream=None
+                     ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked EFLA forward. q, k: [B,H,T,d]; v: [B,H,T,d]; beta: [B,H,T]
+    (all fp32 or all bf16, contiguous, on one GPU); s0: [B,H,d,d] fp32 or None.
+    Returns (o [B,H,T,d] in the input dtype, S_T [B,H,d,d] fp32 or None).
+    ``s_final`` may be passed (and may be ``s0`` itself to advance in place)."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    dv = v.shape[3]
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, dev)
+        if s0.shape != (B, H, d, dv):
+            raise ValueError("s0 must be [B, H, d_k, d_v]")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+    else:
+        _require(o, "o", dt, dev)
+    if s_final is None and return_state:
+        s_final = torch.empty((B, H, d, dv), dtype=torch.float32, device=dev)
+    elif s_final is not None:
+        _require(s_final, "s_final", torch.float32, dev)
+    ws_bytes = int(lib.efla_fwd_chunked_workspace_bytes(B, H, T, d, dv, chunk, _DTYPES[dt]))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    st = lib.efla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
+                              _ptr(s_final), _ptr(ws), ws_bytes, B, H, T, d, dv, int(chunk),
+                              _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
+    return o, s_final
+
+
+def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            beta: torch.Tensor, state: torch.Tensor,
+                            o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One token per head: q, k, v [B,H,d]; beta [B,H]; state [B,H,d,d] fp32,
+    advanced in place. Returns o [B,H,d] = S_t^T q_t in the input dtype."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d]")
+    B, H, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape[:2] != (B, H) or beta.shape != (B, H):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    dv = v.shape[2]
+    _require(state, "state", torch.float32, dev)
+    if state.shape != (B, H, d, dv):
+        raise ValueError("state must be [B, H, d_k, d_v]")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    else:
+        _require(o, "o", dt, dev)
+    st = lib.efla_fwd_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(state),
+                                     _ptr(o), B, H, d, dv, _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
+    return o

@@ -1,0 +1,108 @@
+/*
+ * efla.h — C ABI of the MI355X (gfx950) Exact Flow Linear Attention forward.
+ *
+ * The operation (papernotes.org note "Exact Flow Linear Attention: Exact
+ * Solution from Continuous-Time Dynamics"):
+ *   - section 关键设计 item 2: with lambda_t = ||k_t||^2, the exact-flow
+ *     coefficient alpha_t = (1 - exp(-beta_t lambda_t)) / lambda_t and the
+ *     update S_t = (I - alpha_t k_t k_t^T) S_{t-1} + alpha_t k_t v_t^T;
+ *   - section 损失函数 / 训练策略: lambda is floored at 1e-12 and the numerator
+ *     is -expm1(-beta lambda), evaluated in fp32 here;
+ *   - section 整体框架 (flowchart node F): the output o_t = S_t^T q_t is read
+ *     after the update;
+ *   - section 整体框架 (last paragraph): the same recurrence runs either token
+ *     by token (decode) or chunk-parallel in the WY/UT form of DeltaNet.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
+ *     aligned. The caller owns every buffer; the library never allocates,
+ *     frees or synchronises, keeps no per-call state and is safe to call from
+ *     several host threads.
+ *   - q, k: [B, H, T, d_k]; v, o: [B, H, T, d_v]; beta: [B, H, T]; all in the
+ *     element type `dt` (fp32 or bf16). The state is always fp32, laid out
+ *     [B, H, d_k, d_v] with the row index running over the key dimension.
+ *     Only d_k == d_v is supported.
+ *   - No scaling is applied to q; o_t = S_t^T q_t exactly. bf16 outputs are
+ *     rounded to nearest even from fp32 accumulators.
+ *   - beta may be any finite real; NaN and Inf in the inputs propagate to the
+ *     outputs and are not sanitised.
+ *   - `stream` is a hipStream_t (NULL = the default stream). EFLA_OK means the
+ *     work was enqueued on that stream; completion is observed through the
+ *     stream (event or synchronise).
+ *   - Argument errors are detected on the host before any launch; such a
+ *     call returns the error code and writes nothing. A launch failure
+ *     reported by the HIP runtime returns EFLA_ERR_HIP. No C++ exception
+ *     crosses this interface.
+ */
+#ifndef EFLA_H
+#define EFLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { EFLA_DTYPE_F32 = 0, EFLA_DTYPE_BF16 = 1 } efla_dtype;
+
+typedef enum {
+  EFLA_OK = 0,
+  EFLA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  EFLA_ERR_BAD_SHAPE = 2,    /* B, H or T < 1, or d_k != d_v */
+  EFLA_ERR_UNSUPPORTED = 3,  /* head dim, chunk size or dtype outside the supported set */
+  EFLA_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
+  EFLA_ERR_WORKSPACE = 5,    /* workspace smaller than efla_fwd_chunked_workspace_bytes() */
+  EFLA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+} efla_status;
+
+/*
+ * Bytes of device workspace efla_fwd_chunked needs for these sizes (0 when
+ * the fused path needs none). Returns 0 for unsupported sizes as well;
+ * efla_fwd_chunked reports those.
+ */
+size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                        efla_dtype dt);
+
+/*
+ * Chunk-parallel EFLA forward over a whole sequence (WY/UT form; section
+ * 整体框架 of the papernotes note).
+ *   q, k, v   inputs as above, element type dt.
+ *   beta      [B, H, T] step sizes, element type dt.
+ *   s0        [B, H, d_k, d_v] fp32 initial state, or NULL for zeros.
+ *   o         [B, H, T, d_v] output, element type dt.
+ *   s_final   [B, H, d_k, d_v] fp32 final state S_T, or NULL to skip it. It
+ *             may alias s0 (the state is then advanced in place).
+ *   workspace, workspace_bytes   caller-owned scratch of at least
+ *             efla_fwd_chunked_workspace_bytes() bytes (may be NULL/0 when
+ *             that is 0).
+ *   chunk     tokens per chunk, one of 16, 32, 64. T need not be a multiple.
+ * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64};
+ * fp32 with d = 128 needs chunk <= 32. Anything else: EFLA_ERR_UNSUPPORTED.
+ */
+efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                             const float* s0, void* o, float* s_final, void* workspace,
+                             size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                             int chunk, efla_dtype dt, void* stream);
+
+/*
+ * One token per head, token-serial (the recurrent decode form; section 整体框架
+ * of the papernotes note).
+ *   q, k      [B, H, d_k], element type dt.
+ *   v         [B, H, d_v], element type dt.
+ *   beta      [B, H], element type dt.
+ *   state     [B, H, d_k, d_v] fp32; read, then overwritten with S_t.
+ *   o         [B, H, d_v] output S_t^T q_t, element type dt.
+ * Supported: d in {16, 32, 64, 128}, fp32 or bf16.
+ */
+efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
+                                    const void* beta, float* state, void* o, int B, int H,
+                                    int d_k, int d_v, efla_dtype dt, void* stream);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* efla_status_string(efla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EFLA_H */

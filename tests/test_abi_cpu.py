@@ -1,0 +1,97 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+that include/efla.h declares, and rejects bad arguments on the host before
+any launch (no GPU call is made by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_recurrent_efla_amd as efla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "efla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(efla.LIB_PATH),
+                                reason="libefla.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(efla_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("efla_fwd_chunked", "efla_fwd_recurrent_step", "efla_fwd_chunked_workspace_bytes",
+              "efla_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(efla.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in efla.STATUS_NAMES.items():
+        assert efla.status_string(code).startswith(name)
+    assert efla.status_string(99) == "EFLA_ERR_UNKNOWN"
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def chunked(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, s0=None, o=FAKE, sf=None, ws=None, wsb=0,
+            B=1, H=1, T=8, dk=64, dv=64, chunk=64, dt=1):
+    return lib.efla_fwd_chunked(q, k, v, beta, s0, o, sf, ws, wsb, B, H, T, dk, dv, chunk, dt,
+                                None)
+
+
+def step(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, state=FAKE, o=FAKE, B=1, H=1, dk=64, dv=64,
+         dt=1):
+    return lib.efla_fwd_recurrent_step(q, k, v, beta, state, o, B, H, dk, dv, dt, None)
+
+
+def test_chunked_rejects_bad_arguments_before_launch():
+    lib = efla.load_library()
+    assert chunked(lib, q=None) == 1
+    assert chunked(lib, beta=None) == 1
+    assert chunked(lib, o=None) == 1
+    assert chunked(lib, B=0) == 2
+    assert chunked(lib, H=-1) == 2
+    assert chunked(lib, T=0) == 2
+    assert chunked(lib, dv=32) == 2
+    assert chunked(lib, dk=48, dv=48) == 3
+    assert chunked(lib, dk=256, dv=256) == 3
+    assert chunked(lib, chunk=8) == 3
+    assert chunked(lib, chunk=128) == 3
+    assert chunked(lib, dt=2) == 3
+    assert chunked(lib, dk=128, dv=128, chunk=64, dt=0) == 3  # fp32, d=128 needs chunk <= 32
+    assert chunked(lib, q=FAKE + 8) == 4
+    assert chunked(lib, o=FAKE + 4) == 4
+    assert chunked(lib, s0=FAKE + 4) == 4
+    assert chunked(lib, sf=FAKE + 12) == 4
+    assert chunked(lib, beta=FAKE + 1) == 4          # bf16 beta must be 2-byte aligned
+    assert chunked(lib, beta=FAKE + 2, dt=0) == 4    # fp32 beta must be 4-byte aligned
+
+
+def test_step_rejects_bad_arguments_before_launch():
+    lib = efla.load_library()
+    assert step(lib, state=None) == 1
+    assert step(lib, q=None) == 1
+    assert step(lib, B=0) == 2
+    assert step(lib, dv=16) == 2
+    assert step(lib, dk=96, dv=96) == 3
+    assert step(lib, dt=7) == 3
+    assert step(lib, state=FAKE + 8) == 4
+    assert step(lib, k=FAKE + 2) == 4
+
+
+def test_workspace_query():
+    # the fused kernel needs no workspace for any supported size
+    for d in efla.SUPPORTED_HEAD_DIMS:
+        for c in efla.SUPPORTED_CHUNKS:
+            assert efla.load_library().efla_fwd_chunked_workspace_bytes(2, 4, 1000, d, d, c, 1) == 0

@@ -1,0 +1,265 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Error metric, per head and per output tensor: max over elements of
+|x - x_ref| divided by max |x_ref| (normwise relative). Bars: 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs (fp32 state and accumulation in both cases).
+The oracle consumes exactly the values the GPU receives (inputs upcast to
+fp64); input rounding is not counted as error.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import efla_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module")
+def efla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import delta_rule_recurrent_efla_amd as m
+
+    m.load_library()
+    return m
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def normwise(x, ref):
+    """max over heads of max|x - ref| / max|ref| (last two dims per head)."""
+    x = torch.as_tensor(x).double().cpu()
+    ref = torch.as_tensor(ref).double()
+    if x.dim() == 1:
+        x, ref = x[None, None], ref[None, None]
+    err = (x - ref).abs().flatten(-2).amax(-1)
+    scale = ref.abs().flatten(-2).amax(-1).clamp_min(1e-30)
+    return float((err / scale).max())
+
+
+def to_dev(x):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def run_chunked(efla, x, chunk, s0=None):
+    g = to_dev(x)
+    o, sT = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"],
+                                  None if s0 is None else s0.cuda(), chunk=chunk)
+    torch.cuda.synchronize()
+    return o.float().cpu(), sT.cpu()
+
+
+def supported(dt, d, c):
+    return not (dt == "f32" and d == 128 and c == 64)
+
+
+# ------------------------------------------------------------ small sweeps
+CASES = [(dt, d, c) for dt in ("f32", "bf16") for d in (16, 32, 64, 128) for c in (16, 32, 64)
+         if supported(dt, d, c)]
+
+
+@pytest.mark.parametrize("dt,d,c", CASES)
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_chunked_small_ragged(efla, dt, d, c, with_s0):
+    T = 3 * c + 5  # several chunks and a ragged tail
+    note(f"[chunked small] dtype={dt} d={d} chunk={c} T={T} s0={with_s0}")
+    x = efla_inputs.random_case(1000 + d + c, B=2, H=3, T=T, d=d, dtype=dt,
+                                s0_std=0.5 if with_s0 else 0.0)
+    o, sT = run_chunked(efla, x, c, x["s0"])
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"], nthreads=8)
+    tol = TOL[DT[dt]]
+    eo, es = normwise(o, o_ref), normwise(sT, s_ref)
+    note(f"   err o={eo:.3e} S_T={es:.3e} (tol {tol})")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("T", [1, 7, 16, 63, 64, 65, 200])
+def test_chunked_edge_lengths(efla, dt, d, T):
+    note(f"[chunked edge] dtype={dt} d={d} T={T}")
+    x = efla_inputs.random_case(77 + T, B=1, H=2, T=T, d=d, dtype=dt, s0_std=0.3)
+    o, sT = run_chunked(efla, x, 64, x["s0"])
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"])
+    tol = TOL[DT[dt]]
+    assert normwise(o, o_ref) <= tol and normwise(sT, s_ref) <= tol
+
+
+# ------------------------------------------------------------ the five configs
+SAMPLE_HEADS = {"layer340m_d128": 6, "layer1p3b_d128": 6, "stiff_long_d128": 2}
+
+
+@pytest.mark.parametrize("name", list(efla_inputs.WORKLOADS))
+def test_config_parity(efla, name):
+    w = efla_inputs.WORKLOADS[name]
+    note(f"[config] {name}: B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} {w.dtype}")
+    x = efla_inputs.make_inputs(w)
+    o, sT = run_chunked(efla, x, w.chunk, x["s0"])
+    assert torch.isfinite(o).all() and torch.isfinite(sT).all()
+    nh = w.B * w.H
+    flat = lambda t: None if t is None else t.reshape((nh,) + tuple(t.shape[2:]))
+    heads = list(range(nh))
+    if name in SAMPLE_HEADS:
+        n = SAMPLE_HEADS[name]
+        heads = sorted(set(np.linspace(0, nh - 1, n).round().astype(int).tolist()))
+    sel = lambda t: None if t is None else flat(t)[heads]
+    o_ref, s_ref, norms = oracle.fwd(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]),
+                                     sel(x["s0"]), nthreads=16, want_norms=True)
+    tol = TOL[w.torch_dtype]
+    eo = normwise(flat(o)[heads], o_ref)
+    es = normwise(flat(sT)[heads], s_ref)
+    note(f"   heads={heads[:8]}{'...' if len(heads) > 8 else ''} err o={eo:.3e} S_T={es:.3e} "
+         f"(tol {tol}); oracle max ||S_t||_F={norms.max():.3g}")
+    assert eo <= tol and es <= tol
+
+
+def test_layer340m_decode_continues_forward(efla):
+    """256 single-token steps from the chunked forward's final state."""
+    w = efla_inputs.WORKLOADS["layer340m_d128"]
+    note(f"[decode] {w.name}: {w.decode_steps} steps from S_T")
+    x = efla_inputs.make_inputs(w)
+    g = to_dev(x)
+    _, st = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], None, chunk=w.chunk)
+    outs = []
+    for i in range(w.decode_steps):
+        outs.append(efla.efla_fwd_recurrent_step(
+            g["dec_q"][:, :, i].contiguous(), g["dec_k"][:, :, i].contiguous(),
+            g["dec_v"][:, :, i].contiguous(), g["dec_beta"][:, :, i].contiguous(), st))
+    od = torch.stack(outs, 2).float().cpu()
+    torch.cuda.synchronize()
+    nh = w.B * w.H
+    heads = [0, 37, 90, nh - 1]
+    f = lambda t: t.reshape((nh,) + tuple(t.shape[2:]))[heads]
+    _, s_ref = oracle.fwd(f(x["q"]), f(x["k"]), f(x["v"]), f(x["beta"]), nthreads=8)
+    od_ref, sd_ref = oracle.fwd(f(x["dec_q"]), f(x["dec_k"]), f(x["dec_v"]), f(x["dec_beta"]),
+                                s_ref)
+    eo = normwise(f(od), od_ref)
+    es = normwise(f(st.cpu()), sd_ref)
+    note(f"   err decode o={eo:.3e} S={es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_decode_steps(efla, dt, d):
+    note(f"[decode small] dtype={dt} d={d}")
+    steps = 12
+    x = efla_inputs.random_case(300 + d, B=2, H=3, T=steps, d=d, dtype=dt, s0_std=0.5)
+    g = to_dev(x)
+    st = g["s0"].clone()
+    outs = [efla.efla_fwd_recurrent_step(g["q"][:, :, i].contiguous(), g["k"][:, :, i].contiguous(),
+                                         g["v"][:, :, i].contiguous(),
+                                         g["beta"][:, :, i].contiguous(), st)
+            for i in range(steps)]
+    od = torch.stack(outs, 2).float().cpu()
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"])
+    tol = TOL[DT[dt]]
+    assert normwise(od, o_ref) <= tol and normwise(st.cpu(), s_ref) <= tol
+
+
+# ------------------------------------------------------------ properties
+def test_single_token_chunked_equals_decode(efla):
+    x = efla_inputs.random_case(5, B=2, H=4, T=1, d=128, dtype="f32", s0_std=0.5)
+    x["q"], x["k"] = x["q"], x["k"]
+    g = to_dev(x)
+    # fp32 d=128 needs chunk <= 32
+    o1, s1 = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=32)
+    st = g["s0"].clone()
+    o2 = efla.efla_fwd_recurrent_step(g["q"][:, :, 0].contiguous(), g["k"][:, :, 0].contiguous(),
+                                      g["v"][:, :, 0].contiguous(), g["beta"][:, :, 0].contiguous(),
+                                      st)
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"])
+    assert normwise(o1.cpu()[:, :, 0], o_ref[:, :, 0]) <= 1e-4
+    assert normwise(o2.cpu(), o_ref[:, :, 0]) <= 1e-4
+    assert normwise(s1.cpu(), s_ref) <= 1e-4 and normwise(st.cpu(), s_ref) <= 1e-4
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_chaining_matches_single_call(efla, dt):
+    d, T, T1 = 64, 300, 128
+    x = efla_inputs.random_case(9, B=2, H=2, T=T, d=d, dtype=dt, s0_std=0.2)
+    g = to_dev(x)
+    o, s = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=64)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o1, s1 = efla.efla_fwd_chunked(sl(g["q"], 0, T1), sl(g["k"], 0, T1), sl(g["v"], 0, T1),
+                                   sl(g["beta"], 0, T1), g["s0"], chunk=64)
+    o2, s2 = efla.efla_fwd_chunked(sl(g["q"], T1, T), sl(g["k"], T1, T), sl(g["v"], T1, T),
+                                   sl(g["beta"], T1, T), s1, chunk=64)
+    tol = TOL[DT[dt]]
+    assert normwise(torch.cat([o1, o2], 2).float().cpu(), o.float().cpu().double()) <= tol
+    assert normwise(s2.cpu(), s.cpu().double()) <= tol
+
+
+def test_deterministic_bitwise(efla):
+    w = efla_inputs.scaled(efla_inputs.WORKLOADS["layer1p3b_d128"], B=2, H=4, T=700)
+    g = to_dev(efla_inputs.make_inputs(w))
+    runs = [efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=64)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, s in runs[1:]:
+        assert torch.equal(o.view(torch.int16), runs[0][0].view(torch.int16))
+        assert torch.equal(s, runs[0][1])
+
+
+def test_every_output_written(efla):
+    w = efla_inputs.scaled(efla_inputs.WORKLOADS["layer340m_d128"], B=1, H=3, T=333)
+    g = to_dev(efla_inputs.make_inputs(w))
+    o = torch.full_like(g["v"], float("nan"))
+    s = torch.full((1, 3, 128, 128), float("nan"), device="cuda")
+    efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], None, chunk=64, o=o, s_final=s)
+    st = torch.full((1, 3, 128, 128), float("nan"), device="cuda")
+    st.zero_()
+    od = torch.full((1, 3, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    efla.efla_fwd_recurrent_step(g["q"][:, :, 0].contiguous(), g["k"][:, :, 0].contiguous(),
+                                 g["v"][:, :, 0].contiguous(), g["beta"][:, :, 0].contiguous(),
+                                 st, o=od)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    assert torch.isfinite(od.float()).all()
+
+
+def test_state_advanced_in_place(efla):
+    x = efla_inputs.random_case(11, B=2, H=2, T=150, d=64, dtype="bf16", s0_std=0.4)
+    g = to_dev(x)
+    s = g["s0"].clone()
+    o, s_out = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], s, chunk=32, s_final=s)
+    assert s_out.data_ptr() == s.data_ptr()
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"])
+    assert normwise(s.cpu(), s_ref) <= 2e-2 and normwise(o.float().cpu(), o_ref) <= 2e-2
+
+
+def test_zero_step_size_and_zero_keys(efla):
+    x = efla_inputs.random_case(13, B=1, H=2, T=90, d=64, dtype="f32", s0_std=0.5)
+    x["beta"] = torch.zeros_like(x["beta"])
+    o, s = run_chunked(efla, x, 32, x["s0"])
+    assert torch.equal(s, x["s0"])  # nothing is ever written
+    o_ref, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"])
+    assert normwise(o, o_ref) <= 1e-4
+    y = efla_inputs.random_case(14, B=1, H=2, T=90, d=64, dtype="f32", s0_std=0.5)
+    y["k"] = torch.zeros_like(y["k"])
+    o, s = run_chunked(efla, y, 64, y["s0"])
+    assert torch.equal(s, y["s0"])
+
+
+def test_misaligned_pointer_is_rejected(efla):
+    n = 2 * 2 * 40 * 64
+    buf = torch.zeros(n + 8, dtype=torch.bfloat16, device="cuda")
+    q = buf[1:1 + n].view(2, 2, 40, 64)
+    k = torch.zeros(2, 2, 40, 64, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(2, 2, 40, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(efla.EflaError) as ei:
+        efla.efla_fwd_chunked(q, k, k, b, None, chunk=64)
+    assert ei.value.status == 4
+    with pytest.raises(efla.EflaError) as ei:
+        efla.efla_fwd_chunked(k, k, k, b, None, chunk=48)
+    assert ei.value.status == 3
