@@ -16,13 +16,19 @@
 //
 // One workgroup (4 wave64s) owns one (head, BV-column slice of the state)
 // and walks the chunks in order; the d_k x BV fp32 state never leaves the
-// MFMA accumulator registers of the wave that owns its 16 columns (columns
-// of S evolve independently, so the slice split is exact). Chunk tiles are
-// staged in LDS; T is never formed: its 16x16 diagonal blocks are inverted
-// by forward substitution in fp32 and W, U come from a blocked forward solve
-// whose right-hand sides stay in registers.
+// MFMA accumulator registers of the waves that own its columns (32 columns
+// per wave; columns of S evolve independently, so the slice split is exact).
+// Chunk tiles are staged in LDS; T is never formed: its 16x16 diagonal blocks
+// are inverted by forward substitution in fp32 and W, U come from a blocked
+// forward solve whose right-hand sides stay in registers. The next chunk's
+// loads are issued before the current chunk's compute.
 
 #include "efla_device.hpp"
+
+// Waves per workgroup that hold the state slice (2: 32 columns each; 4: 16).
+#ifndef EFLA_STATE_WAVES
+#define EFLA_STATE_WAVES 2
+#endif
 
 namespace efla {
 
@@ -49,16 +55,16 @@ template <typename CT, int D, int C, int BV>
 struct __attribute__((aligned(16))) ChunkedSmem {
   static constexpr int P = Mma<CT>::PAD;
   static constexpr int NB = C / 16;
-  CT K[C][D + P];      // keys, row-major
-  CT Kt[D][C + P];     // keys, transposed
-  CT Q[C][D + P];      // queries
-  CT Vt[BV][C + P];    // value slice, transposed
-  CT Wn[C][D + P];     // -W
-  CT An[C][C + P];     // -A (strictly lower part only is meaningful)
-  CT M[C][C + P];      // lower-incl-diag(Q K^T)
-  CT O[C][BV + P];     // output staging
-  float Adt[NB][16][20]; // fp32 diagonal blocks of A, transposed (row j = column j)
-  CT Td[NB][16][16 + P]; // inverses of I + diagonal blocks
+  CT K[C][D + P];         // keys, row-major
+  CT Kt[D][C + P];        // keys, transposed, XOR-swizzled columns (see tsw)
+  CT Q[C][D + P];         // queries
+  CT Vt[BV][C + P];       // value slice, transposed, swizzled like Kt
+  CT Wn[C][D + P];        // -W
+  CT An[C][C + P];        // -A (only the strictly lower part is read)
+  CT M[C][C + P];         // lower-incl-diag(Q K^T) (only J <= I blocks are read)
+  CT O[C][BV + P];        // output staging
+  float Adt[NB][16][20];  // fp32 diagonal blocks of A, transposed
+  CT Td[NB][16][16 + P];  // (I + diagonal block of A)^{-1}
   float alpha[C];
 };
 
@@ -75,20 +81,49 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <typename CT, int D, int C, int BV>
+// Work split of the blocked solve: every wave advances a fixed list of
+// 16-column tiles of [K | V_slice] through the row blocks. A state wave's
+// first CPW slots are its own value tiles (their solution U stays in its
+// registers); key tiles go to the least-loaded wave; spare slots repeat key
+// tile 0 and store nothing.
+template <int NW, int SW, int CPW, int NKT>
+struct SolvePlan {
+  static constexpr int NVT = SW * CPW;
+  static constexpr int NTW = (NKT + NVT + NW - 1) / NW > CPW ? (NKT + NVT + NW - 1) / NW : CPW;
+  int kind[NW][NTW];  // 0 value tile, 1 key tile, 2 spare
+  int idx[NW][NTW];
+  constexpr SolvePlan() : kind(), idx() {
+    int n[NW] = {};
+    for (int w = 0; w < NW; ++w)
+      for (int t = 0; t < NTW; ++t) kind[w][t] = 2, idx[w][t] = 0;
+    for (int w = 0; w < SW; ++w)
+      for (int c = 0; c < CPW; ++c) kind[w][n[w]] = 0, idx[w][n[w]] = w * CPW + c, ++n[w];
+    for (int m = 0; m < NKT; ++m) {
+      int best = 0;
+      for (int w = 1; w < NW; ++w)
+        if (n[w] < n[best]) best = w;
+      kind[best][n[best]] = 1, idx[best][n[best]] = m, ++n[best];
+    }
+  }
+};
+
+template <typename CT, int D, int C, int BV, int SWQ>
 __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
-  using Pack = typename MM::Pack;
+  using Frag = typename MM::Frag;
   using Vec = typename Vec16<CT>::type;
-  constexpr int NB = C / 16;    // 16-row blocks per chunk
-  constexpr int NKT = D / 16;   // 16-row tiles of the state
-  constexpr int NVT = BV / 16;  // 16-column tiles of the slice (one per wave)
+  constexpr int NB = C / 16;    // 16-token blocks per chunk
+  constexpr int NKT = D / 16;   // 16-row tiles of the state (key dimension)
+  constexpr int NVT = BV / 16;  // 16-column tiles of the state slice
   constexpr int NW = 4;
+  constexpr int SW = SWQ < NVT ? SWQ : NVT;   // waves that own state columns
+  constexpr int CPW = NVT / SW;               // column tiles per state wave
   constexpr int VE = 16 / sizeof(CT);
-  static_assert(NVT <= NW, "one state column tile per wave");
-  constexpr int KPW = (NKT + NW - 1) / NW;  // key tiles per wave in the solve
-  constexpr int NTW = 1 + KPW;              // solve tiles per wave
-  static_assert(C % 16 == 0 && D % 16 == 0 && BV % 16 == 0, "tile sizes");
+  constexpr int NFK = NFrag<CT, NKT>::value;  // fragments over the key dim
+  constexpr int NFB = NFrag<CT, NB>::value;   // fragments over a chunk
+  static_assert(C % 16 == 0 && D % 16 == 0 && BV % 16 == 0 && SW <= NW, "tile sizes");
+  constexpr SolvePlan<NW, SW, CPW, NKT> plan{};
+  constexpr int NTW = plan.NTW;
 
   __shared__ ChunkedSmem<CT, D, C, BV> sm;
 
@@ -97,6 +132,12 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   const int w = tid >> 6;
   const int li = lane & 15;
   const int g = lane >> 4;
+
+  // Transposed tiles (rows = feature index d, columns = tokens) XOR their
+  // column index with tsw(d) in 4-element groups: the staging writes, where
+  // the lanes of a wave hold 16 different d, then spread over the LDS banks,
+  // while every reader still gets 4 contiguous tokens.
+  auto tsw = [](int d) { return ((d / VE) & (C / 4 - 1)) * 4; };
 
   // Workgroups are dispatched round-robin over the 8 XCDs; remap so that the
   // column slices of one head are adjacent on one XCD and share its L2.
@@ -114,26 +155,33 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   const CT* bg = (const CT*)a.beta + (size_t)head * T;
   CT* og = (CT*)a.o + (size_t)head * T * D;
 
-  const bool owner = w < NVT;
-  const int kfirst = (w + NW - (NVT % NW)) % NW;  // first key tile of this wave
-  const int scol = v0 + 16 * w + li;  // state column held by this lane
-  floatx4 sacc[NKT];
+  // ---- state slice: wave w < SW owns columns v0 + 16 (w CPW + c) + [0, 16)
+  const bool owner = w < SW;
+  floatx4 sacc[CPW][NKT];
 #pragma unroll
-  for (int rt = 0; rt < NKT; ++rt) sacc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt) sacc[c][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
   if (owner && a.s0) {
     const float* s0 = a.s0 + (size_t)head * D * D;
 #pragma unroll
-    for (int rt = 0; rt < NKT; ++rt)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[rt][e] = s0[(size_t)(16 * rt + 4 * g + e) * D + scol];
+      for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sacc[c][rt][e] = s0[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
   }
   // Retire the initial-state loads here: left pending, they make the compiler
   // wait on every outstanding load (the next chunk's prefetch included)
   // inside the chunk loop.
 #pragma unroll
-  for (int rt = 0; rt < NKT; ++rt) asm volatile("" : "+v"(sacc[rt]));
-  floatx4 uacc[NB];
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt) asm volatile("" : "+v"(sacc[c][rt]));
+  floatx4 uacc[CPW][NB];
 
+  // ---- register prefetch of one chunk (coalesced 16-byte loads)
   constexpr int VPR = D / VE;    // 16-byte vectors per K/Q row
   constexpr int VPRV = BV / VE;  // 16-byte vectors per V-slice row
   constexpr int NLK = (C * VPR + 255) / 256;
@@ -171,25 +219,24 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
     const int t0 = ch * C;
     const int nval = min(C, T - t0);
 
-    // ---- chunk ch (prefetched in registers) -> LDS: K (both layouts), Q and
-    //      the V slice; lambda = ||k||^2 and alpha per row
+    // ---- chunk ch (prefetched) -> LDS; lambda = ||k||^2 and alpha per row
     {
 #pragma unroll
       for (int j = 0; j < NLK; ++j) {
         const int idx = tid + 256 * j;
         if (idx < C * VPR) {
           const int r = idx / VPR, cv = idx % VPR;
-          *(Vec*)&sm.K[r][cv * VE] = kreg[j];
-          *(Vec*)&sm.Q[r][cv * VE] = qreg[j];
+          st16(&sm.K[r][cv * VE], kreg[j]);
+          st16(&sm.Q[r][cv * VE], qreg[j]);
           float ss = 0.f;
 #pragma unroll
           for (int e = 0; e < VE; ++e) {
-            sm.Kt[cv * VE + e][r] = kreg[j][e];
+            const int d = cv * VE + e;
+            sm.Kt[d][r ^ tsw(d)] = kreg[j][e];
             const float x = to_f32(kreg[j][e]);
             ss += x * x;
           }
-#pragma unroll
-          for (int off = 1; off < VPR; off <<= 1) ss += __shfl_xor(ss, off);
+          ss = group_sum<VPR>(ss);
           if (cv == 0) sm.alpha[r] = gate_alpha(to_f32(breg[j]), ss);
         }
       }
@@ -199,7 +246,10 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
         if (idx < C * VPRV) {
           const int r = idx / VPRV, cv = idx % VPRV;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) sm.Vt[cv * VE + e][r] = vreg[j][e];
+          for (int e = 0; e < VE; ++e) {
+            const int d = cv * VE + e;
+            sm.Vt[d][r ^ tsw(d)] = vreg[j][e];
+          }
         }
       }
     }
@@ -207,32 +257,76 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
     if (ch + 1 < nchunks) prefetch(ch + 1);
     __syncthreads();
 
-    // ---- Gram and Q K^T on the lower block triangle
+    // ---- Gram, diagonal-block inverses and Q K^T, one barrier.
+    //      Wave w first computes diagonal Gram block w, writes its scaled
+    //      strictly-lower part (fp32, transposed) to LDS and inverts
+    //      I + A_ww by column-parallel right-looking forward substitution
+    //      (lane i owns column i; once t_j is final, column j of A is
+    //      eliminated from the rows below, all independently). The remaining
+    //      lower-triangle tiles of K K^T (-> -A) and Q K^T (-> M) are then
+    //      shared out. Tile (I, J) is computed as X_J Y_I^T so that a lane
+    //      ends up with 4 consecutive columns of row 16 I + li.
     {
-      constexpr int NT = NB * (NB + 1) / 2;
-      for (int job = w; job < 2 * NT; job += NW) {
-        const bool isq = job >= NT;
-        const int jj = isq ? job - NT : job;
-        int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= jj) ++I;
-        const int J = jj - I * (I + 1) / 2;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        // (K_J X_I^T)[4g+e][li] = x_{16I+li} . k_{16J+4g+e}
-        MM::template ll<D>(acc, &sm.K[16 * J + li][0],
-                           isq ? &sm.Q[16 * I + li][0] : &sm.K[16 * I + li][0]);
+      auto gram_store = [&](int I, int J, floatx4 acc) {
         const int r = 16 * I + li;
         const int cb = 16 * J + 4 * g;
-        if (!isq) {
-          const float al = sm.alpha[r];
-          floatx4 ad;
+        const float al = sm.alpha[r];
+        floatx4 ad;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] : 0.f;
-          MM::store_t(&sm.An[r][16 * J], -ad);
-          if (I == J) {
+        for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] : 0.f;
+        MM::store_t(&sm.An[r][16 * J], -ad);
+        return ad;
+      };
+      if (w < NB) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        MM::template ll<D>(acc, &sm.K[16 * w + li][0], &sm.K[16 * w + li][0]);
+        const floatx4 ad = gram_store(w, w, acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Adt[I][4 * g + e][li] = ad[e];
-          }
+        for (int e = 0; e < 4; ++e) sm.Adt[w][4 * g + e][li] = ad[e];
+        // the block is private to this wave: order its LDS writes before the
+        // reads below without a workgroup barrier
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+          floatx4 a4[4];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) a4[q4] = *(const floatx4*)&sm.Adt[w][j][4 * q4];
+#pragma unroll
+          for (int r = j + 1; r < 16; ++r) t[r] -= a4[r >> 2][r & 3] * t[j];
+        }
+        // lane groups g = 0..3 hold identical columns; group g writes rows 4g..4g+3
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((r >> 2) == g) sm.Td[w][r][li] = from_f32<CT>(t[r]);
+      }
+      constexpr int NOFF = NB * (NB - 1) / 2;   // strictly-lower Gram tiles
+      constexpr int NQK = NB * (NB + 1) / 2;    // lower-incl-diag Q K^T tiles
+      for (int job = w; job < NOFF + NQK; job += NW) {
+        const bool isq = job >= NOFF;
+        const int jj = isq ? job - NOFF : job;
+        int I, J;
+        if (isq) {
+          I = 0;
+          while ((I + 1) * (I + 2) / 2 <= jj) ++I;
+          J = jj - I * (I + 1) / 2;
         } else {
+          I = 1;
+          while (I * (I + 1) / 2 <= jj) ++I;
+          J = jj - I * (I - 1) / 2;
+        }
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        MM::template ll<D>(acc, &sm.K[16 * J + li][0],
+                           isq ? &sm.Q[16 * I + li][0] : &sm.K[16 * I + li][0]);
+        if (!isq) {
+          gram_store(I, J, acc);
+        } else {
+          const int r = 16 * I + li;
+          const int cb = 16 * J + 4 * g;
           floatx4 m;
 #pragma unroll
           for (int e = 0; e < 4; ++e) m[e] = (cb + e <= r) ? acc[e] : 0.f;
@@ -242,108 +336,129 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
     }
     __syncthreads();
 
-    // ---- (I + A_bb)^{-1} for each 16x16 diagonal block: column-parallel,
-    //      right-looking forward substitution in fp32 (lane group g takes
-    //      block g, lane i its column i; after t_j is final, column j of A
-    //      is eliminated from the rows below, so the updates are independent).
-    if (w == 0 && g < NB) {
-      float t[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) {
-        floatx4 a4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) a4[q4] = *(const floatx4*)&sm.Adt[g][j][4 * q4];
-#pragma unroll
-        for (int r = j + 1; r < 16; ++r) t[r] -= a4[r >> 2][r & 3] * t[j];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Td[g][r][li] = from_f32<CT>(t[r]);
-    }
-    __syncthreads();
-
-    // ---- blocked forward solve (I + A) X = diag(a) [K | V_slice] over
-    //      16-column tiles. Each wave takes its value tile (kept in registers
-    //      as U) and KPW key tiles (written to LDS as -W); the tiles advance
-    //      through the row blocks together so their MFMA chains overlap.
+    // ---- blocked forward solve (I + A) X = diag(a) [K | V_slice]:
+    //      Y_i = diag(a_i) B_i - sum_{j<i} A_ij X_j,  X_i = (I + A_ii)^{-1} Y_i,
+    //      all of this wave's tiles advancing together so their MFMA chains
+    //      overlap. A value tile's X (= U) stays in registers. A key tile's X
+    //      (= W) is also formed transposed, X_i^T = Y_i^T (I + A_ii)^{-T}, whose
+    //      accumulator holds 4 consecutive columns of a row of W: it is
+    //      stored negated and row-major with 8-byte writes.
     {
       const CT* rhs[NTW];
-      int kt[NTW];  // key tile index, or -1 for the value tile, -2 for padding
+      int swz[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        int m;
-        if (t == 0 && owner) {
-          kt[t] = -1;
-          rhs[t] = &sm.Vt[16 * w + li][0];
-          continue;
-        }
-        m = kfirst + NW * (owner ? t - 1 : t);
-        kt[t] = m < NKT ? m : -2;  // padding slots recompute tile 0 and store nothing
-        rhs[t] = &sm.Kt[16 * (m < NKT ? m : 0) + li][0];
+        const int row = 16 * plan.idx[w][t] + li;
+        rhs[t] = plan.kind[w][t] == 0 ? &sm.Vt[row][0] : &sm.Kt[row][0];
+        swz[t] = tsw(row);
       }
       floatx4 x[NTW][NB];
+      Frag xf[NTW][NFB];
       static_for<NB>([&](auto ib) {
         constexpr int i = decltype(ib)::value;
+        const floatx4 al = *(const floatx4*)&sm.alpha[16 * i + 4 * g];
+        const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
+        Frag an[NFrag<CT, (i > 0 ? i : 1)>::value];
+        if constexpr (i > 0) {
+#pragma unroll
+          for (int f = 0; f < NFrag<CT, i>::value; ++f)
+            an[f] = MM::template lds<i>(&sm.An[16 * i + li][0], f, 0);
+        }
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          floatx4 acc;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * i + 4 * g + e;
-            acc[e] = sm.alpha[r] * to_f32(rhs[t][r]);
-          }
+          floatx4 y = al * MM::load4(rhs[t] + ((16 * i + 4 * g) ^ swz[t]));
           if constexpr (i > 0) {
-            Pack p[PackCount<CT, i>::value];
-            MM::template pack<i>(x[t], p);
-            MM::template lp<i>(acc, &sm.An[16 * i + li][0], p);
+#pragma unroll
+            for (int f = 0; f < NFrag<CT, i>::value; ++f) {
+              // fragment f of X_{<i}; its upper tile exists only once block 2f+1 < i
+              Frag xin = xf[t][f];
+              if constexpr (Mma<CT>::KT == 2) {
+                if (2 * f + 1 >= i) xin = MM::template acc<1>(&x[t][2 * f], 0);
+              }
+              y = MM::mma(y, an[f], xin);
+            }
           }
-          Pack pa[PackCount<CT, 1>::value];
-          MM::template pack<1>(&acc, pa);
-          floatx4 xi = {0.f, 0.f, 0.f, 0.f};
-          MM::template lp<1>(xi, &sm.Td[i][li][0], pa);
-          x[t][i] = xi;
+          const Frag yf = MM::template acc<1>(&y, 0);
+          x[t][i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
+          if constexpr (Mma<CT>::KT == 2) {
+            if constexpr (i % 2 == 1) xf[t][i / 2] = MM::template acc<2>(&x[t][i - 1], 0);
+          } else {
+            xf[t][i] = MM::template acc<1>(&x[t][i], 0);
+          }
+          if (plan.kind[w][t] == 1) {
+            const floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
+            MM::store_t(&sm.Wn[16 * i + li][16 * plan.idx[w][t]], -xt);
+          }
         }
       });
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        if (kt[t] == -1) {
+        if (plan.kind[w][t] == 0) {
+          const int c = plan.idx[w][t] - w * CPW;
 #pragma unroll
-          for (int i = 0; i < NB; ++i) uacc[i] = x[t][i];
-        } else if (kt[t] >= 0) {
+          for (int cc = 0; cc < CPW; ++cc)
+            if (cc == c) {
 #pragma unroll
-          for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sm.Wn[16 * i + 4 * g + e][16 * kt[t] + li] = from_f32<CT>(-x[t][i][e]);
+              for (int i = 0; i < NB; ++i) uacc[cc][i] = x[t][i];
+            }
         }
       }
     }
     __syncthreads();
 
-    // ---- serial part: U' = U - W S, O = Q S + M U', S += K^T U'
+    // ---- serial part, per state wave and column tile c:
+    //      U' = U - W S;  O^T = S^T Q^T + U'^T M^T;  S += K^T U'
     if (owner) {
-      Pack spk[PackCount<CT, NKT>::value];
-      MM::template pack<NKT>(sacc, spk);
-      floatx4 oacc[NB];
+      Frag sf[CPW][NFK];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int f = 0; f < NFK; ++f) sf[c][f] = MM::template acc<NKT>(sacc[c], f);
+      floatx4 oacc[CPW][NB];
 #pragma unroll
       for (int ut = 0; ut < NB; ++ut) {
-        MM::template lp<NKT>(uacc[ut], &sm.Wn[16 * ut + li][0], spk);
-        oacc[ut] = floatx4{0.f, 0.f, 0.f, 0.f};
-        MM::template lp<NKT>(oacc[ut], &sm.Q[16 * ut + li][0], spk);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) oacc[c][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NFK; ++f) {
+          const Frag wf = MM::template lds<NKT>(&sm.Wn[16 * ut + li][0], f, 0);
+          const Frag qf = MM::template lds<NKT>(&sm.Q[16 * ut + li][0], f, 0);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c) {
+            uacc[c][ut] = MM::mma(uacc[c][ut], wf, sf[c][f]);
+            oacc[c][ut] = MM::mma(oacc[c][ut], sf[c][f], qf);
+          }
+        }
       }
-      Pack upk[PackCount<CT, NB>::value];
-      MM::template pack<NB>(uacc, upk);
+      Frag uf[CPW][NFB];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int f = 0; f < NFB; ++f) uf[c][f] = MM::template acc<NB>(uacc[c], f);
       static_for<NB>([&](auto ub) {
         constexpr int ut = decltype(ub)::value;
-        MM::template lp<ut + 1>(oacc[ut], &sm.M[16 * ut + li][0], upk);
+#pragma unroll
+        for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
+          const Frag mf = MM::template lds<ut + 1>(&sm.M[16 * ut + li][0], f, 0);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c) oacc[c][ut] = MM::mma(oacc[c][ut], uf[c][f], mf);
+        }
       });
 #pragma unroll
-      for (int rt = 0; rt < NKT; ++rt) MM::template lp<NB>(sacc[rt], &sm.Kt[16 * rt + li][0], upk);
+      for (int rt = 0; rt < NKT; ++rt) {
+        const int row = 16 * rt + li;
 #pragma unroll
-      for (int ut = 0; ut < NB; ++ut)
+        for (int f = 0; f < NFB; ++f) {
+          const Frag kf = MM::template lds<NB>(&sm.Kt[row][0], f, tsw(row));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.O[16 * ut + 4 * g + e][16 * w + li] = from_f32<CT>(oacc[ut][e]);
+          for (int c = 0; c < CPW; ++c) sacc[c][rt] = MM::mma(sacc[c][rt], kf, uf[c][f]);
+        }
+      }
+      // O^T tile (c, ut): lane holds O[16 ut + li][16 (w CPW + c) + 4 g + e]
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int ut = 0; ut < NB; ++ut) MM::store_t(&sm.O[16 * ut + li][16 * (w * CPW + c)], oacc[c][ut]);
     }
     __syncthreads();
 
@@ -352,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
       constexpr int VPRO = BV / VE;
       for (int idx = tid; idx < C * VPRO; idx += 256) {
         const int r = idx / VPRO, cv = idx % VPRO;
-        if (r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = *(const Vec*)&sm.O[r][cv * VE];
+        if (r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = ld16(&sm.O[r][cv * VE]);
       }
     }
   }
@@ -360,9 +475,12 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   if (owner && a.s_final) {
     float* sf = a.s_final + (size_t)head * D * D;
 #pragma unroll
-    for (int rt = 0; rt < NKT; ++rt)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sf[(size_t)(16 * rt + 4 * g + e) * D + scol] = sacc[rt][e];
+      for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li] = sacc[c][rt][e];
   }
 }
 
@@ -375,7 +493,7 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, hipStream_t stre
   ChunkedArgs a = in;
   a.nvt = D / BV;
   dim3 grid((unsigned)(NH * a.nvt)), block(256);
-  hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, BV>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, BV, EFLA_STATE_WAVES>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,25 @@ __device__ __forceinline__ float gate_alpha(float beta, float lam) {
   return -expm1f(-beta * lamc) / lamc;
 }
 
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
+// every lane of a group receiving the group's sum. Within a 16-lane row the
+// exchange uses DPP (quad permutes, then half-row and row mirrors).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                              decltype(ctrl)::value, 0xf, 0xf,
+                                                              false));
+  };
+  if constexpr (N >= 2) x += dpp(x, std::integral_constant<int, 0xB1>{});   // quad_perm 1,0,3,2
+  if constexpr (N >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
+  if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  static_assert(N <= 32, "group size");
+  return x;
+}
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 
@@ -43,17 +62,28 @@ template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
 // ---------------------------------------------------------------------------
-// MFMA traits. All pointers are LDS pointers already offset to the lane's
-// row (A) or column (B), k running contiguously.
+// MFMA traits.
+//
+// A "fragment" is one lane's share of an MFMA operand for a k-step covering
+// KT 16-row tiles: bf16 MFMAs (16x16x32) cover two tiles per instruction, fp32
+// MFMAs (16x16x4) one tile in four instructions. Inside a tile, k slot
+// (g, e) is row 4g + e, so an accumulator tile (rows 4g + e per lane) turns
+// into a fragment with no data movement across lanes:
+//   * as the B operand of A*X (k running over X's rows), or
+//   * as the A operand of X^T*B (k running over X's rows again).
+// LDS rows are read with the same k order: 4 contiguous elements at
+// column (16 t + 4 g) ^ swz, where swz (a multiple of 4) is the row's XOR
+// swizzle (0 for unswizzled arrays).
 template <typename CT>
 struct Mma;
 
 template <>
 struct Mma<bf16> {
-  static constexpr int PAD = 8;  // 16-byte row padding in elements
-  typedef bf16x8 Pack;           // B operand covering two 16-row tiles
+  static constexpr int PAD = 4;  // row padding (elements): 8-byte offset between rows
+  static constexpr int KT = 2;   // 16-row tiles per fragment
+  typedef bf16x8 Frag;
 
-  __device__ __forceinline__ static floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
+  __device__ __forceinline__ static floatx4 mma(floatx4 c, Frag a, Frag b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ __forceinline__ static bf16x4 cvt4(floatx4 v) {
@@ -62,105 +92,101 @@ struct Mma<bf16> {
   __device__ __forceinline__ static bf16x8 cat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-
-  // c += A[16 x K] * B[K x 16]; A row and B column both from LDS, k contiguous.
-  // K is a multiple of 16.
+  // Fragment f (tiles 2f, 2f+1) of NR accumulator tiles.
+  template <int NR>
+  __device__ __forceinline__ static Frag acc(const floatx4* t, int f) {
+    bf16x4 hi = {};
+    if (2 * f + 1 < NR) hi = cvt4(t[2 * f + 1]);
+    return cat(cvt4(t[2 * f]), hi);
+  }
+  // Fragment f of an LDS row restricted to NR tiles.
+  template <int NR>
+  __device__ __forceinline__ static Frag lds(const bf16* row, int f, int swz) {
+    const int g = lane_id() >> 4;
+    bf16x4 lo = *(const bf16x4*)(row + ((32 * f + 4 * g) ^ swz));
+    bf16x4 hi = {};
+    if (2 * f + 1 < NR) hi = *(const bf16x4*)(row + ((32 * f + 16 + 4 * g) ^ swz));
+    return cat(lo, hi);
+  }
+  // c += A[16 x K] * B[K x 16] with A row and B column from LDS, natural k
+  // order (8 contiguous elements per lane). K is a multiple of 16.
   template <int K>
   __device__ __forceinline__ static void ll(floatx4& c, const bf16* arow, const bf16* bcol) {
     const int g = lane_id() >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 + 32 <= K; k0 += 32) {
-      bf16x8 a = *(const bf16x8*)(arow + k0 + 8 * g);
-      bf16x8 b = *(const bf16x8*)(bcol + k0 + 8 * g);
-      c = mfma(a, b, c);
-    }
+    for (int k0 = 0; k0 + 32 <= K; k0 += 32) c = mma(c, ld8(arow + k0 + 8 * g), ld8(bcol + k0 + 8 * g));
     if constexpr (K % 32 == 16) {
       constexpr int k0 = K - 16;
       bf16x8 a = {}, b = {};
       if (g < 2) {
-        a = *(const bf16x8*)(arow + k0 + 8 * g);
-        b = *(const bf16x8*)(bcol + k0 + 8 * g);
+        a = ld8(arow + k0 + 8 * g);
+        b = ld8(bcol + k0 + 8 * g);
       }
-      c = mfma(a, b, c);
+      c = mma(c, a, b);
     }
   }
-
-  // Pack NR accumulator row tiles (rows 16r + 4g + e) into B operands.
-  template <int NR>
-  __device__ __forceinline__ static void pack(const floatx4* t, Pack* p) {
-#pragma unroll
-    for (int r = 0; r < NR; r += 2) {
-      bf16x4 lo = cvt4(t[r]);
-      bf16x4 hi = {};
-      if (r + 1 < NR) hi = cvt4(t[r + 1]);
-      p[r / 2] = cat(lo, hi);
-    }
+  // 8 contiguous elements from an 8-byte aligned LDS address (two 8-byte reads).
+  __device__ __forceinline__ static bf16x8 ld8(const bf16* p) {
+    return cat(*(const bf16x4*)p, *(const bf16x4*)(p + 4));
   }
-
-  // c += A[16 x 16*NR] * B where B's 16-row tiles come packed from registers.
-  // A is read with the matching k order (4 contiguous per 16-row tile).
-  template <int NR>
-  __device__ __forceinline__ static void lp(floatx4& c, const bf16* arow, const Pack* p) {
-    const int g = lane_id() >> 4;
-#pragma unroll
-    for (int r = 0; r < NR; r += 2) {
-      bf16x4 lo = *(const bf16x4*)(arow + 16 * r + 4 * g);
-      bf16x4 hi = {};
-      if (r + 1 < NR) hi = *(const bf16x4*)(arow + 16 * (r + 1) + 4 * g);
-      c = mfma(cat(lo, hi), p[r / 2], c);
-    }
-  }
-
-  // Accumulator tile -> LDS, transposed: lane writes its 4 rows as 4
-  // consecutive elements of row (lane's column) of dst.
+  // Accumulator tile -> 4 contiguous elements at dst_row + 4g.
   __device__ __forceinline__ static void store_t(bf16* dst_row, floatx4 v) {
     const int g = lane_id() >> 4;
     *(bf16x4*)(dst_row + 4 * g) = cvt4(v);
+  }
+  __device__ __forceinline__ static floatx4 load4(const bf16* p) {
+    return __builtin_convertvector(*(const bf16x4*)p, floatx4);
   }
 };
 
 template <>
 struct Mma<float> {
   static constexpr int PAD = 4;
-  typedef floatx4 Pack;  // one 16-row tile, kept in fp32
+  static constexpr int KT = 1;
+  typedef floatx4 Frag;  // the four k-slices of one tile
 
-  __device__ __forceinline__ static floatx4 mfma(float a, float b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  __device__ __forceinline__ static floatx4 mma(floatx4 c, Frag a, Frag b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+    return c;
   }
-
+  template <int NR>
+  __device__ __forceinline__ static Frag acc(const floatx4* t, int f) {
+    return t[f];
+  }
+  template <int NR>
+  __device__ __forceinline__ static Frag lds(const float* row, int f, int swz) {
+    const int g = lane_id() >> 4;
+    return *(const floatx4*)(row + ((16 * f + 4 * g) ^ swz));
+  }
   template <int K>
   __device__ __forceinline__ static void ll(floatx4& c, const float* arow, const float* bcol) {
     const int g = lane_id() >> 4;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4) c = mfma(arow[k0 + g], bcol[k0 + g], c);
+    for (int k0 = 0; k0 < K; k0 += 4)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[k0 + g], bcol[k0 + g], c, 0, 0, 0);
   }
-
-  template <int NR>
-  __device__ __forceinline__ static void pack(const floatx4* t, Pack* p) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) p[r] = t[r];
-  }
-
-  template <int NR>
-  __device__ __forceinline__ static void lp(floatx4& c, const float* arow, const Pack* p) {
-    const int g = lane_id() >> 4;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) c = mfma(arow[16 * r + 4 * g + s], p[r][s], c);
-    }
-  }
-
   __device__ __forceinline__ static void store_t(float* dst_row, floatx4 v) {
     const int g = lane_id() >> 4;
     *(floatx4*)(dst_row + 4 * g) = v;
   }
+  __device__ __forceinline__ static floatx4 load4(const float* p) { return *(const floatx4*)p; }
 };
 
-// Number of packs needed for NR row tiles.
+// 16-byte register vector <-> LDS at 8-byte alignment (bf16 rows are padded
+// by 8 bytes, so a 16-byte LDS access is issued as two 8-byte ones).
+__device__ __forceinline__ void st16(bf16* p, bf16x8 v) {
+  *(bf16x4*)p = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+  *(bf16x4*)(p + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 ld16(const bf16* p) { return Mma<bf16>::ld8(p); }
+__device__ __forceinline__ void st16(float* p, floatx4 v) { *(floatx4*)p = v; }
+__device__ __forceinline__ floatx4 ld16(const float* p) { return *(const floatx4*)p; }
+
+// Number of fragments covering NR 16-row tiles.
 template <typename CT, int NR>
-struct PackCount {
-  static constexpr int value = sizeof(CT) == 2 ? (NR + 1) / 2 : NR;
+struct NFrag {
+  static constexpr int value = (NR + Mma<CT>::KT - 1) / Mma<CT>::KT;
 };
 
 }  // namespace efla
