@@ -183,6 +183,44 @@ __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return Mma<bf16>::ld8(p)
 __device__ __forceinline__ void st16(float* p, floatx4 v) { *(floatx4*)p = v; }
 __device__ __forceinline__ floatx4 ld16(const float* p) { return *(const floatx4*)p; }
 
+// Four consecutive rows row0 .. row0+3 of column col0 + (lane & 15) of a
+// row-major LDS tile with leading dimension ld (elements). row0 may differ
+// between the four 16-lane groups; col0 is a multiple of 16.
+//   bf16: one ds_read_b64_tr_b16. Within each 16-lane group, lane a + 4m
+//   addresses row row0 + m, columns col0 + 4a .. col0 + 4a + 3, and the
+//   instruction returns to lane 4a + b column col0 + 4a + b of those four rows.
+//   fp32: four 4-byte reads.
+__device__ __forceinline__ bf16x4 ldtr4(const bf16* base, int ld, int row0, int col0) {
+  const int li = lane_id() & 15;
+  const bf16* p = base + (row0 + (li >> 2)) * ld + col0 + 4 * (li & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4*)(p));
+}
+__device__ __forceinline__ floatx4 ldtr4(const float* base, int ld, int row0, int col0) {
+  const int li = lane_id() & 15;
+  const float* p = base + row0 * ld + col0 + li;
+  return floatx4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+}
+__device__ __forceinline__ floatx4 to_f32x4(bf16x4 v) { return __builtin_convertvector(v, floatx4); }
+__device__ __forceinline__ floatx4 to_f32x4(floatx4 v) { return v; }
+
+// Fragment f (k over rows 32f.. or 16f.. of a row-major tile) of the
+// transposed tile, for a 16-column block at col0: lane i gets column col0 + i.
+// NR bounds the row tiles present.
+template <int NR>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16* base, int ld, int f, int col0) {
+  const int g = lane_id() >> 4;
+  bf16x4 lo = ldtr4(base, ld, 32 * f + 4 * g, col0);
+  bf16x4 hi = {};
+  if (2 * f + 1 < NR) hi = ldtr4(base, ld, 32 * f + 16 + 4 * g, col0);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int NR>
+__device__ __forceinline__ floatx4 tr_frag(const float* base, int ld, int f, int col0) {
+  const int g = lane_id() >> 4;
+  return ldtr4(base, ld, 16 * f + 4 * g, col0);
+}
+
 // Number of fragments covering NR 16-row tiles.
 template <typename CT, int NR>
 struct NFrag {
