@@ -25,9 +25,13 @@
 
 #include "efla_device.hpp"
 
-// Waves per workgroup that hold the state slice (2: 32 columns each; 4: 16).
+// Waves per workgroup that hold the state slice (2: 32 columns each; 4: 16),
+// for the 4-wave kernel and for the state group of the pipelined kernel.
 #ifndef EFLA_STATE_WAVES
 #define EFLA_STATE_WAVES 2
+#endif
+#ifndef EFLA_PIPE_STATE_WAVES
+#define EFLA_PIPE_STATE_WAVES 2
 #endif
 
 namespace efla {
@@ -501,20 +505,25 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 template <typename CT, int D, int C, int BV>
 struct __attribute__((aligned(16))) PipeSmem {
   static constexpr int P = Mma<CT>::PAD;
-  static constexpr int PK = 16 / sizeof(CT);  // K, Q rows padded by 16 bytes
+  static constexpr int PP = Mma<CT>::PADP;
   static constexpr int NB = C / 16;
+  // the column permutation acts inside 32-column blocks: permuted rows hold
+  // at least 32 positions
+  static constexpr int DP = (D < 32 ? 32 : D) + PP;
+  static constexpr int CP = (C < 32 ? 32 : C) + PP;
   struct Buf {
-    CT K[C][D + PK];
-    CT Q[C][D + PK];
-    CT V[C][BV + P];   // value slice
-    CT T[C][C + P];    // (I + A)^{-1}; only the lower block triangle is read
-    CT M[C][C + P];    // lower-incl-diag(Q K^T); only J <= I blocks are read
+    CT K[C][DP];       // keys, column-permuted rows
+    CT Q[C][DP];       // queries, column-permuted rows
+    CT V[C][BV + P];   // value slice, natural layout
+    CT T[C][CP];       // (I + A)^{-1}, permuted; only the lower block triangle is read
+    CT M[C][CP];       // lower-incl-diag(Q K^T), permuted; only J <= I blocks are read
     float alpha[C];
   } buf[2];
-  CT An[C][C + P];        // -A, strictly lower part (prep-private)
+  CT An[C][CP];           // -(K K^T), permuted, blocks below the diagonal (prep-private)
   float Adt[NB][16][20];  // fp32 diagonal blocks of A, transposed (prep-private)
-  CT Td[NB][16][16 + P];  // (I + A_bb)^{-1} (prep-private)
+  CT Td[NB][16][16 + P];  // (I + A_bb)^{-1}, natural layout (prep-private)
   CT O[C][BV + P];        // output staging (state group)
+  float betas[C];         // step sizes of the chunk being prepared (prep-private)
 };
 
 template <typename CT, int D, int C, int BV>
@@ -522,8 +531,9 @@ constexpr size_t pipe_smem_bytes() {
   return sizeof(PipeSmem<CT, D, C, BV>);
 }
 
-// Strictly-lower Gram tiles and lower-incl-diag Q K^T tiles, enumerated
-// (I, J) row by row; job j goes to prep wave j % 4.
+// Gram tiles below the diagonal blocks and lower-incl-diag Q K^T tiles,
+// enumerated (I, J) row by row; job j goes to prep wave 1 + j % 3 (prep wave 0
+// owns the diagonal Gram blocks).
 template <int NB>
 struct PrepJobs {
   static constexpr int NOFF = NB * (NB - 1) / 2;
@@ -540,8 +550,16 @@ struct PrepJobs {
   }
 };
 
-template <typename CT, int D, int C, int BV>
-__global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
+// 16-byte register vector of 8 (bf16) or 4 (fp32) consecutive columns
+// starting at c0 -> column-permuted LDS row.
+__device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
+  *(bf16x4*)(row + Mma<bf16>::pcol(c0)) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+  *(bf16x4*)(row + Mma<bf16>::pcol(c0 + 4)) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
+
+template <typename CT, int D, int C, int BV, int NSW>
+__global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
   using Vec = typename Vec16<CT>::type;
@@ -549,18 +567,21 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
   constexpr int NB = C / 16;
   constexpr int NKT = D / 16;
   constexpr int NVT = BV / 16;
+  constexpr int SW = NSW < NVT ? NSW : NVT;  // state waves holding columns
+  constexpr int CPW = NVT / SW;              // 16-column tiles per state wave
   constexpr int VE = 16 / sizeof(CT);
   constexpr int NFK = NFrag<CT, NKT>::value;
   constexpr int NFB = NFrag<CT, NB>::value;
-  constexpr int LDK = D + Sm::PK;
+  constexpr int LDK = Sm::DP;
   constexpr int LDV = BV + Sm::P;
-  static_assert(NVT <= 4 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
+  constexpr int NST = 64 * NSW;  // state-group threads
+  static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
 
   __shared__ Sm sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;  // 0-3 state group, 4-7 prep group
+  const int w = tid >> 6;  // 0..NSW-1 state group, NSW..NSW+3 prep group
   const int li = lane & 15;
   const int g = lane >> 4;
 
@@ -573,29 +594,35 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
   const int T = a.T;
   const int nchunks = (T + C - 1) / C;
 
-  if (w < 4) {
+  if (w < NSW) {
     // ======================= state group =======================
-    const bool owner = w < NVT;
-    const int scol = v0 + 16 * w + li;
+    const bool owner = w < SW;
     CT* og = (CT*)a.o + (size_t)head * T * D;
-    floatx4 sacc[NKT];
+    floatx4 sacc[CPW][NKT];
 #pragma unroll
-    for (int rt = 0; rt < NKT; ++rt) sacc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) sacc[c][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (owner && a.s0) {
       const float* s0 = a.s0 + (size_t)head * D * D;
 #pragma unroll
-      for (int rt = 0; rt < NKT; ++rt)
+      for (int c = 0; c < CPW; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[rt][e] = s0[(size_t)(16 * rt + 4 * g + e) * D + scol];
+        for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[c][rt][e] = s0[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
     }
 #pragma unroll
-    for (int rt = 0; rt < NKT; ++rt) asm volatile("" : "+v"(sacc[rt]));
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) asm volatile("" : "+v"(sacc[c][rt]));
 
     auto store_out = [&](int chunk) {
       const int t0 = chunk * C;
       const int nval = min(C, T - t0);
       constexpr int VPRO = BV / VE;
-      for (int idx = tid; idx < C * VPRO; idx += 256) {
+      for (int idx = tid; idx < C * VPRO; idx += NST) {
         const int r = idx / VPRO, cv = idx % VPRO;
         if (r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = ld16(&sm.O[r][cv * VE]);
       }
@@ -604,48 +631,78 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
     for (int c = -1; c < nchunks; ++c) {
       const bool act = c >= 0 && owner;
       const auto& B = sm.buf[c & 1];
-      floatx4 oacc[NB], y[NB];
-      Frag sf[NFK], uf[NFB];
-      // ---- phase A: K S, S^T Q^T, Y = diag(a)(V - K S); store outputs of c-1
+      floatx4 oacc[CPW][NB], y[CPW][NB];
+      Frag uf[CPW][NFB], sf[CPW][NFK];
+      // ---- phase A: K S, Y = diag(a)(V - K S); store outputs of c-1
       if (c >= 1) store_out(c - 1);
       if (act) {
 #pragma unroll
-        for (int f = 0; f < NFK; ++f) sf[f] = MM::template acc<NKT>(sacc, f);
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
-          floatx4 p = {0.f, 0.f, 0.f, 0.f};
-          oacc[ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+          floatx4 p[CPW];
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc) p[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
-            p = MM::mma(p, MM::template lds<NKT>(&B.K[16 * ut + li][0], f, 0), sf[f]);
-            oacc[ut] = MM::mma(oacc[ut], sf[f], MM::template lds<NKT>(&B.Q[16 * ut + li][0], f, 0));
+            const Frag kf = MM::template ldp<NKT>(&B.K[16 * ut + li][0], f);
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) p[cc] = MM::mma(p[cc], kf, sf[cc][f]);
           }
           const floatx4 al = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
-          const floatx4 vv = to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * w));
-          y[ut] = al * (vv - p);
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc) {
+            const floatx4 vv =
+                to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
+            y[cc][ut] = al * (vv - p[cc]);
+          }
         }
       }
       __syncthreads();
-      // ---- phase B: U' = T Y, O^T += U'^T M^T
+      // ---- phase B: O^T = S^T Q^T; U' = T Y; O^T += U'^T M^T
       if (act) {
-        Frag yf[NFB];
 #pragma unroll
-        for (int f = 0; f < NFB; ++f) yf[f] = MM::template acc<NB>(y, f);
-        floatx4 u[NB];
+        for (int ut = 0; ut < NB; ++ut) {
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int f = 0; f < NFK; ++f) {
+            const Frag qf = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf);
+          }
+        }
+        Frag yf[CPW][NFB];
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) yf[cc][f] = MM::template acc<NB>(y[cc], f);
+        floatx4 u[CPW][NB];
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
-          u[ut] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f)
-            u[ut] = MM::mma(u[ut], MM::template lds<ut + 1>(&B.T[16 * ut + li][0], f, 0), yf[f]);
+          for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
+            const Frag tf = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = MM::mma(u[cc][ut], tf, yf[cc][f]);
+          }
         });
 #pragma unroll
-        for (int f = 0; f < NFB; ++f) uf[f] = MM::template acc<NB>(u, f);
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) uf[cc][f] = MM::template acc<NB>(u[cc], f);
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
 #pragma unroll
-          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f)
-            oacc[ut] = MM::mma(oacc[ut], uf[f], MM::template lds<ut + 1>(&B.M[16 * ut + li][0], f, 0));
+          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
+            const Frag mf = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], uf[cc][f], mf);
+          }
         });
       }
       __syncthreads();
@@ -654,10 +711,16 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
 #pragma unroll
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
-          for (int f = 0; f < NFB; ++f)
-            sacc[rt] = MM::mma(sacc[rt], tr_frag<NB>(&B.K[0][0], LDK, f, 16 * rt), uf[f]);
+          for (int f = 0; f < NFB; ++f) {
+            const Frag kt = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
 #pragma unroll
-        for (int ut = 0; ut < NB; ++ut) MM::store_t(&sm.O[16 * ut + li][16 * w], oacc[ut]);
+            for (int cc = 0; cc < CPW; ++cc) sacc[cc][rt] = MM::mma(sacc[cc][rt], kt, uf[cc][f]);
+          }
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int ut = 0; ut < NB; ++ut)
+            MM::store_t(&sm.O[16 * ut + li][16 * (w * CPW + cc)], oacc[cc][ut]);
       }
       __syncthreads();
     }
@@ -665,14 +728,17 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
     if (owner && a.s_final) {
       float* sf = a.s_final + (size_t)head * D * D;
 #pragma unroll
-      for (int rt = 0; rt < NKT; ++rt)
+      for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sf[(size_t)(16 * rt + 4 * g + e) * D + scol] = sacc[rt][e];
+        for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + cc) + li] = sacc[cc][rt][e];
     }
   } else {
     // ======================= prep group =======================
-    const int pw = w - 4;        // prep wave 0..3
-    const int ptid = tid - 256;  // 0..255
+    const int pw = w - NSW;      // prep wave 0..3
+    const int ptid = tid - NST;  // 0..255
     const CT* qg = (const CT*)a.q + (size_t)head * T * D;
     const CT* kg = (const CT*)a.k + (size_t)head * T * D;
     const CT* vg = (const CT*)a.v + (size_t)head * T * D;
@@ -682,6 +748,7 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
     constexpr int VPRV = BV / VE;
     constexpr int NLK = (C * VPR + 255) / 256;
     constexpr int NLV = (C * VPRV + 255) / 256;
+    constexpr int RPJ = 64 / VPR;  // rows a wave stages per load slot
     Vec kreg[NLK], qreg[NLK], vreg[NLV];
     CT breg[NLK];
     auto prefetch = [&](int chunk) {
@@ -714,23 +781,21 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
       const int n = c + 1;  // chunk being prepared
       const bool act = n < nchunks;
       auto& B = sm.buf[n & 1];
-      // ---- phase A: stage chunk n; a = -expm1(-beta lambda)/lambda per row
+      // Opaque per-iteration copies of the lane coordinates: masks and
+      // identity entries derived from them are then rebuilt inside the loop
+      // instead of being hoisted out and held in registers across it.
+      int li = lane & 15, g = lane >> 4;
+      asm volatile("" : "+v"(li), "+v"(g));
+      // ---- phase A: stage chunk n (keys, queries, value slice, step sizes)
       if (act) {
 #pragma unroll
         for (int j = 0; j < NLK; ++j) {
           const int idx = ptid + 256 * j;
           if (idx < C * VPR) {
             const int r = idx / VPR, cv = idx % VPR;
-            st16(&B.K[r][cv * VE], kreg[j]);
-            st16(&B.Q[r][cv * VE], qreg[j]);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-              const float x = to_f32(kreg[j][e]);
-              ss += x * x;
-            }
-            ss = group_sum<VPR>(ss);
-            if (cv == 0) B.alpha[r] = gate_alpha(to_f32(breg[j]), ss);
+            st_perm(&B.K[r][0], cv * VE, kreg[j]);
+            st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+            if (cv == 0) sm.betas[r] = to_f32(breg[j]);
           }
         }
 #pragma unroll
@@ -744,88 +809,109 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
         if (n + 1 < nchunks) prefetch(n + 1);
       }
       __syncthreads();
-      // ---- phase B: diagonal Gram block + its inverse (wave pw = block), then
-      //      the remaining Gram (-> -A) and Q K^T (-> M) tiles.
+      // ---- phase B.
+      //  prep wave 0: the NB diagonal Gram blocks; lambda_r = ||k_r||^2 is
+      //  their diagonal; a_r = -expm1(-beta_r lambda_r)/lambda_r for all C rows
+      //  at once (lane = row); the scaled strictly-lower blocks A_bb, then
+      //  (I + A_bb)^{-1} for all blocks together by column-parallel right-
+      //  looking forward substitution in fp32 (lane group g = block g, lane li
+      //  = column li: once t_j is final, column j is eliminated from the rows
+      //  below, all independently).
+      //  prep waves 1..3: Gram tiles below the diagonal blocks (stored as
+      //  -K K^T, unscaled: a is applied in the solve) and lower-incl-diag
+      //  Q K^T tiles (-> M).
       if (act) {
-        auto gram_scaled = [&](int I, int J, floatx4 acc) {
-          const int r = 16 * I + li;
-          const int cb = 16 * J + 4 * g;
-          const float al = B.alpha[r];
-          floatx4 ad;
+        if (pw == 0) {
+          floatx4 dg[NB];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] : 0.f;
-          MM::store_t(&sm.An[r][16 * J], -ad);
-          return ad;
-        };
-        auto tile_jobs = [&](auto pwc) {
-          constexpr int PW = decltype(pwc)::value;
-          using JB = PrepJobs<NB>;
-          constexpr int NJ = (JB::N - PW + 3) / 4;  // jobs PW, PW+4, ...
-          floatx4 acc[NJ > 0 ? NJ : 1];
-          static_for<NJ>([&](auto jc) {
-            constexpr int j = PW + 4 * decltype(jc)::value;
-            constexpr int I = JB::I(j), J = JB::J(j);
-            acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
-            MM::template ll<D>(acc[decltype(jc)::value], &B.K[16 * J + li][0],
-                               JB::is_qk(j) ? &B.Q[16 * I + li][0] : &B.K[16 * I + li][0]);
-          });
-          static_for<NJ>([&](auto jc) {
-            constexpr int j = PW + 4 * decltype(jc)::value;
-            constexpr int I = JB::I(j), J = JB::J(j);
-            const floatx4 v = acc[decltype(jc)::value];
-            if constexpr (JB::is_qk(j)) {
-              const int r = 16 * I + li;
-              const int cb = 16 * J + 4 * g;
-              floatx4 m;
+          for (int I = 0; I < NB; ++I) {
+            dg[I] = floatx4{0.f, 0.f, 0.f, 0.f};
+            MM::template llp<D>(dg[I], &B.K[16 * I + li][0], &B.K[16 * I + li][0]);
+          }
+          // lane (g, li) of block I holds G[16I + li][16I + 4g + e]: the
+          // diagonal entry of row 16I + li sits in lane group li / 4, slot li % 4
+          const int src = 16 * (li >> 2) + li;
+          float lam = 0.f;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) m[e] = (cb + e <= r) ? v[e] : 0.f;
-              MM::store_t(&B.M[r][16 * J], m);
-            } else {
-              gram_scaled(I, J, v);
-            }
-          });
-        };
-        if (pw < NB) {
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-          MM::template ll<D>(acc, &B.K[16 * pw + li][0], &B.K[16 * pw + li][0]);
-          const floatx4 ad = gram_scaled(pw, pw, acc);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.Adt[pw][4 * g + e][li] = ad[e];
+          for (int I = 0; I < NB; ++I) {
+            const float dI = dg[I][li & 3];
+            const float got = __shfl(dI, src);
+            if ((lane >> 4) == I) lam = got;  // lane l handles row l (block l / 16)
+          }
+          if (lane < C) B.alpha[lane] = gate_alpha(sm.betas[lane], lam);
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        switch (pw) {
-          case 0: tile_jobs(std::integral_constant<int, 0>{}); break;
-          case 1: tile_jobs(std::integral_constant<int, 1>{}); break;
-          case 2: tile_jobs(std::integral_constant<int, 2>{}); break;
-          default: tile_jobs(std::integral_constant<int, 3>{}); break;
-        }
-        if (pw < NB) {
-          // column-parallel right-looking forward substitution in fp32 (lane
-          // li owns column li; once t_j is final, column j of A is eliminated
-          // from the rows below, all independently)
-          float t[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
+          for (int I = 0; I < NB; ++I) {
+            const float al = B.alpha[16 * I + li];
+            floatx4 ad;
 #pragma unroll
-          for (int j = 0; j < 15; ++j) {
-            floatx4 a4[4];
+            for (int e = 0; e < 4; ++e) ad[e] = (4 * g + e < li) ? al * dg[I][e] : 0.f;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) a4[q4] = *(const floatx4*)&sm.Adt[pw][j][4 * q4];
-#pragma unroll
-            for (int r = j + 1; r < 16; ++r) t[r] -= a4[r >> 2][r & 3] * t[j];
+            for (int e = 0; e < 4; ++e) sm.Adt[I][4 * g + e][li] = ad[e];
           }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (g < NB) {
+            // every 4-group of column j of A below the diagonal is read up
+            // front (39 16-byte reads): one LDS round trip instead of fifteen
+            floatx4 acol[15][4];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if ((r >> 2) == g) sm.Td[pw][r][li] = from_f32<CT>(t[r]);
+            for (int j = 0; j < 15; ++j)
+#pragma unroll
+              for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = *(const floatx4*)&sm.Adt[g][j][4 * q4];
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < 15; ++j)
+#pragma unroll
+              for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.Td[g][r][li] = from_f32<CT>(t[r]);
+          }
+        } else {
+          auto tile_jobs = [&](auto pwc) {
+            constexpr int PW = decltype(pwc)::value;  // 1..3
+            using JB = PrepJobs<NB>;
+            constexpr int NJ = (JB::N - (PW - 1) + 2) / 3;  // jobs PW-1, PW+2, ...
+            floatx4 acc[NJ > 0 ? NJ : 1];
+            static_for<NJ>([&](auto jc) {
+              constexpr int j = PW - 1 + 3 * decltype(jc)::value;
+              constexpr int I = JB::I(j), J = JB::J(j);
+              acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
+              MM::template llp<D>(acc[decltype(jc)::value], &B.K[16 * J + li][0],
+                                  JB::is_qk(j) ? &B.Q[16 * I + li][0] : &B.K[16 * I + li][0]);
+            });
+            static_for<NJ>([&](auto jc) {
+              constexpr int j = PW - 1 + 3 * decltype(jc)::value;
+              constexpr int I = JB::I(j), J = JB::J(j);
+              floatx4 v = acc[decltype(jc)::value];
+              if constexpr (JB::is_qk(j)) {
+                if constexpr (I == J) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
+                }
+                MM::store_tp(&B.M[16 * I + li][0], J, v);
+              } else {
+                MM::store_tp(&sm.An[16 * I + li][0], J, -v);
+              }
+            });
+          };
+          switch (pw) {
+            case 1: tile_jobs(std::integral_constant<int, 1>{}); break;
+            case 2: tile_jobs(std::integral_constant<int, 2>{}); break;
+            default: tile_jobs(std::integral_constant<int, 3>{}); break;
+          }
         }
       }
       __syncthreads();
       // ---- phase C: column tile m = pw of T = (I + A)^{-1}:
-      //      X_i = (I + A_ii)^{-1} (E_i - sum_{m<=j<i} A_ij X_j), i >= m, where
-      //      E is the identity; X_i^T is also formed so T is written
-      //      row-major with 8-byte stores.
+      //      X_m = (I + A_mm)^{-1},
+      //      X_i = (I + A_ii)^{-1} diag(a_i) sum_{m<=j<i} (-K_i K_j^T) X_j, i > m;
+      //      X_i^T is also formed so T is written row-major with 8-byte stores.
       if (act && pw < NB) {
         auto col_tile = [&](auto mc) {
           constexpr int m = decltype(mc)::value;
@@ -834,9 +920,11 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
             constexpr int i = decltype(ib)::value;
             if constexpr (i >= m) {
               floatx4 yv;
+              if constexpr (i == m) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) yv[e] = (i == m && 4 * g + e == li) ? 1.f : 0.f;
-              if constexpr (i > m) {
+                for (int e = 0; e < 4; ++e) yv[e] = (4 * g + e == li) ? 1.f : 0.f;
+              } else {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int f = 0; f < NFrag<CT, i>::value; ++f) {
                   if constexpr (MM::KT == 2) {
@@ -845,15 +933,16 @@ __global__ __launch_bounds__(512, 1) void efla_chunked_pipe_kernel(ChunkedArgs a
                     if (f < m) continue;
                   }
                   floatx4 xin[2] = {x[MM::KT * f], MM::KT == 2 && 2 * f + 1 < i ? x[2 * f + 1] : x[MM::KT * f]};
-                  yv = MM::mma(yv, MM::template lds<i>(&sm.An[16 * i + li][0], f, 0),
-                               MM::template acc<(MM::KT == 2 ? 2 : 1)>(xin, 0));
+                  acc = MM::mma(acc, MM::template ldp<i>(&sm.An[16 * i + li][0], f),
+                                MM::template acc<(MM::KT == 2 ? 2 : 1)>(xin, 0));
                 }
+                yv = *(const floatx4*)&B.alpha[16 * i + 4 * g] * acc;
               }
               const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
               const Frag yf = MM::template acc<1>(&yv, 0);
               x[i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
               const floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
-              MM::store_t(&B.T[16 * i + li][16 * m], xt);
+              MM::store_tp(&B.T[16 * i + li][0], m, xt);
             } else {
               x[i] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
@@ -880,7 +969,9 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, hipStream_t stre
   a.nvt = D / BV;
   dim3 grid((unsigned)(NH * a.nvt));
   if constexpr (pipe_smem_bytes<CT, D, C, BV>() <= 160 * 1024) {
-    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV>), grid, dim3(512), 0, stream, a);
+    constexpr int NSW = EFLA_PIPE_STATE_WAVES;
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW>), grid, dim3(64 * (NSW + 4)), 0,
+                       stream, a);
   } else {
     static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");
     hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, BV, EFLA_STATE_WAVES>), grid, dim3(256), 0,

@@ -79,9 +79,18 @@ struct Mma;
 
 template <>
 struct Mma<bf16> {
-  static constexpr int PAD = 4;  // row padding (elements): 8-byte offset between rows
-  static constexpr int KT = 2;   // 16-row tiles per fragment
+  static constexpr int PAD = 4;   // row padding (elements) of unpermuted tiles
+  static constexpr int PADP = 8;  // row padding of column-permuted tiles (16-byte rows)
+  static constexpr int KT = 2;    // 16-row tiles per fragment
   typedef bf16x8 Frag;
+
+  // Column-permuted LDS layout (used by the pipelined kernel): inside every
+  // 32-column block, column 16h + 4g + e is stored at position 8g + 4h + e,
+  // so the 8 elements lane group g needs for one fragment (columns 4g..4g+3
+  // of both 16-column tiles) are one 16-byte read.
+  __device__ __forceinline__ static constexpr int pcol(int c) {
+    return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+  }
 
   __device__ __forceinline__ static floatx4 mma(floatx4 c, Frag a, Frag b) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -99,7 +108,8 @@ struct Mma<bf16> {
     if (2 * f + 1 < NR) hi = cvt4(t[2 * f + 1]);
     return cat(cvt4(t[2 * f]), hi);
   }
-  // Fragment f of an LDS row restricted to NR tiles.
+  // Fragment f of an unpermuted LDS row (k contiguous), restricted to NR tiles:
+  // columns 32f + 4g.. and 32f + 16 + 4g.., XOR-swizzled by swz.
   template <int NR>
   __device__ __forceinline__ static Frag lds(const bf16* row, int f, int swz) {
     const int g = lane_id() >> 4;
@@ -108,8 +118,15 @@ struct Mma<bf16> {
     if (2 * f + 1 < NR) hi = *(const bf16x4*)(row + ((32 * f + 16 + 4 * g) ^ swz));
     return cat(lo, hi);
   }
+  // Fragment f of a column-permuted LDS row (16-byte aligned), NR tiles.
+  template <int NR>
+  __device__ __forceinline__ static Frag ldp(const bf16* row, int f) {
+    const int g = lane_id() >> 4;
+    if (2 * f + 1 < NR) return *(const bf16x8*)(row + 32 * f + 8 * g);
+    return cat(*(const bf16x4*)(row + 32 * f + 8 * g), bf16x4{});
+  }
   // c += A[16 x K] * B[K x 16] with A row and B column from LDS, natural k
-  // order (8 contiguous elements per lane). K is a multiple of 16.
+  // order (8 contiguous elements per lane, 8-byte aligned). K % 16 == 0.
   template <int K>
   __device__ __forceinline__ static void ll(floatx4& c, const bf16* arow, const bf16* bcol) {
     const int g = lane_id() >> 4;
@@ -125,6 +142,14 @@ struct Mma<bf16> {
       c = mma(c, a, b);
     }
   }
+  // Same product for two column-permuted rows (16-byte reads; the k order is
+  // the permuted one, identical for both operands).
+  template <int K>
+  __device__ __forceinline__ static void llp(floatx4& c, const bf16* arow, const bf16* bcol) {
+#pragma unroll
+    for (int f = 0; f < (K + 31) / 32; ++f)
+      c = mma(c, ldp<K / 16>(arow, f), ldp<K / 16>(bcol, f));
+  }
   // 8 contiguous elements from an 8-byte aligned LDS address (two 8-byte reads).
   __device__ __forceinline__ static bf16x8 ld8(const bf16* p) {
     return cat(*(const bf16x4*)p, *(const bf16x4*)(p + 4));
@@ -134,6 +159,11 @@ struct Mma<bf16> {
     const int g = lane_id() >> 4;
     *(bf16x4*)(dst_row + 4 * g) = cvt4(v);
   }
+  // Accumulator tile -> columns 16 J + 4g .. + 3 of a column-permuted row.
+  __device__ __forceinline__ static void store_tp(bf16* row, int J, floatx4 v) {
+    const int g = lane_id() >> 4;
+    *(bf16x4*)(row + pcol(16 * J + 4 * g)) = cvt4(v);
+  }
   __device__ __forceinline__ static floatx4 load4(const bf16* p) {
     return __builtin_convertvector(*(const bf16x4*)p, floatx4);
   }
@@ -142,8 +172,12 @@ struct Mma<bf16> {
 template <>
 struct Mma<float> {
   static constexpr int PAD = 4;
+  static constexpr int PADP = 4;
   static constexpr int KT = 1;
   typedef floatx4 Frag;  // the four k-slices of one tile
+
+  // fp32 fragments are already one 16-byte read: no column permutation.
+  __device__ __forceinline__ static constexpr int pcol(int c) { return c; }
 
   __device__ __forceinline__ static floatx4 mma(floatx4 c, Frag a, Frag b) {
 #pragma unroll
@@ -166,9 +200,22 @@ struct Mma<float> {
     for (int k0 = 0; k0 < K; k0 += 4)
       c = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[k0 + g], bcol[k0 + g], c, 0, 0, 0);
   }
+  template <int NR>
+  __device__ __forceinline__ static Frag ldp(const float* row, int f) {
+    const int g = lane_id() >> 4;
+    return *(const floatx4*)(row + 16 * f + 4 * g);
+  }
+  template <int K>
+  __device__ __forceinline__ static void llp(floatx4& c, const float* arow, const float* bcol) {
+    ll<K>(c, arow, bcol);
+  }
   __device__ __forceinline__ static void store_t(float* dst_row, floatx4 v) {
     const int g = lane_id() >> 4;
     *(floatx4*)(dst_row + 4 * g) = v;
+  }
+  __device__ __forceinline__ static void store_tp(float* row, int J, floatx4 v) {
+    const int g = lane_id() >> 4;
+    *(floatx4*)(row + 16 * J + 4 * g) = v;
   }
   __device__ __forceinline__ static floatx4 load4(const float* p) { return *(const floatx4*)p; }
 };
@@ -190,12 +237,15 @@ __device__ __forceinline__ floatx4 ld16(const float* p) { return *(const floatx4
 //   addresses row row0 + m, columns col0 + 4a .. col0 + 4a + 3, and the
 //   instruction returns to lane 4a + b column col0 + 4a + b of those four rows.
 //   fp32: four 4-byte reads.
+template <bool PERM = false>
 __device__ __forceinline__ bf16x4 ldtr4(const bf16* base, int ld, int row0, int col0) {
   const int li = lane_id() & 15;
-  const bf16* p = base + (row0 + (li >> 2)) * ld + col0 + 4 * (li & 3);
+  const int col = col0 + 4 * (li & 3);
+  const bf16* p = base + (row0 + (li >> 2)) * ld + (PERM ? Mma<bf16>::pcol(col) : col);
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
       (__attribute__((address_space(3))) bf16x4*)(p));
 }
+template <bool PERM = false>
 __device__ __forceinline__ floatx4 ldtr4(const float* base, int ld, int row0, int col0) {
   const int li = lane_id() & 15;
   const float* p = base + row0 * ld + col0 + li;
@@ -207,18 +257,18 @@ __device__ __forceinline__ floatx4 to_f32x4(floatx4 v) { return v; }
 // Fragment f (k over rows 32f.. or 16f.. of a row-major tile) of the
 // transposed tile, for a 16-column block at col0: lane i gets column col0 + i.
 // NR bounds the row tiles present.
-template <int NR>
+template <int NR, bool PERM = false>
 __device__ __forceinline__ bf16x8 tr_frag(const bf16* base, int ld, int f, int col0) {
   const int g = lane_id() >> 4;
-  bf16x4 lo = ldtr4(base, ld, 32 * f + 4 * g, col0);
+  bf16x4 lo = ldtr4<PERM>(base, ld, 32 * f + 4 * g, col0);
   bf16x4 hi = {};
-  if (2 * f + 1 < NR) hi = ldtr4(base, ld, 32 * f + 16 + 4 * g, col0);
+  if (2 * f + 1 < NR) hi = ldtr4<PERM>(base, ld, 32 * f + 16 + 4 * g, col0);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int NR>
+template <int NR, bool PERM = false>
 __device__ __forceinline__ floatx4 tr_frag(const float* base, int ld, int f, int col0) {
   const int g = lane_id() >> 4;
-  return ldtr4(base, ld, 16 * f + 4 * g, col0);
+  return ldtr4<PERM>(base, ld, 16 * f + 4 * g, col0);
 }
 
 // Number of fragments covering NR 16-row tiles.
