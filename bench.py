@@ -4,8 +4,8 @@ One step = one chunked EFLA forward (gate, Gram, UT solve, WY factors, state
 passing, outputs and final state) over the whole synthetic workload, with
 inputs already resident in HBM. Prints one JSON line with head-tokens/s
 (B*H*T per second), the roofline position of the kernel, the fp64 CPU oracle
-timed on this host on a bounded sample, and the single-token decode step
-measured on the 340M-layer shape.
+timed on this host over whole passes of the same workload (about ten
+seconds), and the single-token decode step measured on the 340M-layer shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -22,6 +22,56 @@ sys.path.insert(0, ROOT)
 
 METRIC = "EFLA fwd tokens/s at B·H·T, d=128 (1 MI355X); % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_FLOPS = 2.5166e15
+KERNEL_SOURCES = ("delta_rule_recurrent_efla_amd/csrc/efla_chunked.hip",
+                  "delta_rule_recurrent_efla_amd/csrc/efla_device.hpp",
+                  "delta_rule_recurrent_efla_amd/build.py")
+COPY_CAL_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the chunked kernel's sources and build flags: HBM-traffic
+    counters taken for one build are only reported for that same build."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the chunked kernel on ``workload`` from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when there is
+    none or it was taken for other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"efla_chunked_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "-")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, reps: int = 5):
+    """A plain device copy of COPY_CAL_BYTES (fp32) so that a rocprofv3 --pmc
+    run of this script records FETCH_SIZE / WRITE_SIZE for a kernel of known
+    traffic next to the EFLA kernel; the ratio scales the EFLA counters."""
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def alg_bytes_fwd(w, with_s0: bool) -> int:
@@ -62,21 +112,29 @@ def time_launches(fn, steps, warmup, stream):
     return t_all0.elapsed_time(t_all1), per
 
 
-def cpu_baseline(w, x, budget_heads: int):
+def cpu_baseline(w, x, min_seconds: float, max_threads: int = 16):
+    """The fp64 oracle on the same inputs, over whole passes of the workload
+    (all heads, full T) until ``min_seconds`` of wall time have passed."""
     import oracle
 
-    nthreads = max(1, min(16, os.cpu_count() or 1))
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
     nh = w.B * w.H
-    nsel = max(1, min(nh, budget_heads))
-    f = lambda t: None if t is None else t.reshape((nh,) + tuple(t.shape[2:]))[:nsel]
-    args = [f(x["q"]), f(x["k"]), f(x["v"]), f(x["beta"]), f(x["s0"])]
-    use = min(nthreads, nsel)
-    t0 = time.perf_counter()
-    oracle.fwd(*args, nthreads=use)
-    dt = time.perf_counter() - t0
-    return {"value": nsel * w.T / dt, "unit": "head-tokens/s", "cores": use, "kind": "oracle",
-            "sample": f"{nsel} of {nh} heads, full T={w.T}, fp64 sequential recurrence, "
-                      f"{use} threads, {dt:.2f} s wall"}
+    use = max(1, min(max_threads, avail, nh))
+    args = [x["q"], x["k"], x["v"], x["beta"], x["s0"]]
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.fwd(*args, nthreads=use)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": passes * w.head_tokens / dt, "unit": "head-tokens/s", "cores": use,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over the whole workload ({nh} heads x T={w.T}), "
+                      f"fp64 sequential recurrence, {use} threads, {dt:.1f} s wall"}
 
 
 def bench_decode(efla, torch, efla_inputs, steps=256):
@@ -115,7 +173,9 @@ def main():
     ap.add_argument("--workload", default="layer1p3b_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (HBM-counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,6 +209,7 @@ def main():
     nbytes = alg_bytes_fwd(w, g["s0"] is not None)
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     flops = alg_flops_fwd(w)
+    traffic = measured_traffic(w.name)
 
     res = {
         "metric": METRIC,
@@ -167,15 +228,18 @@ def main():
                    "chunk": w.chunk, "head_tokens": w.head_tokens,
                    "s0": g["s0"] is not None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "alg_bytes_per_launch": nbytes,
                      "avg_launch_ms": avg_launch_ms,
-                     "mfma_bf16_frac": flops / (avg_launch_ms * 1e-3) / 2.5166e15},
+                     "kernel": "efla_chunked_pipe_kernel",
+                     "mfma_bf16_frac": flops / (avg_launch_ms * 1e-3) / BF16_PEAK_FLOPS},
     }
     if not args.no_decode:
         res["decode"] = bench_decode(efla, torch, efla_inputs)
+    if args.copy_calibration:
+        copy_calibration(torch)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -28,6 +28,13 @@ FLAGS = [
     "-fPIC",
     # keep the compiler from emitting packed-fp32 VALU ops on the device
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no sinking of look-alike code out of the per-wave role branches into a
+    # common successor: with it, the chunked kernel's tile-job dispatch was
+    # compiled so that one wave stored its Q K^T tile through an address
+    # register that was never set on its path (tile (1,0) of a 32-row chunk
+    # landed on (1,1)); with each branch keeping its own stores, every store
+    # has its constant offset
+    "-mllvm", "-simplifycfg-sink-common=false",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

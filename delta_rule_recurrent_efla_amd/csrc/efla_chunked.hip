@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches stay scalar
   const int li = lane & 15;
   const int g = lane >> 4;
 
@@ -581,7 +581,8 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;  // 0..NSW-1 state group, NSW..NSW+3 prep group
+  // wave-uniform (scalar), so role dispatch compiles to scalar branches
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..NSW-1 state, NSW..NSW+3 prep
   const int li = lane & 15;
   const int g = lane >> 4;
 
