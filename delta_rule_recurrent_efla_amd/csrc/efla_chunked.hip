@@ -520,7 +520,8 @@ struct __attribute__((aligned(16))) PipeSmem {
     float alpha[C];
   } buf[2];
   CT An[C][CP];           // -(K K^T), permuted, blocks below the diagonal (prep-private)
-  float Adt[NB][16][20];  // fp32 diagonal blocks of A, transposed (prep-private)
+  float Adt[NB][17][20];  // fp32 diagonal blocks of A, transposed; the 17th row
+                          // staggers the blocks over the LDS banks (prep-private)
   CT Td[NB][16][16 + P];  // (I + A_bb)^{-1}, natural layout (prep-private)
   CT O[C][BV + P];        // output staging (state group)
   float betas[C];         // step sizes of the chunk being prepared (prep-private)
@@ -532,8 +533,8 @@ constexpr size_t pipe_smem_bytes() {
 }
 
 // Gram tiles below the diagonal blocks and lower-incl-diag Q K^T tiles,
-// enumerated (I, J) row by row; job j goes to prep wave 1 + j % 3 (prep wave 0
-// owns the diagonal Gram blocks).
+// enumerated (I, J) row by row; job j goes to prep wave 2 + j % 2 (prep
+// waves 0 and 1 own the diagonal Gram blocks).
 template <int NB>
 struct PrepJobs {
   static constexpr int NOFF = NB * (NB - 1) / 2;
@@ -623,9 +624,18 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
       const int t0 = chunk * C;
       const int nval = min(C, T - t0);
       constexpr int VPRO = BV / VE;
-      for (int idx = tid; idx < C * VPRO; idx += NST) {
+      constexpr int NO = (C * VPRO + NST - 1) / NST;
+      Vec ov[NO];
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const int idx = tid + NST * j;
+        if (idx < C * VPRO) ov[j] = ld16(&sm.O[idx / VPRO][(idx % VPRO) * VE]);
+      }
+#pragma unroll
+      for (int j = 0; j < NO; ++j) {
+        const int idx = tid + NST * j;
         const int r = idx / VPRO, cv = idx % VPRO;
-        if (r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = ld16(&sm.O[r][cv * VE]);
+        if (idx < C * VPRO && r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = ov[j];
       }
     };
 
@@ -810,84 +820,97 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
         if (n + 1 < nchunks) prefetch(n + 1);
       }
       __syncthreads();
-      // ---- phase B.
-      //  prep wave 0: the NB diagonal Gram blocks; lambda_r = ||k_r||^2 is
-      //  their diagonal; a_r = -expm1(-beta_r lambda_r)/lambda_r for all C rows
-      //  at once (lane = row); the scaled strictly-lower blocks A_bb, then
-      //  (I + A_bb)^{-1} for all blocks together by column-parallel right-
-      //  looking forward substitution in fp32 (lane group g = block g, lane li
-      //  = column li: once t_j is final, column j is eliminated from the rows
-      //  below, all independently).
-      //  prep waves 1..3: Gram tiles below the diagonal blocks (stored as
-      //  -K K^T, unscaled: a is applied in the solve) and lower-incl-diag
-      //  Q K^T tiles (-> M).
+      // ---- phase B. Prep waves 0 and 1 (each alone on its SIMD) own the
+      //  diagonal blocks b = pw, pw + 2: G_bb = K_b K_b^T; lambda_r = ||k_r||^2
+      //  is its diagonal and a_r = -expm1(-beta_r lambda_r)/lambda_r for the
+      //  block's rows (every lane holds a_r of its row: no LDS round trip); the
+      //  scaled strictly-lower block A_bb = diag(a_b) strictly-lower(G_bb), and
+      //  (I + A_bb)^{-1} by column-parallel right-looking forward substitution
+      //  in fp32 (lane group g = block pw + 2g, lane li = column li: once t_j
+      //  is final, column j is eliminated from the rows below, all
+      //  independently).
+      //  Prep waves 2 and 3 (which share their SIMDs with the state waves)
+      //  take the Gram tiles below the diagonal blocks (stored as -K K^T,
+      //  unscaled: a is applied in the solve) and the lower-incl-diag Q K^T
+      //  tiles (-> M), alternately.
       if (act) {
-        if (pw == 0) {
-          floatx4 dg[NB];
+        if (pw < 2) {
+          auto diag = [&](auto pwc) {
+            constexpr int PW = decltype(pwc)::value;           // 0..1
+            constexpr int NDB = NB > PW ? (NB - PW + 1) / 2 : 0;  // blocks PW, PW + 2
+            if constexpr (NDB > 0) {
+              floatx4 dg[NDB];
 #pragma unroll
-          for (int I = 0; I < NB; ++I) {
-            dg[I] = floatx4{0.f, 0.f, 0.f, 0.f};
-            MM::template llp<D>(dg[I], &B.K[16 * I + li][0], &B.K[16 * I + li][0]);
-          }
-          // lane (g, li) of block I holds G[16I + li][16I + 4g + e]: the
-          // diagonal entry of row 16I + li sits in lane group li / 4, slot li % 4
-          const int src = 16 * (li >> 2) + li;
-          float lam = 0.f;
+              for (int i = 0; i < NDB; ++i) {
+                dg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+                MM::template llp<D>(dg[i], &B.K[16 * (PW + 2 * i) + li][0], &B.K[16 * (PW + 2 * i) + li][0]);
+              }
 #pragma unroll
-          for (int I = 0; I < NB; ++I) {
-            const float dI = dg[I][li & 3];
-            const float got = __shfl(dI, src);
-            if ((lane >> 4) == I) lam = got;  // lane l handles row l (block l / 16)
-          }
-          if (lane < C) B.alpha[lane] = gate_alpha(sm.betas[lane], lam);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              for (int i = 0; i < NDB; ++i) {
+                const int b = PW + 2 * i;
+                // lane (g, li) holds G[4g + e][li] = G[li][4g + e]; the diagonal
+                // entry of row li sits in lane 16 (li / 4) + li, slot li % 4
+                const float lam = __shfl(dg[i][li & 3], 16 * (li >> 2) + li);
+                const float al = gate_alpha(sm.betas[16 * b + li], lam);
+                if (g == 0) B.alpha[16 * b + li] = al;
 #pragma unroll
-          for (int I = 0; I < NB; ++I) {
-            const float al = B.alpha[16 * I + li];
-            floatx4 ad;
+                for (int e = 0; e < 4; ++e) sm.Adt[b][4 * g + e][li] = (4 * g + e < li) ? al * dg[i][e] : 0.f;
+              }
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              if (g < NDB) {
+                const float* Ab = &sm.Adt[PW + 2 * g][0][0];
+                // The 4-groups of column j of A below the diagonal are read in
+                // two batches (columns 0-6, then 7-14, issued after three
+                // elimination steps): two LDS round trips instead of fifteen,
+                // while the second batch reuses the registers of the first.
+                floatx4 acol[15][4];
+                float t[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ad[e] = (4 * g + e < li) ? al * dg[I][e] : 0.f;
+                for (int j = 0; j < 7; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Adt[I][4 * g + e][li] = ad[e];
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          if (g < NB) {
-            // every 4-group of column j of A below the diagonal is read up
-            // front (39 16-byte reads): one LDS round trip instead of fifteen
-            floatx4 acol[15][4];
+                  for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = *(const floatx4*)&Ab[20 * j + 4 * q4];
 #pragma unroll
-            for (int j = 0; j < 15; ++j)
+                for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
 #pragma unroll
-              for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = *(const floatx4*)&sm.Adt[g][j][4 * q4];
-            float t[16];
+                for (int j = 0; j < 15; ++j) {
+                  if (j == 3) {
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
+                    for (int jj = 7; jj < 15; ++jj)
 #pragma unroll
-            for (int j = 0; j < 15; ++j)
+                      for (int q4 = (jj + 1) >> 2; q4 < 4; ++q4)
+                        acol[jj][q4] = *(const floatx4*)&Ab[20 * jj + 4 * q4];
+                    __builtin_amdgcn_sched_barrier(0);
+                  }
 #pragma unroll
-              for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
+                  for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
+                }
+                CT* Tb = &sm.Td[PW + 2 * g][0][0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.Td[g][r][li] = from_f32<CT>(t[r]);
-          }
+                for (int r = 0; r < 16; ++r) Tb[(16 + Sm::P) * r + li] = from_f32<CT>(t[r]);
+              }
+            }
+          };
+          if (pw == 0) diag(std::integral_constant<int, 0>{});
+          else diag(std::integral_constant<int, 1>{});
         } else {
           auto tile_jobs = [&](auto pwc) {
-            constexpr int PW = decltype(pwc)::value;  // 1..3
+            constexpr int PW = decltype(pwc)::value;  // 2..3
             using JB = PrepJobs<NB>;
-            constexpr int NJ = (JB::N - (PW - 1) + 2) / 3;  // jobs PW-1, PW+2, ...
+            constexpr int J0 = PW - 2;
+            constexpr int NJ = JB::N > J0 ? (JB::N - J0 + 1) / 2 : 0;  // jobs J0, J0 + 2, ...
             floatx4 acc[NJ > 0 ? NJ : 1];
             static_for<NJ>([&](auto jc) {
-              constexpr int j = PW - 1 + 3 * decltype(jc)::value;
+              constexpr int j = J0 + 2 * decltype(jc)::value;
               constexpr int I = JB::I(j), J = JB::J(j);
               acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
               MM::template llp<D>(acc[decltype(jc)::value], &B.K[16 * J + li][0],
                                   JB::is_qk(j) ? &B.Q[16 * I + li][0] : &B.K[16 * I + li][0]);
             });
             static_for<NJ>([&](auto jc) {
-              constexpr int j = PW - 1 + 3 * decltype(jc)::value;
+              constexpr int j = J0 + 2 * decltype(jc)::value;
               constexpr int I = JB::I(j), J = JB::J(j);
               floatx4 v = acc[decltype(jc)::value];
               if constexpr (JB::is_qk(j)) {
@@ -901,11 +924,8 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
               }
             });
           };
-          switch (pw) {
-            case 1: tile_jobs(std::integral_constant<int, 1>{}); break;
-            case 2: tile_jobs(std::integral_constant<int, 2>{}); break;
-            default: tile_jobs(std::integral_constant<int, 3>{}); break;
-          }
+          if (pw == 2) tile_jobs(std::integral_constant<int, 2>{});
+          else tile_jobs(std::integral_constant<int, 3>{});
         }
       }
       __syncthreads();
