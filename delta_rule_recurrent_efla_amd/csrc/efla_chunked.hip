@@ -489,42 +489,53 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 }
 
 // ===========================================================================
-// Pipelined variant: 8 waves per workgroup. Waves 0-3 (state group) run the
-// serial state pass of chunk c while waves 4-7 (prep group) prepare chunk c+1,
-// so on every SIMD one wave's MFMA stream overlaps the other's latency-bound
-// prep. The prep produces, per chunk, A = strictly-lower(diag(a) K K^T),
-// T = (I + A)^{-1} (full, lower triangular), M = lower-incl-diag(Q K^T) and a;
-// the state pass then needs no WY factor:
+// Pipelined variant: NSW state waves plus four prep waves per workgroup. The
+// state waves run the serial state pass of chunk c while the prep waves
+// prepare chunk c+1. The prep produces, per chunk, a, the diagonal-block
+// inverses, T = (I + A)^{-1} with A = strictly-lower(diag(a) K K^T) (full,
+// lower triangular) and M = lower-incl-diag(Q K^T); the state pass then needs
+// no WY factor:
 //   Y  = diag(a) (V - K S)
 //   U' = T Y                       (= U - W S with W = T diag(a) K, U = T diag(a) V)
 //   O^T = S^T Q^T + U'^T M^T       (read out after each update)
 //   S <- S + K^T U'
+// Two workgroup barriers per chunk split it into phases A and B:
+//   state waves    A: K S, Y; S^T Q^T            B: T Y, U'^T M^T, K^T U'; store O
+//   prep 0, 1      A: diagonal Gram blocks from  B: Gram tiles below the diagonal,
+//   ("solvers")       registers, a, (I+A_bb)^-1     column tiles of T
+//   prep 2..5      A: stage K, Q, V into LDS;    B: Q K^T tiles (M); load the
+//   ("loaders")       load the next chunk's K       next chunk's Q, V
+// Waves are placed on the SIMDs round robin: the two state waves and the two
+// solvers get a SIMD each, and every SIMD also runs one loader. Every global
+// load is issued as soon as its registers are free and consumed one chunk
+// later.
 // K, Q, V, T, M and a are double-buffered in LDS; K^T and the columns of V
-// are read with ds_read_b64_tr_b16 straight from the row-major tiles. Both
-// groups pass three workgroup barriers per chunk.
+// are read with ds_read_b64_tr_b16 straight from the row-major tiles.
 template <typename CT, int D, int C, int BV>
 struct __attribute__((aligned(16))) PipeSmem {
-  static constexpr int P = Mma<CT>::PAD;
-  static constexpr int PP = Mma<CT>::PADP;
   static constexpr int NB = C / 16;
-  // the column permutation acts inside 32-column blocks: permuted rows hold
-  // at least 32 positions
-  static constexpr int DP = (D < 32 ? 32 : D) + PP;
-  static constexpr int CP = (C < 32 ? 32 : C) + PP;
+  // Row strides: on gfx950 the 16-byte fragment reads and the transposed
+  // 8-byte reads of a tile are free of bank conflicts when the row stride is
+  // 32 bytes modulo 64 (measured: an odd multiple of 32 bytes halves their
+  // LDS cycles against the other strides). The column permutation acts
+  // inside 32-column blocks, so permuted rows hold at least 32 positions.
+  static constexpr int RP = 32 / (int)sizeof(CT);
+  static constexpr int DP = (D < 32 ? 32 : D) + RP;
+  static constexpr int CP = (C < 32 ? 32 : C) + RP;
+  static constexpr int VS = BV + ((32 - (int)sizeof(CT) * BV % 64 + 64) % 64) / (int)sizeof(CT);
+  static constexpr int TDS = 32 / (int)sizeof(CT) + (sizeof(CT) == 4 ? 16 : 0);  // 32 or 96 bytes
   struct Buf {
     CT K[C][DP];       // keys, column-permuted rows
     CT Q[C][DP];       // queries, column-permuted rows
-    CT V[C][BV + P];   // value slice, natural layout
+    CT V[C][VS];       // value slice, natural layout
     CT T[C][CP];       // (I + A)^{-1}, permuted; only the lower block triangle is read
     CT M[C][CP];       // lower-incl-diag(Q K^T), permuted; only J <= I blocks are read
     float alpha[C];
   } buf[2];
-  CT An[C][CP];           // -(K K^T), permuted, blocks below the diagonal (prep-private)
+  CT An[2][C][CP];        // -(K K^T) blocks below the diagonal, permuted, one copy per solver
   float Adt[NB][17][20];  // fp32 diagonal blocks of A, transposed; the 17th row
-                          // staggers the blocks over the LDS banks (prep-private)
-  CT Td[NB][16][16 + P];  // (I + A_bb)^{-1}, natural layout (prep-private)
-  CT O[C][BV + P];        // output staging (state group)
-  float betas[C];         // step sizes of the chunk being prepared (prep-private)
+                          // staggers the blocks over the LDS banks
+  CT Td[NB][16][TDS];     // (I + A_bb)^{-1}, natural layout
 };
 
 template <typename CT, int D, int C, int BV>
@@ -533,8 +544,7 @@ constexpr size_t pipe_smem_bytes() {
 }
 
 // Gram tiles below the diagonal blocks and lower-incl-diag Q K^T tiles,
-// enumerated (I, J) row by row; job j goes to prep wave 2 + j % 2 (prep
-// waves 0 and 1 own the diagonal Gram blocks).
+// enumerated (I, J) row by row.
 template <int NB>
 struct PrepJobs {
   static constexpr int NOFF = NB * (NB - 1) / 2;
@@ -551,6 +561,21 @@ struct PrepJobs {
   }
 };
 
+// Column tile m of T goes to solver 0 when it is the first or (with four
+// tiles) the last one, else to solver 1: with NB = 4 the dependent chains are
+// 3 + 0 and 2 + 1 block steps.
+template <int NB>
+__host__ __device__ constexpr int t_owner(int m) {
+  return NB == 4 ? ((m == 0 || m == 3) ? 0 : 1) : (m == 0 ? 0 : 1);
+}
+template <int NB>
+__host__ __device__ constexpr int t_first(int pw) {
+  int f = NB;
+  for (int m = NB - 1; m >= 0; --m)
+    if (t_owner<NB>(m) == pw) f = m;
+  return f;
+}
+
 // 16-byte register vector of 8 (bf16) or 4 (fp32) consecutive columns
 // starting at c0 -> column-permuted LDS row.
 __device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
@@ -560,7 +585,7 @@ __device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
 __device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
 
 template <typename CT, int D, int C, int BV, int NSW>
-__global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
+__global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
   using Vec = typename Vec16<CT>::type;
@@ -574,16 +599,19 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
   constexpr int NFK = NFrag<CT, NKT>::value;
   constexpr int NFB = NFrag<CT, NB>::value;
   constexpr int LDK = Sm::DP;
-  constexpr int LDV = BV + Sm::P;
+  constexpr int LDV = Sm::VS;
   constexpr int NST = 64 * NSW;  // state-group threads
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
+  static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
+                    (Sm::VS * sizeof(CT)) % 64 == 32 && (Sm::TDS * sizeof(CT)) % 64 == 32,
+                "row strides");
 
   __shared__ Sm sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform (scalar), so role dispatch compiles to scalar branches
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..NSW-1 state, NSW..NSW+3 prep
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..NSW-1 state, then 2 solvers, 4 loaders
   const int li = lane & 15;
   const int g = lane >> 4;
 
@@ -597,9 +625,8 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
   const int nchunks = (T + C - 1) / C;
 
   if (w < NSW) {
-    // ======================= state group =======================
+    // ======================= state waves =======================
     const bool owner = w < SW;
-    CT* og = (CT*)a.o + (size_t)head * T * D;
     floatx4 sacc[CPW][NKT];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -620,37 +647,36 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
       for (int rt = 0; rt < NKT; ++rt) asm volatile("" : "+v"(sacc[c][rt]));
 
-    auto store_out = [&](int chunk) {
-      const int t0 = chunk * C;
-      const int nval = min(C, T - t0);
-      constexpr int VPRO = BV / VE;
-      constexpr int NO = (C * VPRO + NST - 1) / NST;
-      Vec ov[NO];
-#pragma unroll
-      for (int j = 0; j < NO; ++j) {
-        const int idx = tid + NST * j;
-        if (idx < C * VPRO) ov[j] = ld16(&sm.O[idx / VPRO][(idx % VPRO) * VE]);
-      }
-#pragma unroll
-      for (int j = 0; j < NO; ++j) {
-        const int idx = tid + NST * j;
-        const int r = idx / VPRO, cv = idx % VPRO;
-        if (idx < C * VPRO && r < nval) *(Vec*)(og + (size_t)(t0 + r) * D + v0 + cv * VE) = ov[j];
-      }
-    };
-
+    __syncthreads();  // a of the first chunk
     for (int c = -1; c < nchunks; ++c) {
       const bool act = c >= 0 && owner;
       const auto& B = sm.buf[c & 1];
       floatx4 oacc[CPW][NB], y[CPW][NB];
-      Frag uf[CPW][NFB], sf[CPW][NFK];
-      // ---- phase A: K S, Y = diag(a)(V - K S); store outputs of c-1
-      if (c >= 1) store_out(c - 1);
+      Frag sf[CPW][NFK];
+      // ---- phase A: K S, Y = diag(a)(V - K S); O^T = S^T Q^T. All K
+      //      fragments (and V, a) are requested first, the Q fragments while
+      //      the K S products run: one exposed LDS round trip, not one per
+      //      fragment
       if (act) {
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
+        Frag kf[NB][NFK];
+        floatx4 al[NB], vv[CPW][NB];
+#pragma unroll
+        for (int ut = 0; ut < NB; ++ut)
+#pragma unroll
+          for (int f = 0; f < NFK; ++f) kf[ut][f] = MM::template ldp<NKT>(&B.K[16 * ut + li][0], f);
+#pragma unroll
+        for (int ut = 0; ut < NB; ++ut) {
+          al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc)
+            vv[cc][ut] = to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Frag qf[NB][NFK];
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
           floatx4 p[CPW];
@@ -658,38 +684,43 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
           for (int cc = 0; cc < CPW; ++cc) p[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
-            const Frag kf = MM::template ldp<NKT>(&B.K[16 * ut + li][0], f);
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) p[cc] = MM::mma(p[cc], kf, sf[cc][f]);
+            for (int cc = 0; cc < CPW; ++cc) p[cc] = MM::mma(p[cc], kf[ut][f], sf[cc][f]);
+            qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
           }
-          const floatx4 al = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) {
-            const floatx4 vv =
-                to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
-            y[cc][ut] = al * (vv - p[cc]);
-          }
+          for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (vv[cc][ut] - p[cc]);
         }
-      }
-      __syncthreads();
-      // ---- phase B: O^T = S^T Q^T; U' = T Y; O^T += U'^T M^T
-      if (act) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
-            const Frag qf = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf);
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
           }
         }
-        Frag yf[CPW][NFB];
+      }
+      __syncthreads();
+      // ---- phase B: U' = T Y; S += K^T U'; O^T += U'^T M^T; store O. T
+      //      fragments first, K^T fragments while T Y runs, M fragments while
+      //      K^T U' runs
+      if (act) {
+        Frag yf[CPW][NFB], uf[CPW][NFB];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) yf[cc][f] = MM::template acc<NB>(y[cc], f);
+        Frag tf[NB][NFB];
+        static_for<NB>([&](auto ub) {
+          constexpr int ut = decltype(ub)::value;
+#pragma unroll
+          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        Frag kt[NKT][NFB];
         floatx4 u[CPW][NB];
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
@@ -697,45 +728,66 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
           for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
-            const Frag tf = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = MM::mma(u[cc][ut], tf, yf[cc][f]);
+            for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = MM::mma(u[cc][ut], tf[ut][f], yf[cc][f]);
           }
+#pragma unroll
+          for (int rt = ut * NKT / NB; rt < (ut + 1) * NKT / NB; ++rt)
+#pragma unroll
+            for (int f = 0; f < NFB; ++f) kt[rt][f] = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
         });
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) uf[cc][f] = MM::template acc<NB>(u[cc], f);
+        __builtin_amdgcn_sched_barrier(0);
+        Frag mf[NB][NFB];
+#pragma unroll
+        for (int rt = 0; rt < NKT; ++rt) {
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) {
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) sacc[cc][rt] = MM::mma(sacc[cc][rt], kt[rt][f], uf[cc][f]);
+          }
+          if (rt < NB) {
+            static_for<NB>([&](auto ub) {
+              constexpr int ut = decltype(ub)::value;
+              if (ut == rt) {
+#pragma unroll
+                for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
+              }
+            });
+          }
+        }
+        static_for<NB>([&](auto ub) {  // row tiles past the K^T loop (NKT < NB)
+          constexpr int ut = decltype(ub)::value;
+          if constexpr (ut >= NKT) {
+#pragma unroll
+            for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
+          }
+        });
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
 #pragma unroll
           for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
-            const Frag mf = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], uf[cc][f], mf);
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], uf[cc][f], mf[ut][f]);
           }
         });
-      }
-      __syncthreads();
-      // ---- phase C: S += K^T U'; stage O^T
-      if (act) {
+        // lane (g, li) holds columns 4g..4g+3 of token row 16 ut + li of its
+        // 16-column tile: 4 contiguous outputs, a 32-byte row segment per tile
+        const int nval = min(C, T - c * C);
+        CT* orow = (CT*)a.o + ((size_t)head * T + (size_t)c * C + li) * D + v0 + 4 * g;
 #pragma unroll
-        for (int rt = 0; rt < NKT; ++rt)
+        for (int ut = 0; ut < NB; ++ut)
+          if (16 * ut + li < nval) {
 #pragma unroll
-          for (int f = 0; f < NFB; ++f) {
-            const Frag kt = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
-#pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) sacc[cc][rt] = MM::mma(sacc[cc][rt], kt, uf[cc][f]);
+            for (int cc = 0; cc < CPW; ++cc)
+              store4(orow + (size_t)16 * ut * D + 16 * (w * CPW + cc), oacc[cc][ut]);
           }
-#pragma unroll
-        for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-          for (int ut = 0; ut < NB; ++ut)
-            MM::store_t(&sm.O[16 * ut + li][16 * (w * CPW + cc)], oacc[cc][ut]);
       }
       __syncthreads();
     }
-    store_out(nchunks - 1);
     if (owner && a.s_final) {
       float* sf = a.s_final + (size_t)head * D * D;
 #pragma unroll
@@ -746,237 +798,357 @@ __global__ __launch_bounds__(64 * (NSW + 4), 1) void efla_chunked_pipe_kernel(Ch
           for (int e = 0; e < 4; ++e)
             sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + cc) + li] = sacc[cc][rt][e];
     }
+  } else if (w < NSW + 2) {
+    // ======================= solvers (prep waves 0, 1) =======================
+    const int pw = w - NSW;
+    const CT* kg = (const CT*)a.k + (size_t)head * T * D;
+    auto solver = [&](auto pwc) {
+      constexpr int PW = decltype(pwc)::value;
+      constexpr int NDB = NB > PW ? (NB - PW + 1) / 2 : 0;  // diagonal blocks PW, PW + 2
+      // Rows of the diagonal blocks in MFMA operand layout, straight from
+      // HBM: lane (g, li) holds row 16 b + li, 16-byte pieces at columns
+      // 32 f + 8 g (bf16) or 16 f + 4 g (fp32). Both Gram operands are these
+      // same registers, so the k order only has to be consistent.
+      constexpr int NPC = sizeof(CT) == 2 ? (D + 31) / 32 : D / 16;  // pieces per row
+      constexpr int PST = sizeof(CT) == 2 ? 32 : 16;                 // column stride of pieces
+      Vec kd[NDB > 0 ? NDB : 1][NPC];
+      // rows past T are clamped here; their a is zero
+      auto load_rows = [&](int chunk) {
+        const int t0 = chunk * C;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) {
+          const int t = min(t0 + 16 * (PW + 2 * i) + li, T - 1);
+#pragma unroll
+          for (int f = 0; f < NPC; ++f) {
+            const int col = PST * f + VE * g;
+            if (col < D) kd[i][f] = *(const Vec*)(kg + (size_t)t * D + col);
+            else kd[i][f] = Vec{};
+          }
+        }
+      };
+      if constexpr (NDB > 0) load_rows(0);
+      // blocks of this solver's An copy left of its first column tile are
+      // never computed; they are read only against zero blocks of X, so they
+      // must hold zeros, not stale bits
+      if constexpr (t_first<NB>(PW) > 0 && t_first<NB>(PW) < NB) {
+        constexpr int NZ = (int)(sizeof(CT) * C * Sm::CP / 16);
+        floatx4* z = (floatx4*)&sm.An[PW][0][0];
+        for (int i = lane; i < NZ; i += 64) z[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      __syncthreads();  // a of the first chunk
+
+      for (int c = -1; c < nchunks; ++c) {
+        const int n = c + 1;  // chunk being prepared
+        const bool act = n < nchunks;
+        auto& B = sm.buf[n & 1];
+        int li = lane & 15, g = lane >> 4;
+        asm volatile("" : "+v"(li), "+v"(g));
+        // ---- phase A: (I + A_bb)^{-1} for the diagonal blocks (a of this
+        //      chunk was written by the loaders one chunk ahead; it is zero for
+        //      rows past T, which clears their rows of A)
+        if constexpr (NDB > 0) {
+          if (act) {
+            float al[NDB];
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) al[i] = B.alpha[16 * (PW + 2 * i) + li];
+            floatx4 dg[NDB];
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) {
+              dg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int f = 0; f < NPC; ++f) dg[i] = MM::mma(dg[i], kd[i][f], kd[i][f]);
+            }
+            // the row registers are free again: fetch the next chunk's rows now,
+            // so their latency is covered by the rest of this chunk (always
+            // issued, the last chunk's again at the end: a conditional load
+            // would make the compiler copy the registers at the loop latch and
+            // wait there for every load in flight)
+            load_rows(min(n + 1, nchunks - 1));
+            // lane (g, li) holds G[4g + e][li] = G[li][4g + e]: row li of A_bb
+            // is a_li G[li][c], c < li, stored transposed
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                sm.Adt[PW + 2 * i][4 * g + e][li] = (4 * g + e < li) ? al[i] * dg[i][e] : 0.f;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (g < NDB) {
+              // column-parallel right-looking forward substitution in fp32:
+              // lane group g = block PW + 2g, lane li = column li; once t_j is
+              // final, column j is eliminated from the rows below. The
+              // 4-groups of column j below the diagonal are read in two batches
+              // (columns 0-6, then 7-14, issued after three elimination steps):
+              // two LDS round trips instead of fifteen.
+              const float* Ab = &sm.Adt[PW + 2 * g][0][0];
+              floatx4 acol[15][4];
+              float t[16];
+#pragma unroll
+              for (int j = 0; j < 7; ++j)
+#pragma unroll
+                for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = *(const floatx4*)&Ab[20 * j + 4 * q4];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
+#pragma unroll
+              for (int j = 0; j < 15; ++j) {
+                if (j == 3) {
+                  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                  for (int jj = 7; jj < 15; ++jj)
+#pragma unroll
+                    for (int q4 = (jj + 1) >> 2; q4 < 4; ++q4)
+                      acol[jj][q4] = *(const floatx4*)&Ab[20 * jj + 4 * q4];
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
+              }
+              CT* Tb = &sm.Td[PW + 2 * g][0][0];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) Tb[Sm::TDS * r + li] = from_f32<CT>(t[r]);
+            }
+          }
+        }
+        __syncthreads();
+        // ---- phase B: the Gram tiles below the diagonal that this solver's
+        //      column tiles of T need (stored as -K K^T, unscaled: a is
+        //      applied in the solve), then those column tiles:
+        //        X_m = (I + A_mm)^{-1},
+        //        X_i = (I + A_ii)^{-1} diag(a_i) sum_{m<=j<i} (-K_i K_j^T) X_j, i > m;
+        //      X_i^T is formed too so T is written row-major.
+        constexpr int M0 = t_first<NB>(PW);
+        if constexpr (M0 < NB) {
+          if (act) {
+            auto& An = sm.An[PW];
+            // K row blocks M0.. read once into registers, then every Gram tile
+            // (i, j), i > j >= M0, from them
+            Frag kf[NB][NFK];
+            static_for<NB>([&](auto ib) {
+              constexpr int i = decltype(ib)::value;
+              if constexpr (i >= M0) {
+#pragma unroll
+                for (int f = 0; f < NFK; ++f) kf[i][f] = MM::template ldp<NKT>(&B.K[16 * i + li][0], f);
+              }
+            });
+            static_for<NB>([&](auto ib) {
+              constexpr int i = decltype(ib)::value;
+              static_for<i>([&](auto jb) {
+                constexpr int j = decltype(jb)::value;
+                if constexpr (j >= M0) {
+                  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, kf[j][f], kf[i][f]);
+                  MM::store_tp(&An[16 * i + li][0], j, -acc);
+                }
+              });
+            });
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            static_for<NB>([&](auto mb) {
+              constexpr int m = decltype(mb)::value;
+              if constexpr (t_owner<NB>(m) == PW) {
+                floatx4 x[NB];
+                static_for<NB>([&](auto ib) {
+                  constexpr int i = decltype(ib)::value;
+                  if constexpr (i >= m) {
+                    floatx4 yv;
+                    if constexpr (i == m) {
+#pragma unroll
+                      for (int e = 0; e < 4; ++e) yv[e] = (4 * g + e == li) ? 1.f : 0.f;
+                    } else {
+                      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                      for (int f = 0; f < NFrag<CT, i>::value; ++f) {
+                        if constexpr (MM::KT == 2) {
+                          if (2 * f + 1 < m) continue;  // both tiles of the fragment are zero
+                        } else {
+                          if (f < m) continue;
+                        }
+                        floatx4 xin[2] = {x[MM::KT * f],
+                                          MM::KT == 2 && 2 * f + 1 < i ? x[2 * f + 1] : x[MM::KT * f]};
+                        acc = MM::mma(acc, MM::template ldp<i>(&An[16 * i + li][0], f),
+                                      MM::template acc<(MM::KT == 2 ? 2 : 1)>(xin, 0));
+                      }
+                      yv = *(const floatx4*)&B.alpha[16 * i + 4 * g] * acc;
+                    }
+                    const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
+                    const Frag yf = MM::template acc<1>(&yv, 0);
+                    x[i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
+                    const floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
+                    MM::store_tp(&B.T[16 * i + li][0], m, xt);
+                  } else {
+                    x[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+                  }
+                });
+              }
+            });
+          }
+        }
+        __syncthreads();
+      }
+    };
+    if (pw == 0) solver(std::integral_constant<int, 0>{});
+    else solver(std::integral_constant<int, 1>{});
   } else {
-    // ======================= prep group =======================
-    const int pw = w - NSW;      // prep wave 0..3
-    const int ptid = tid - NST;  // 0..255
+    // ======================= loaders (prep waves 2, 3) =======================
+    const int lt = tid - NST - 128;  // loader thread 0..255
     const CT* qg = (const CT*)a.q + (size_t)head * T * D;
     const CT* kg = (const CT*)a.k + (size_t)head * T * D;
     const CT* vg = (const CT*)a.v + (size_t)head * T * D;
-    const CT* bg = (const CT*)a.beta + (size_t)head * T;
-
+    constexpr int NLT = 256;
     constexpr int VPR = D / VE;
     constexpr int VPRV = BV / VE;
-    constexpr int NLK = (C * VPR + 255) / 256;
-    constexpr int NLV = (C * VPRV + 255) / 256;
-    constexpr int RPJ = 64 / VPR;  // rows a wave stages per load slot
+    constexpr int NLK = (C * VPR + NLT - 1) / NLT;
+    constexpr int NLV = (C * VPRV + NLT - 1) / NLT;
+    const CT* bg = (const CT*)a.beta + (size_t)head * T;
     Vec kreg[NLK], qreg[NLK], vreg[NLV];
-    CT breg[NLK];
-    auto prefetch = [&](int chunk) {
+    CT breg;
+    // Row-sum layout of the key slots: slot j, lane (q, p) = (lane / VPR,
+    // lane % VPR) holds piece p of row (64 w' + NLT j) / VPR + q of this wave
+    // w'. Lane (q, p < NLK) computes a for slot p's row q and loads its beta.
+    const int lw = lt >> 6;        // loader wave 0..3
+    const int lq = lane / VPR, lp = lane % VPR;
+    const int arow = (64 * lw + NLT * lp) / VPR + lq;  // row of this lane's a (when lp < NLK)
+    // coalesced 16-byte loads of one chunk; rows past T are clamped here and
+    // zeroed when staged
+    auto load_k = [&](int chunk) {
       const int t0 = chunk * C;
-      const int nval = min(C, T - t0);
 #pragma unroll
       for (int j = 0; j < NLK; ++j) {
-        const int idx = ptid + 256 * j;
+        const int idx = lt + NLT * j;
         const int r = idx / VPR, cv = idx % VPR;
-        kreg[j] = Vec{};
-        qreg[j] = Vec{};
-        breg[j] = from_f32<CT>(0.f);
-        if (idx < C * VPR && r < nval) {
-          kreg[j] = *(const Vec*)(kg + (size_t)(t0 + r) * D + cv * VE);
-          qreg[j] = *(const Vec*)(qg + (size_t)(t0 + r) * D + cv * VE);
-          breg[j] = bg[t0 + r];
-        }
+        if (idx < C * VPR) kreg[j] = *(const Vec*)(kg + (size_t)min(t0 + r, T - 1) * D + cv * VE);
+      }
+      breg = bg[min(t0 + min(arow, C - 1), T - 1)];
+    };
+    // lambda = ||k||^2 per row by a DPP row sum over the row's VPR lanes, then
+    // a = -expm1(-beta lambda)/lambda for the chunk whose keys are in kreg, into
+    // that chunk's buffer; zero for rows past T
+    auto gate_rows = [&](int chunk, float* alpha) {
+      float lam[NLK];
+#pragma unroll
+      for (int j = 0; j < NLK; ++j) lam[j] = group_sum<VPR>(sumsq(kreg[j]));
+      float l = lam[0];
+#pragma unroll
+      for (int j = 1; j < NLK; ++j) l = lp == j ? lam[j] : l;
+      const int nval = min(C, T - chunk * C);
+      if (lp < NLK && arow < C) alpha[arow] = arow < nval ? gate_alpha(to_f32(breg), l) : 0.f;
+    };
+    auto load_qv = [&](int chunk) {
+      const int t0 = chunk * C;
+#pragma unroll
+      for (int j = 0; j < NLK; ++j) {
+        const int idx = lt + NLT * j;
+        const int r = idx / VPR, cv = idx % VPR;
+        if (idx < C * VPR) qreg[j] = *(const Vec*)(qg + (size_t)min(t0 + r, T - 1) * D + cv * VE);
       }
 #pragma unroll
       for (int j = 0; j < NLV; ++j) {
-        const int idx = ptid + 256 * j;
+        const int idx = lt + NLT * j;
         const int r = idx / VPRV, cv = idx % VPRV;
-        vreg[j] = Vec{};
-        if (idx < C * VPRV && r < nval) vreg[j] = *(const Vec*)(vg + (size_t)(t0 + r) * D + v0 + cv * VE);
+        if (idx < C * VPRV) vreg[j] = *(const Vec*)(vg + (size_t)min(t0 + r, T - 1) * D + v0 + cv * VE);
       }
     };
-    prefetch(0);
-
-    for (int c = -1; c < nchunks; ++c) {
-      const int n = c + 1;  // chunk being prepared
-      const bool act = n < nchunks;
-      auto& B = sm.buf[n & 1];
-      // Opaque per-iteration copies of the lane coordinates: masks and
-      // identity entries derived from them are then rebuilt inside the loop
-      // instead of being hoisted out and held in registers across it.
-      int li = lane & 15, g = lane >> 4;
-      asm volatile("" : "+v"(li), "+v"(g));
-      // ---- phase A: stage chunk n (keys, queries, value slice, step sizes)
-      if (act) {
-#pragma unroll
-        for (int j = 0; j < NLK; ++j) {
-          const int idx = ptid + 256 * j;
-          if (idx < C * VPR) {
-            const int r = idx / VPR, cv = idx % VPR;
-            st_perm(&B.K[r][0], cv * VE, kreg[j]);
-            st_perm(&B.Q[r][0], cv * VE, qreg[j]);
-            if (cv == 0) sm.betas[r] = to_f32(breg[j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NLV; ++j) {
-          const int idx = ptid + 256 * j;
-          if (idx < C * VPRV) {
-            const int r = idx / VPRV, cv = idx % VPRV;
-            st16(&B.V[r][cv * VE], vreg[j]);
-          }
-        }
-        if (n + 1 < nchunks) prefetch(n + 1);
-      }
+    auto loader = [&](auto pwc) {
+      constexpr int PW = decltype(pwc)::value;  // loader 0..3
+      using JB = PrepJobs<NB>;
+      constexpr int NJ = JB::NQK > PW ? (JB::NQK - PW + 3) / 4 : 0;  // Q K^T jobs PW, PW + 4, ...
+      load_k(0);
+      load_qv(0);
+      gate_rows(0, sm.buf[0].alpha);
       __syncthreads();
-      // ---- phase B. Prep waves 0 and 1 (each alone on its SIMD) own the
-      //  diagonal blocks b = pw, pw + 2: G_bb = K_b K_b^T; lambda_r = ||k_r||^2
-      //  is its diagonal and a_r = -expm1(-beta_r lambda_r)/lambda_r for the
-      //  block's rows (every lane holds a_r of its row: no LDS round trip); the
-      //  scaled strictly-lower block A_bb = diag(a_b) strictly-lower(G_bb), and
-      //  (I + A_bb)^{-1} by column-parallel right-looking forward substitution
-      //  in fp32 (lane group g = block pw + 2g, lane li = column li: once t_j
-      //  is final, column j is eliminated from the rows below, all
-      //  independently).
-      //  Prep waves 2 and 3 (which share their SIMDs with the state waves)
-      //  take the Gram tiles below the diagonal blocks (stored as -K K^T,
-      //  unscaled: a is applied in the solve) and the lower-incl-diag Q K^T
-      //  tiles (-> M), alternately.
-      if (act) {
-        if (pw < 2) {
-          auto diag = [&](auto pwc) {
-            constexpr int PW = decltype(pwc)::value;           // 0..1
-            constexpr int NDB = NB > PW ? (NB - PW + 1) / 2 : 0;  // blocks PW, PW + 2
-            if constexpr (NDB > 0) {
-              floatx4 dg[NDB];
+      for (int c = -1; c < nchunks; ++c) {
+        const int n = c + 1;  // chunk being prepared
+        const bool act = n < nchunks;
+        auto& B = sm.buf[n & 1];
+        int li = lane & 15, g = lane >> 4;
+        asm volatile("" : "+v"(li), "+v"(g));
+        // ---- phase A: stage chunk n (keys, queries, value slice)
+        if (act) {
+          const int nval = min(C, T - n * C);
+          auto stage = [&](auto fullc) {
+            constexpr bool FULL = decltype(fullc)::value;  // no rows past T
 #pragma unroll
-              for (int i = 0; i < NDB; ++i) {
-                dg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-                MM::template llp<D>(dg[i], &B.K[16 * (PW + 2 * i) + li][0], &B.K[16 * (PW + 2 * i) + li][0]);
-              }
-#pragma unroll
-              for (int i = 0; i < NDB; ++i) {
-                const int b = PW + 2 * i;
-                // lane (g, li) holds G[4g + e][li] = G[li][4g + e]; the diagonal
-                // entry of row li sits in lane 16 (li / 4) + li, slot li % 4
-                const float lam = __shfl(dg[i][li & 3], 16 * (li >> 2) + li);
-                const float al = gate_alpha(sm.betas[16 * b + li], lam);
-                if (g == 0) B.alpha[16 * b + li] = al;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sm.Adt[b][4 * g + e][li] = (4 * g + e < li) ? al * dg[i][e] : 0.f;
-              }
-              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-              __builtin_amdgcn_wave_barrier();
-              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-              if (g < NDB) {
-                const float* Ab = &sm.Adt[PW + 2 * g][0][0];
-                // The 4-groups of column j of A below the diagonal are read in
-                // two batches (columns 0-6, then 7-14, issued after three
-                // elimination steps): two LDS round trips instead of fifteen,
-                // while the second batch reuses the registers of the first.
-                floatx4 acol[15][4];
-                float t[16];
-#pragma unroll
-                for (int j = 0; j < 7; ++j)
-#pragma unroll
-                  for (int q4 = (j + 1) >> 2; q4 < 4; ++q4) acol[j][q4] = *(const floatx4*)&Ab[20 * j + 4 * q4];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) t[r] = (r == li) ? 1.f : 0.f;
-#pragma unroll
-                for (int j = 0; j < 15; ++j) {
-                  if (j == 3) {
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int jj = 7; jj < 15; ++jj)
-#pragma unroll
-                      for (int q4 = (jj + 1) >> 2; q4 < 4; ++q4)
-                        acol[jj][q4] = *(const floatx4*)&Ab[20 * jj + 4 * q4];
-                    __builtin_amdgcn_sched_barrier(0);
-                  }
-#pragma unroll
-                  for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
+            for (int j = 0; j < NLK; ++j) {
+              const int idx = lt + NLT * j;
+              if (idx < C * VPR) {
+                const int r = idx / VPR, cv = idx % VPR;
+                Vec kk = kreg[j], qq = qreg[j];
+                if constexpr (!FULL) {
+                  if (r >= nval) kk = qq = Vec{};
                 }
-                CT* Tb = &sm.Td[PW + 2 * g][0][0];
+                st_perm(&B.K[r][0], cv * VE, kk);
+                st_perm(&B.Q[r][0], cv * VE, qq);
+              }
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Tb[(16 + Sm::P) * r + li] = from_f32<CT>(t[r]);
+            for (int j = 0; j < NLV; ++j) {
+              const int idx = lt + NLT * j;
+              if (idx < C * VPRV) {
+                const int r = idx / VPRV, cv = idx % VPRV;
+                Vec vv = vreg[j];
+                if constexpr (!FULL) {
+                  if (r >= nval) vv = Vec{};
+                }
+                *(Vec*)&B.V[r][cv * VE] = vv;  // 16-byte aligned rows
               }
             }
           };
-          if (pw == 0) diag(std::integral_constant<int, 0>{});
-          else diag(std::integral_constant<int, 1>{});
-        } else {
-          auto tile_jobs = [&](auto pwc) {
-            constexpr int PW = decltype(pwc)::value;  // 2..3
-            using JB = PrepJobs<NB>;
-            constexpr int J0 = PW - 2;
-            constexpr int NJ = JB::N > J0 ? (JB::N - J0 + 1) / 2 : 0;  // jobs J0, J0 + 2, ...
-            floatx4 acc[NJ > 0 ? NJ : 1];
+          if (nval == C) stage(std::true_type{});
+          else stage(std::false_type{});
+        }
+        load_k(min(n + 1, nchunks - 1));
+        __syncthreads();
+        // ---- phase B: load the queries and values of chunk n + 1; this
+        //      wave's lower-incl-diag Q K^T tiles (-> M)
+        load_qv(min(n + 1, nchunks - 1));
+        if constexpr (NJ > 0) {
+          if (act) {
+            // every fragment of this wave's tiles is requested first, then
+            // the products: one exposed LDS round trip
+            Frag kfr[NJ][NFK], qfr[NJ][NFK];
             static_for<NJ>([&](auto jc) {
-              constexpr int j = J0 + 2 * decltype(jc)::value;
+              constexpr int j = JB::NOFF + PW + 4 * decltype(jc)::value;
               constexpr int I = JB::I(j), J = JB::J(j);
+#pragma unroll
+              for (int f = 0; f < NFK; ++f) {
+                kfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&B.K[16 * J + li][0], f);
+                qfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&B.Q[16 * I + li][0], f);
+              }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            floatx4 acc[NJ];
+            static_for<NJ>([&](auto jc) {
               acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
-              MM::template llp<D>(acc[decltype(jc)::value], &B.K[16 * J + li][0],
-                                  JB::is_qk(j) ? &B.Q[16 * I + li][0] : &B.K[16 * I + li][0]);
+#pragma unroll
+              for (int f = 0; f < NFK; ++f)
+                acc[decltype(jc)::value] = MM::mma(acc[decltype(jc)::value], kfr[decltype(jc)::value][f], qfr[decltype(jc)::value][f]);
             });
             static_for<NJ>([&](auto jc) {
-              constexpr int j = J0 + 2 * decltype(jc)::value;
+              constexpr int j = JB::NOFF + PW + 4 * decltype(jc)::value;
               constexpr int I = JB::I(j), J = JB::J(j);
               floatx4 v = acc[decltype(jc)::value];
-              if constexpr (JB::is_qk(j)) {
-                if constexpr (I == J) {
+              if constexpr (I == J) {
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
-                }
-                MM::store_tp(&B.M[16 * I + li][0], J, v);
-              } else {
-                MM::store_tp(&sm.An[16 * I + li][0], J, -v);
+                for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
               }
+              MM::store_tp(&B.M[16 * I + li][0], J, v);
             });
-          };
-          if (pw == 2) tile_jobs(std::integral_constant<int, 2>{});
-          else tile_jobs(std::integral_constant<int, 3>{});
+          }
         }
+        // a of chunk n + 1 (its keys arrived during this phase)
+        if (n + 1 < nchunks) gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
+        __syncthreads();
       }
-      __syncthreads();
-      // ---- phase C: column tile m = pw of T = (I + A)^{-1}:
-      //      X_m = (I + A_mm)^{-1},
-      //      X_i = (I + A_ii)^{-1} diag(a_i) sum_{m<=j<i} (-K_i K_j^T) X_j, i > m;
-      //      X_i^T is also formed so T is written row-major with 8-byte stores.
-      if (act && pw < NB) {
-        auto col_tile = [&](auto mc) {
-          constexpr int m = decltype(mc)::value;
-          floatx4 x[NB];
-          static_for<NB>([&](auto ib) {
-            constexpr int i = decltype(ib)::value;
-            if constexpr (i >= m) {
-              floatx4 yv;
-              if constexpr (i == m) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) yv[e] = (4 * g + e == li) ? 1.f : 0.f;
-              } else {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int f = 0; f < NFrag<CT, i>::value; ++f) {
-                  if constexpr (MM::KT == 2) {
-                    if (2 * f + 1 < m) continue;  // both tiles of the fragment are zero
-                  } else {
-                    if (f < m) continue;
-                  }
-                  floatx4 xin[2] = {x[MM::KT * f], MM::KT == 2 && 2 * f + 1 < i ? x[2 * f + 1] : x[MM::KT * f]};
-                  acc = MM::mma(acc, MM::template ldp<i>(&sm.An[16 * i + li][0], f),
-                                MM::template acc<(MM::KT == 2 ? 2 : 1)>(xin, 0));
-                }
-                yv = *(const floatx4*)&B.alpha[16 * i + 4 * g] * acc;
-              }
-              const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
-              const Frag yf = MM::template acc<1>(&yv, 0);
-              x[i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
-              const floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
-              MM::store_tp(&B.T[16 * i + li][0], m, xt);
-            } else {
-              x[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
-          });
-        };
-        switch (pw) {
-          case 0: col_tile(std::integral_constant<int, 0>{}); break;
-          case 1: if constexpr (NB > 1) col_tile(std::integral_constant<int, (NB > 1 ? 1 : 0)>{}); break;
-          case 2: if constexpr (NB > 2) col_tile(std::integral_constant<int, (NB > 2 ? 2 : 0)>{}); break;
-          default: if constexpr (NB > 3) col_tile(std::integral_constant<int, (NB > 3 ? 3 : 0)>{}); break;
-        }
-      }
-      __syncthreads();
+    };
+    switch (w - NSW - 2) {
+      case 0: loader(std::integral_constant<int, 0>{}); break;
+      case 1: loader(std::integral_constant<int, 1>{}); break;
+      case 2: loader(std::integral_constant<int, 2>{}); break;
+      default: loader(std::integral_constant<int, 3>{}); break;
     }
   }
 }
@@ -991,7 +1163,7 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, hipStream_t stre
   dim3 grid((unsigned)(NH * a.nvt));
   if constexpr (pipe_smem_bytes<CT, D, C, BV>() <= 160 * 1024) {
     constexpr int NSW = EFLA_PIPE_STATE_WAVES;
-    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW>), grid, dim3(64 * (NSW + 4)), 0,
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW>), grid, dim3(64 * (NSW + 6)), 0,
                        stream, a);
   } else {
     static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");

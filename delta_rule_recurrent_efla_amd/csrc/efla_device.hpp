@@ -228,6 +228,23 @@ __device__ __forceinline__ void st16(bf16* p, bf16x8 v) {
 }
 __device__ __forceinline__ bf16x8 ld16(const bf16* p) { return Mma<bf16>::ld8(p); }
 __device__ __forceinline__ void st16(float* p, floatx4 v) { *(floatx4*)p = v; }
+// Sum of squares of a 16-byte vector, in fp32 (bf16 pairs by packed dot
+// products: the products are exact in fp32).
+__device__ __forceinline__ float sumsq(bf16x8 v) {
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = {v[2 * i], v[2 * i + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(p, p, s, false);
+  }
+  return s;
+}
+__device__ __forceinline__ float sumsq(floatx4 v) { return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]; }
+// Four fp32 values -> 4 consecutive elements at p (8 bytes as bf16, rounded to
+// nearest even; 16 bytes as fp32).
+__device__ __forceinline__ void store4(bf16* p, floatx4 v) { *(bf16x4*)p = __builtin_convertvector(v, bf16x4); }
+__device__ __forceinline__ void store4(float* p, floatx4 v) { *(floatx4*)p = v; }
 __device__ __forceinline__ floatx4 ld16(const float* p) { return *(const floatx4*)p; }
 
 // Four consecutive rows row0 .. row0+3 of column col0 + (lane & 15) of a
