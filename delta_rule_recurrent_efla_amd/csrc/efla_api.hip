@@ -9,8 +9,9 @@
 
 hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v,
                                         const void* beta, const float* s0, void* o,
-                                        float* s_final, int NH, int T, int d, int chunk,
-                                        int is_bf16, hipStream_t stream);
+                                        float* s_final, void* workspace, int NH, int T, int d,
+                                        int chunk, int is_bf16, hipStream_t stream);
+size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16);
 hipError_t efla_internal_launch_decode(const void* q, const void* k, const void* v,
                                        const void* beta, float* state, void* o, int NH, int d,
                                        int is_bf16, hipStream_t stream);
@@ -37,8 +38,13 @@ bool chunked_supported(int d, int chunk, efla_dtype dt) {
 
 extern "C" size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v,
                                                    int chunk, efla_dtype dt) {
-  (void)B; (void)H; (void)T; (void)d_k; (void)d_v; (void)chunk; (void)dt;
-  return 0;  // the fused kernel keeps every intermediate on chip
+  if (B < 1 || H < 1 || T < 1 || d_k != d_v) return 0;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return 0;
+  if (!chunked_supported(d_k, chunk, dt)) return 0;
+  if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return 0;
+  // nonzero only for the time-segmented schedule (few heads, long sequences):
+  // per head and segment, the segment's affine map and its start state
+  return efla_internal_chunked_workspace_bytes(B * H, T, d_k, chunk, dt == EFLA_DTYPE_BF16);
 }
 
 extern "C" efla_status efla_fwd_chunked(const void* q, const void* k, const void* v,
@@ -52,12 +58,12 @@ extern "C" efla_status efla_fwd_chunked(const void* q, const void* k, const void
   if (!chunked_supported(d_k, chunk, dt)) return EFLA_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s0) ||
-      !aligned16(s_final) || !elem_aligned(beta, dt))
+      !aligned16(s_final) || !aligned16(workspace) || !elem_aligned(beta, dt))
     return EFLA_ERR_MISALIGNED;
   const size_t need = efla_fwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk, dt);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return EFLA_ERR_WORKSPACE;
-  const hipError_t e = efla_internal_launch_chunked(q, k, v, beta, s0, o, s_final, B * H, T, d_k,
-                                                    chunk, dt == EFLA_DTYPE_BF16,
+  const hipError_t e = efla_internal_launch_chunked(q, k, v, beta, s0, o, s_final, workspace,
+                                                    B * H, T, d_k, chunk, dt == EFLA_DTYPE_BF16,
                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }

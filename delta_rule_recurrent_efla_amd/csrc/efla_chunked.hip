@@ -23,6 +23,8 @@
 // forward solve whose right-hand sides stay in registers. The next chunk's
 // loads are issued before the current chunk's compute.
 
+#include <algorithm>
+
 #include "efla_device.hpp"
 
 // Waves per workgroup that hold the state slice (2: 32 columns each; 4: 16),
@@ -46,6 +48,19 @@ struct ChunkedArgs {
   float* s_final;
   int T;
   int nvt;  // state column slices per head
+  // Time-segmented passes (pipelined kernel only). mode 0: one pass over the
+  // whole sequence per head. mode 1: per head and segment g < nseg of seg_len
+  // tokens, the segment's affine map S_end = P_g S_start + R_g: virtual head
+  // 2 (h nseg + g) + kind runs the segment from S = 0 with the values
+  // (kind 0, gives R_g) or from S = I with zero values (kind 1, gives P_g),
+  // writes no outputs and stores S_end to seg_out[(h nseg + g) 2 + kind].
+  // mode 2: virtual head h nseg + g runs segment g from seg_s0[h nseg + g]
+  // and writes its outputs; the last segment writes s_final.
+  int mode;
+  int seg_len;
+  int nseg;
+  const float* seg_s0;
+  float* seg_out;
 };
 
 template <typename CT>
@@ -584,7 +599,7 @@ __device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
 }
 __device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
 
-template <typename CT, int D, int C, int BV, int NSW>
+template <typename CT, int D, int C, int BV, int NSW, bool SUMMARY>
 __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
@@ -619,9 +634,33 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   const int total = gridDim.x;
   if (total % 8 == 0 && ((total / 8) % a.nvt) == 0)
     L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
-  const int head = L / a.nvt;
+  const int vh = L / a.nvt;  // virtual head
   const int v0 = (L % a.nvt) * BV;
-  const int T = a.T;
+  int hd = vh, t_begin = 0, T = a.T;
+  // SUMMARY (mode 1): no outputs; odd virtual heads start from S = I with
+  // zero values. Both are compile-time off in the other modes.
+  constexpr bool outs = !SUMMARY;
+  bool ident = false;
+  const float* s0p = a.s0 ? a.s0 + (size_t)hd * D * D : nullptr;
+  float* sfp = a.s_final ? a.s_final + (size_t)hd * D * D : nullptr;
+  if constexpr (SUMMARY) {
+    const int sg = (vh >> 1) % a.nseg;
+    hd = (vh >> 1) / a.nseg;
+    ident = vh & 1;
+    t_begin = sg * a.seg_len;
+    T = a.seg_len;
+    s0p = nullptr;
+    sfp = a.seg_out + ((size_t)(hd * a.nseg + sg) * 2 + (vh & 1)) * D * D;
+  } else if (a.mode == 2) {
+    const int sg = vh % a.nseg;
+    hd = vh / a.nseg;
+    t_begin = sg * a.seg_len;
+    T = min(a.seg_len, a.T - t_begin);
+    s0p = a.seg_s0 + (size_t)(hd * a.nseg + sg) * D * D;
+    sfp = (sg == a.nseg - 1 && a.s_final) ? a.s_final + (size_t)hd * D * D : nullptr;
+  }
+  ident = SUMMARY && __builtin_amdgcn_readfirstlane(ident);
+  const size_t tok0 = (size_t)hd * a.T + t_begin;  // first token of this sequence piece
   const int nchunks = (T + C - 1) / C;
 
   if (w < NSW) {
@@ -632,15 +671,23 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
       for (int rt = 0; rt < NKT; ++rt) sacc[c][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (owner && a.s0) {
-      const float* s0 = a.s0 + (size_t)head * D * D;
+    if (owner && s0p) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
 #pragma unroll
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = s0[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
+            sacc[c][rt][e] = s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
+    }
+    if (SUMMARY && owner && ident) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (w * CPW + c) + li) ? 1.f : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -673,7 +720,8 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc)
-            vv[cc][ut] = to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
+            vv[cc][ut] = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f}
+                                            : to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
         }
         __builtin_amdgcn_sched_barrier(0);
         Frag qf[NB][NFK];
@@ -686,20 +734,22 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           for (int f = 0; f < NFK; ++f) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) p[cc] = MM::mma(p[cc], kf[ut][f], sf[cc][f]);
-            qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
+            if constexpr (outs) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
           }
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (vv[cc][ut] - p[cc]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (outs) {
 #pragma unroll
-        for (int ut = 0; ut < NB; ++ut) {
+          for (int ut = 0; ut < NB; ++ut) {
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int f = 0; f < NFK; ++f) {
+            for (int f = 0; f < NFK; ++f) {
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
+              for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
+            }
           }
         }
       }
@@ -749,7 +799,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) sacc[cc][rt] = MM::mma(sacc[cc][rt], kt[rt][f], uf[cc][f]);
           }
-          if (rt < NB) {
+          if (outs && rt < NB) {  // constant after unrolling
             static_for<NB>([&](auto ub) {
               constexpr int ut = decltype(ub)::value;
               if (ut == rt) {
@@ -759,6 +809,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
             });
           }
         }
+        if constexpr (outs) {
         static_for<NB>([&](auto ub) {  // row tiles past the K^T loop (NKT < NB)
           constexpr int ut = decltype(ub)::value;
           if constexpr (ut >= NKT) {
@@ -777,7 +828,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         // lane (g, li) holds columns 4g..4g+3 of token row 16 ut + li of its
         // 16-column tile: 4 contiguous outputs, a 32-byte row segment per tile
         const int nval = min(C, T - c * C);
-        CT* orow = (CT*)a.o + ((size_t)head * T + (size_t)c * C + li) * D + v0 + 4 * g;
+        CT* orow = (CT*)a.o + (tok0 + (size_t)c * C + li) * D + v0 + 4 * g;
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut)
           if (16 * ut + li < nval) {
@@ -785,11 +836,12 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
             for (int cc = 0; cc < CPW; ++cc)
               store4(orow + (size_t)16 * ut * D + 16 * (w * CPW + cc), oacc[cc][ut]);
           }
+        }
       }
       __syncthreads();
     }
-    if (owner && a.s_final) {
-      float* sf = a.s_final + (size_t)head * D * D;
+    if (owner && sfp) {
+      float* sf = sfp;
 #pragma unroll
       for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
@@ -801,7 +853,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   } else if (w < NSW + 2) {
     // ======================= solvers (prep waves 0, 1) =======================
     const int pw = w - NSW;
-    const CT* kg = (const CT*)a.k + (size_t)head * T * D;
+    const CT* kg = (const CT*)a.k + tok0 * D;
     auto solver = [&](auto pwc) {
       constexpr int PW = decltype(pwc)::value;
       constexpr int NDB = NB > PW ? (NB - PW + 1) / 2 : 0;  // diagonal blocks PW, PW + 2
@@ -995,15 +1047,18 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   } else {
     // ======================= loaders (prep waves 2, 3) =======================
     const int lt = tid - NST - 128;  // loader thread 0..255
-    const CT* qg = (const CT*)a.q + (size_t)head * T * D;
-    const CT* kg = (const CT*)a.k + (size_t)head * T * D;
-    const CT* vg = (const CT*)a.v + (size_t)head * T * D;
+    const CT* kg = (const CT*)a.k + tok0 * D;
+    // without outputs the queries are not needed, and a transition run has no
+    // values: those loads read the key rows instead (same lines, no extra HBM
+    // traffic) and their tiles are not formed
+    const CT* qg = outs ? (const CT*)a.q + tok0 * D : kg;
+    const CT* vg = (SUMMARY && ident) ? kg : (const CT*)a.v + tok0 * D;
     constexpr int NLT = 256;
     constexpr int VPR = D / VE;
     constexpr int VPRV = BV / VE;
     constexpr int NLK = (C * VPR + NLT - 1) / NLT;
     constexpr int NLV = (C * VPRV + NLT - 1) / NLT;
-    const CT* bg = (const CT*)a.beta + (size_t)head * T;
+    const CT* bg = (const CT*)a.beta + tok0;
     Vec kreg[NLK], qreg[NLK], vreg[NLV];
     CT breg;
     // Row-sum layout of the key slots: slot j, lane (q, p) = (lane / VPR,
@@ -1106,7 +1161,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         //      wave's lower-incl-diag Q K^T tiles (-> M)
         load_qv(min(n + 1, nchunks - 1));
         if constexpr (NJ > 0) {
-          if (act) {
+          if (outs && act) {
             // every fragment of this wave's tiles is requested first, then
             // the products: one exposed LDS round trip
             Frag kfr[NJ][NFK], qfr[NJ][NFK];
@@ -1154,16 +1209,162 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 }
 
 // ---------------------------------------------------------------------------
+// Carry of the time-segmented forward: per head, the start state of every
+// segment, S_start(0) = S0 (zeros without one) and
+// S_start(g + 1) = P_g S_start(g) + R_g, in fp32. One workgroup per (head,
+// 16-column slice of S): the columns of S evolve independently, so the
+// slices need no exchange. P_g is staged in LDS each step.
+template <int D>
+__global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, const float* seg_out,
+                                                             float* seg_s0, int nseg) {
+  // fp32 MFMA (16x16x4): lane (g, i) of a 16x16 tile product takes
+  // A[i][k] and B[k][i] for the four k values 16q + 4g + s of k-block q
+  // (s = 0..3: one MFMA each) from one 16-byte read of a row of P and of a
+  // row of S^T; the result holds rows 4g + e of column i. Rows are padded to
+  // an odd multiple of 32 bytes (conflict-free 16-byte reads).
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) float P[D][LD];
+  __shared__ __attribute__((aligned(16))) float St[16][LD];  // S^T of this 16-column slice
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int h = blockIdx.x / (D / 16);
+  const int j0 = (blockIdx.x % (D / 16)) * 16;
+  for (int i = tid; i < D * 16; i += 256) {
+    const int r = i / 16, c = i % 16;
+    St[c][r] = s0 ? s0[((size_t)h * D + r) * D + j0 + c] : 0.f;
+  }
+  __syncthreads();
+  // P_g and this lane's R_g values are fetched into registers one step ahead
+  constexpr int NPL = (D * D / 4 + 255) / 256;  // 16-byte pieces of P per thread
+  constexpr int NT = (D / 16 + 3) / 4;  // 16-row tiles per wave
+  floatx4 pr[NPL], rr[NT];
+  auto fetch = [&](int gs) {
+    const float* R = seg_out + ((size_t)(h * (nseg - 1) + gs) * 2) * D * D;
+    const float* Pg = R + (size_t)D * D;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+      if (tid + 256 * j < D * D / 4) pr[j] = *(const floatx4*)&Pg[4 * (tid + 256 * j)];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int t = w + 4 * tt;
+      if (t < D / 16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rr[tt][e] = R[(size_t)(16 * t + 4 * g + e) * D + j0 + li];
+      }
+    }
+  };
+  if (nseg > 1) fetch(0);
+  for (int gs = 0; gs < nseg; ++gs) {
+    float* dst = seg_s0 + ((size_t)h * nseg + gs) * D * D;
+    for (int i = tid; i < D * 16; i += 256) {
+      const int r = i / 16, c = i % 16;
+      dst[(size_t)r * D + j0 + c] = St[c][r];
+    }
+    if (gs == nseg - 1) break;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e4 = 4 * (tid + 256 * j);
+      if (e4 < D * D) *(floatx4*)&P[e4 / D][e4 % D] = pr[j];
+    }
+    floatx4 acc[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = rr[tt];
+    __syncthreads();
+    if (gs + 1 < nseg - 1) fetch(gs + 1);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int t = w + 4 * tt;
+      if (t < D / 16) {
+        floatx4 c4 = acc[tt];
+#pragma unroll
+        for (int q = 0; q < D / 16; ++q) {
+          const floatx4 a4 = *(const floatx4*)&P[16 * t + li][16 * q + 4 * g];
+          const floatx4 b4 = *(const floatx4*)&St[li][16 * q + 4 * g];
+#pragma unroll
+          for (int sidx = 0; sidx < 4; ++sidx) c4 = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[sidx], b4[sidx], c4, 0, 0, 0);
+        }
+        acc[tt] = c4;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int t = w + 4 * tt;
+      if (t < D / 16) *(floatx4*)&St[li][16 * t + 4 * g] = acc[tt];
+    }
+    __syncthreads();
+  }
+}
+
+// When a plain pass would leave most of the GPU idle (few heads, long
+// sequences), the forward runs as three launches over nseg time segments:
+// the segments' affine maps (mode 1, all segments at once), the carry, then
+// every segment's outputs from its true start state (mode 2). About three
+// times the arithmetic of one pass, spread over ~nseg times more workgroups.
+struct SegPlan {
+  int nseg = 1;
+  int seg_len = 0;
+};
+
+static SegPlan seg_plan(int NH, int T, int d, int C, bool pipelined) {
+  SegPlan p;
+  if (!pipelined) return p;
+  const long long W = (long long)NH * (d / (d < 64 ? d : 64));  // workgroups of one pass
+  const int nchunks = (T + C - 1) / C;
+  if (W >= 128 || nchunks < 64) return p;
+  const long long G = std::min<long long>(256 / W, nchunks / 32);  // segments of >= 32 chunks
+  if (G < 2) return p;
+  const int cps = (int)((nchunks + G - 1) / G);  // chunks per segment
+  p.seg_len = cps * C;
+  p.nseg = (T + p.seg_len - 1) / p.seg_len;
+  if (p.nseg < 2) p = SegPlan{};
+  return p;
+}
+
+static size_t seg_workspace_bytes(const SegPlan& p, int NH, int d) {
+  if (p.nseg < 2) return 0;
+  return (size_t)NH * (3 * (size_t)p.nseg - 2) * d * d * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch. Returns hipSuccess or the launch error.
 template <typename CT, int D, int C>
-static hipError_t launch_chunked(const ChunkedArgs& in, int NH, hipStream_t stream) {
+constexpr bool pipelined() {
+  return pipe_smem_bytes<CT, D, C, (D < 64 ? D : 64)>() <= 160 * 1024;
+}
+
+template <typename CT, int D, int C>
+static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStream_t stream) {
   constexpr int BV = D < 64 ? D : 64;
   ChunkedArgs a = in;
   a.nvt = D / BV;
   dim3 grid((unsigned)(NH * a.nvt));
-  if constexpr (pipe_smem_bytes<CT, D, C, BV>() <= 160 * 1024) {
+  if constexpr (pipelined<CT, D, C>()) {
     constexpr int NSW = EFLA_PIPE_STATE_WAVES;
-    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW>), grid, dim3(64 * (NSW + 6)), 0,
+    const SegPlan sp = seg_plan(NH, a.T, D, C, true);
+    if (sp.nseg >= 2) {
+      float* seg_out = (float*)ws;
+      float* seg_s0 = seg_out + (size_t)NH * (sp.nseg - 1) * 2 * D * D;
+      ChunkedArgs m1 = a;
+      m1.mode = 1;
+      m1.seg_len = sp.seg_len;
+      m1.nseg = sp.nseg - 1;
+      m1.seg_out = seg_out;
+      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, true>),
+                         dim3((unsigned)(NH * (sp.nseg - 1) * 2 * a.nvt)), dim3(64 * (NSW + 6)), 0,
+                         stream, m1);
+      hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0,
+                         stream, a.s0, (const float*)seg_out, seg_s0, sp.nseg);
+      ChunkedArgs m2 = a;
+      m2.mode = 2;
+      m2.seg_len = sp.seg_len;
+      m2.nseg = sp.nseg;
+      m2.seg_s0 = seg_s0;
+      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, false>),
+                         dim3((unsigned)(NH * sp.nseg * a.nvt)), dim3(64 * (NSW + 6)), 0, stream, m2);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, false>), grid, dim3(64 * (NSW + 6)), 0,
                        stream, a);
   } else {
     static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");
@@ -1174,36 +1375,64 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, hipStream_t stre
 }
 
 template <typename CT, int D>
-static hipError_t dispatch_chunk(const ChunkedArgs& a, int NH, int chunk, hipStream_t s) {
+static hipError_t dispatch_chunk(const ChunkedArgs& a, int NH, int chunk, void* ws, hipStream_t s) {
   switch (chunk) {
-    case 16: return launch_chunked<CT, D, 16>(a, NH, s);
-    case 32: return launch_chunked<CT, D, 32>(a, NH, s);
+    case 16: return launch_chunked<CT, D, 16>(a, NH, ws, s);
+    case 32: return launch_chunked<CT, D, 32>(a, NH, ws, s);
     case 64:
       if constexpr (sizeof(CT) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_chunked<CT, D, 64>(a, NH, s);
+      else return launch_chunked<CT, D, 64>(a, NH, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <typename CT, int D>
+static bool pipelined_chunk(int chunk) {
+  switch (chunk) {
+    case 16: return pipelined<CT, D, 16>();
+    case 32: return pipelined<CT, D, 32>();
+    case 64:
+      if constexpr (sizeof(CT) == 4 && D == 128) return false;
+      else return pipelined<CT, D, 64>();
+    default: return false;
+  }
+}
+
 template <typename CT>
-static hipError_t dispatch_d(const ChunkedArgs& a, int NH, int d, int chunk, hipStream_t s) {
+static bool pipelined_d(int d, int chunk) {
   switch (d) {
-    case 16: return dispatch_chunk<CT, 16>(a, NH, chunk, s);
-    case 32: return dispatch_chunk<CT, 32>(a, NH, chunk, s);
-    case 64: return dispatch_chunk<CT, 64>(a, NH, chunk, s);
-    case 128: return dispatch_chunk<CT, 128>(a, NH, chunk, s);
+    case 16: return pipelined_chunk<CT, 16>(chunk);
+    case 32: return pipelined_chunk<CT, 32>(chunk);
+    case 64: return pipelined_chunk<CT, 64>(chunk);
+    case 128: return pipelined_chunk<CT, 128>(chunk);
+    default: return false;
+  }
+}
+
+template <typename CT>
+static hipError_t dispatch_d(const ChunkedArgs& a, int NH, int d, int chunk, void* ws, hipStream_t s) {
+  switch (d) {
+    case 16: return dispatch_chunk<CT, 16>(a, NH, chunk, ws, s);
+    case 32: return dispatch_chunk<CT, 32>(a, NH, chunk, ws, s);
+    case 64: return dispatch_chunk<CT, 64>(a, NH, chunk, ws, s);
+    case 128: return dispatch_chunk<CT, 128>(a, NH, chunk, ws, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace efla
 
-// Internal entry used by the C ABI layer (arguments already validated).
+// Internal entries used by the C ABI layer (arguments already validated).
+size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16) {
+  const bool pipe = is_bf16 ? efla::pipelined_d<efla::bf16>(d, chunk) : efla::pipelined_d<float>(d, chunk);
+  return efla::seg_workspace_bytes(efla::seg_plan(NH, T, d, chunk, pipe), NH, d);
+}
+
 hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v,
                                         const void* beta, const float* s0, void* o,
-                                        float* s_final, int NH, int T, int d, int chunk,
-                                        int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1};
-  if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, stream);
-  return efla::dispatch_d<float>(a, NH, d, chunk, stream);
+                                        float* s_final, void* workspace, int NH, int T, int d,
+                                        int chunk, int is_bf16, hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr};
+  if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, workspace, stream);
+  return efla::dispatch_d<float>(a, NH, d, chunk, workspace, stream);
 }

@@ -56,9 +56,15 @@ typedef enum {
 } efla_status;
 
 /*
- * Bytes of device workspace efla_fwd_chunked needs for these sizes (0 when
- * the fused path needs none). Returns 0 for unsupported sizes as well;
- * efla_fwd_chunked reports those.
+ * Bytes of device workspace efla_fwd_chunked needs for these sizes. It is 0
+ * when one pass over the sequence fills the GPU. For few heads and long
+ * sequences (fewer than 128 workgroups of 64 state columns, and at least 64
+ * chunks; segments of at least 32 chunks) the forward runs over time segments: the affine map S -> P S + R of
+ * every segment, then their composition, then each segment from its true start
+ * state (the chunk recurrence is affine in S, section 整体框架 of the
+ * papernotes note); the workspace then holds, per head and segment, the map
+ * (P, R) and the start state: B H (3 nseg - 2) d_k d_v fp32 values.
+ * Returns 0 for unsupported sizes as well; efla_fwd_chunked reports those.
  */
 size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
                                         efla_dtype dt);
@@ -72,9 +78,11 @@ size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  *   o         [B, H, T, d_v] output, element type dt.
  *   s_final   [B, H, d_k, d_v] fp32 final state S_T, or NULL to skip it. It
  *             may alias s0 (the state is then advanced in place).
- *   workspace, workspace_bytes   caller-owned scratch of at least
- *             efla_fwd_chunked_workspace_bytes() bytes (may be NULL/0 when
- *             that is 0).
+ *   workspace, workspace_bytes   caller-owned device scratch of at least
+ *             efla_fwd_chunked_workspace_bytes() bytes, 16-byte aligned (may
+ *             be NULL/0 when that is 0). Its contents on entry do not matter
+ *             and are overwritten; calls sharing one workspace must not
+ *             overlap in time.
  *   chunk     tokens per chunk, one of 16, 32, 64. T need not be a multiple.
  * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64};
  * fp32 with d = 128 needs chunk <= 32. Anything else: EFLA_ERR_UNSUPPORTED.

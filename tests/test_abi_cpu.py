@@ -91,7 +91,29 @@ def test_step_rejects_bad_arguments_before_launch():
 
 
 def test_workspace_query():
-    # the fused kernel needs no workspace for any supported size
+    lib = efla.load_library()
+    # one pass fills the GPU (or the sequence is short): no workspace
     for d in efla.SUPPORTED_HEAD_DIMS:
         for c in efla.SUPPORTED_CHUNKS:
-            assert efla.load_library().efla_fwd_chunked_workspace_bytes(2, 4, 1000, d, d, c, 1) == 0
+            assert lib.efla_fwd_chunked_workspace_bytes(2, 4, 1000, d, d, c, 1) == 0
+    assert lib.efla_fwd_chunked_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0    # 256 workgroups
+    assert lib.efla_fwd_chunked_workspace_bytes(16, 8, 2048, 128, 128, 64, 1) == 0
+    # few heads, long sequence: time segments. 16 heads x 2 column slices = 32
+    # workgroups -> 8 segments of 128 chunks; per head and segment the map
+    # (P, R) for all but the last segment plus every start state
+    nseg = 8
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 64, 1) == \
+        16 * (3 * nseg - 2) * 128 * 128 * 4
+    # unsupported or invalid sizes report 0
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 48, 1) == 0
+    assert lib.efla_fwd_chunked_workspace_bytes(0, 16, 65536, 128, 128, 64, 1) == 0
+
+
+def test_segmented_call_checks_its_workspace_before_launch():
+    lib = efla.load_library()
+    need = lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 64, 1)
+    assert need > 0
+    kw = dict(B=1, H=16, T=65536, dk=128, dv=128, chunk=64, dt=1)
+    assert chunked(lib, ws=None, wsb=0, **kw) == 5
+    assert chunked(lib, ws=FAKE, wsb=need - 1, **kw) == 5
+    assert chunked(lib, ws=FAKE + 8, wsb=need, **kw) == 4  # workspace must be 16-byte aligned
