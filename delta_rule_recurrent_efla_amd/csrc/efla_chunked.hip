@@ -698,19 +698,19 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     for (int c = -1; c < nchunks; ++c) {
       const bool act = c >= 0 && owner;
       const auto& B = sm.buf[c & 1];
-      floatx4 oacc[CPW][NB], y[CPW][NB];
-      Frag sf[CPW][NFK];
-      // ---- phase A: K S, Y = diag(a)(V - K S); O^T = S^T Q^T. All K
-      //      fragments (and V, a) are requested first, the Q fragments while
-      //      the K S products run: one exposed LDS round trip, not one per
-      //      fragment
+      floatx4 oacc[CPW][NB];
+      Frag sf[CPW][NFK], uf[CPW][NFB], kt[NKT][NFB], qf[NB][NFK];
+      // ---- phase A: K S, Y = diag(a)(V - K S); U' = T Y (T of this chunk
+      //      is ready one phase early). All K fragments (and V, a) are
+      //      requested first, the Q fragments (for phase B) while the K S
+      //      products run, then the T fragments
       if (act) {
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
         Frag kf[NB][NFK];
-        floatx4 al[NB], vv[CPW][NB];
+        floatx4 al[NB], vv[CPW][NB], y[CPW][NB];
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut)
 #pragma unroll
@@ -724,7 +724,6 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
                                             : to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
         }
         __builtin_amdgcn_sched_barrier(0);
-        Frag qf[NB][NFK];
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
           floatx4 p[CPW];
@@ -739,38 +738,17 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (vv[cc][ut] - p[cc]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (outs) {
-#pragma unroll
-          for (int ut = 0; ut < NB; ++ut) {
-#pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int f = 0; f < NFK; ++f) {
-#pragma unroll
-              for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      // ---- phase B: U' = T Y; S += K^T U'; O^T += U'^T M^T; store O. T
-      //      fragments first, K^T fragments while T Y runs, M fragments while
-      //      K^T U' runs
-      if (act) {
-        Frag yf[CPW][NFB], uf[CPW][NFB];
+        Frag yf[CPW][NFB], tf[NB][NFB];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) yf[cc][f] = MM::template acc<NB>(y[cc], f);
-        Frag tf[NB][NFB];
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
 #pragma unroll
           for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
         });
         __builtin_amdgcn_sched_barrier(0);
-        Frag kt[NKT][NFB];
         floatx4 u[CPW][NB];
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
@@ -781,16 +759,38 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) u[cc][ut] = MM::mma(u[cc][ut], tf[ut][f], yf[cc][f]);
           }
-#pragma unroll
-          for (int rt = ut * NKT / NB; rt < (ut + 1) * NKT / NB; ++rt)
-#pragma unroll
-            for (int f = 0; f < NFB; ++f) kt[rt][f] = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
         });
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) uf[cc][f] = MM::template acc<NB>(u[cc], f);
-        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();
+      // ---- phase B: O^T = S^T Q^T (S before this chunk's update, Q from
+      //      phase A), each row block followed by the requests for its share
+      //      of K^T fragments; S += K^T U'; O^T += U'^T M^T; store O. M
+      //      fragments while K^T U' runs
+      if (act) {
+        static_for<NB>([&](auto ub) {
+          constexpr int ut = decltype(ub)::value;
+          if constexpr (outs) {
+            // register-only products would otherwise be hoisted above the
+            // barrier; tying their inputs to this point keeps them in phase B
+#pragma unroll
+            for (int f = 0; f < NFK; ++f) asm volatile("" : "+v"(qf[ut][f]));
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int f = 0; f < NFK; ++f) {
+#pragma unroll
+              for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
+            }
+          }
+#pragma unroll
+          for (int rt = ut * NKT / NB; rt < (ut + 1) * NKT / NB; ++rt)
+#pragma unroll
+            for (int f = 0; f < NFB; ++f) kt[rt][f] = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
+        });
         Frag mf[NB][NFB];
 #pragma unroll
         for (int rt = 0; rt < NKT; ++rt) {
@@ -1111,6 +1111,47 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       constexpr int PW = decltype(pwc)::value;  // loader 0..3
       using JB = PrepJobs<NB>;
       constexpr int NJ = JB::NQK > PW ? (JB::NQK - PW + 3) / 4 : 0;  // Q K^T jobs PW, PW + 4, ...
+      // The first of this wave's jobs of a chunk runs in phase A of the
+      // chunk's own state pass (its K and Q were staged one phase before, the
+      // state reads M only in phase B); the others one chunk ahead in phase B.
+      constexpr int NA = (outs && NJ > 0) ? 1 : 0;
+      // jobs [J0, J1) of this wave on buffer Bm: every fragment first, then
+      // the products (one exposed LDS round trip)
+      auto mtiles = [&](auto& Bm, auto j0c, auto j1c) {
+        constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
+        if constexpr (outs && J1 > J0) {
+          const int li = lane & 15, g = lane >> 4;
+          Frag kfr[J1 - J0][NFK], qfr[J1 - J0][NFK];
+          static_for<J1 - J0>([&](auto jc) {
+            constexpr int j = JB::NOFF + PW + 4 * (J0 + decltype(jc)::value);
+            constexpr int I = JB::I(j), J = JB::J(j);
+#pragma unroll
+            for (int f = 0; f < NFK; ++f) {
+              kfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&Bm.K[16 * J + li][0], f);
+              qfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&Bm.Q[16 * I + li][0], f);
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+          floatx4 acc[J1 - J0];
+          static_for<J1 - J0>([&](auto jc) {
+            acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int f = 0; f < NFK; ++f)
+              acc[decltype(jc)::value] =
+                  MM::mma(acc[decltype(jc)::value], kfr[decltype(jc)::value][f], qfr[decltype(jc)::value][f]);
+          });
+          static_for<J1 - J0>([&](auto jc) {
+            constexpr int j = JB::NOFF + PW + 4 * (J0 + decltype(jc)::value);
+            constexpr int I = JB::I(j), J = JB::J(j);
+            floatx4 v = acc[decltype(jc)::value];
+            if constexpr (I == J) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
+            }
+            MM::store_tp(&Bm.M[16 * I + li][0], J, v);
+          });
+        }
+      };
       load_k(0);
       load_qv(0);
       gate_rows(0, sm.buf[0].alpha);
@@ -1155,44 +1196,17 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           if (nval == C) stage(std::true_type{});
           else stage(std::false_type{});
         }
+        // first M job of the chunk whose state pass runs now
+        if constexpr (NA > 0) {
+          if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
+        }
         load_k(min(n + 1, nchunks - 1));
         __syncthreads();
-        // ---- phase B: load the queries and values of chunk n + 1; this
-        //      wave's lower-incl-diag Q K^T tiles (-> M)
+        // ---- phase B: load the queries and values of chunk n + 1; the rest
+        //      of this wave's lower-incl-diag Q K^T tiles of chunk n (-> M)
         load_qv(min(n + 1, nchunks - 1));
-        if constexpr (NJ > 0) {
-          if (outs && act) {
-            // every fragment of this wave's tiles is requested first, then
-            // the products: one exposed LDS round trip
-            Frag kfr[NJ][NFK], qfr[NJ][NFK];
-            static_for<NJ>([&](auto jc) {
-              constexpr int j = JB::NOFF + PW + 4 * decltype(jc)::value;
-              constexpr int I = JB::I(j), J = JB::J(j);
-#pragma unroll
-              for (int f = 0; f < NFK; ++f) {
-                kfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&B.K[16 * J + li][0], f);
-                qfr[decltype(jc)::value][f] = MM::template ldp<NKT>(&B.Q[16 * I + li][0], f);
-              }
-            });
-            __builtin_amdgcn_sched_barrier(0);
-            floatx4 acc[NJ];
-            static_for<NJ>([&](auto jc) {
-              acc[decltype(jc)::value] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int f = 0; f < NFK; ++f)
-                acc[decltype(jc)::value] = MM::mma(acc[decltype(jc)::value], kfr[decltype(jc)::value][f], qfr[decltype(jc)::value][f]);
-            });
-            static_for<NJ>([&](auto jc) {
-              constexpr int j = JB::NOFF + PW + 4 * decltype(jc)::value;
-              constexpr int I = JB::I(j), J = JB::J(j);
-              floatx4 v = acc[decltype(jc)::value];
-              if constexpr (I == J) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
-              }
-              MM::store_tp(&B.M[16 * I + li][0], J, v);
-            });
-          }
+        if constexpr (NJ > NA) {
+          if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
         }
         // a of chunk n + 1 (its keys arrived during this phase)
         if (n + 1 < nchunks) gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
