@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "EFLA fwd tokens/s at B·H·T, d=128 (1 MI355X); % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_FLOPS = 2.5166e15
+FP32_PEAK_FLOPS = 157.3e12
 KERNEL_SOURCES = ("delta_rule_recurrent_efla_amd/csrc/efla_chunked.hip",
                   "delta_rule_recurrent_efla_amd/csrc/efla_device.hpp",
                   "delta_rule_recurrent_efla_amd/build.py")
@@ -137,6 +138,42 @@ def cpu_baseline(w, x, min_seconds: float, max_threads: int = 16):
                       f"fp64 sequential recurrence, {use} threads, {dt:.1f} s wall"}
 
 
+def bench_other_workloads(efla, torch, efla_inputs, skip: str, steps=10, warmup=3):
+    """Per-launch time of the chunked forward on the other synthetic workloads
+    (not the headline metric): head-tokens/s and the fraction of the HBM
+    roofline on their algorithmic bytes (bf16), or of the fp32 MFMA peak on
+    their useful flops (fp32 inputs)."""
+    out = []
+    for name, w in efla_inputs.WORKLOADS.items():
+        if name == skip:
+            continue
+        x = efla_inputs.make_inputs(w)
+        g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+        o = torch.empty_like(g["v"])
+        sT = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda")
+        ws_bytes = efla.efla_fwd_chunked_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.chunk,
+                                                         w.torch_dtype)
+
+        def fwd():
+            efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=w.chunk, o=o,
+                                  s_final=sT)
+
+        _, per = time_launches(fwd, steps, warmup, torch.cuda.current_stream())
+        per.sort()
+        med = per[len(per) // 2]
+        nbytes = alg_bytes_fwd(w, g["s0"] is not None)
+        rec = {"workload": name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "chunk": w.chunk,
+               "dtype": w.dtype, "ms_per_launch_median": med,
+               "head_tokens_per_s": w.head_tokens / (med * 1e-3),
+               "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "time_segmented": ws_bytes > 0}
+        if w.dtype == "f32":
+            rec["fp32_mfma_frac"] = alg_flops_fwd(w) / (med * 1e-3) / FP32_PEAK_FLOPS
+        out.append(rec)
+        del g, o, sT, x
+    return out
+
+
 def bench_decode(efla, torch, efla_inputs, steps=256):
     w = efla_inputs.WORKLOADS["layer340m_d128"]
     x = efla_inputs.make_inputs(w)
@@ -173,6 +210,8 @@ def main():
     ap.add_argument("--workload", default="layer1p3b_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the per-launch times of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (HBM-counter calibration)")
@@ -236,6 +275,8 @@ def main():
     }
     if not args.no_decode:
         res["decode"] = bench_decode(efla, torch, efla_inputs)
+    if not args.no_others:
+        res["other_workloads"] = bench_other_workloads(efla, torch, efla_inputs, w.name)
     if args.copy_calibration:
         copy_calibration(torch)
     if not args.no_cpu_baseline:
