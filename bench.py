@@ -30,15 +30,29 @@ KERNEL_SOURCES = ("delta_rule_recurrent_efla_amd/csrc/efla_chunked.hip",
 COPY_CAL_BYTES = 1 << 30  # bytes read (and written) by the calibration copy
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines: the hash follows the code,
+    not its comments."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the chunked kernel's sources and build flags: HBM-traffic
-    counters taken for one build are only reported for that same build."""
+    """sha256 over the chunked kernel's code (comments stripped) and build
+    script: HBM-traffic counters taken for one build are only reported for
+    that same code."""
     import hashlib
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        if not rel.endswith(".py"):
+            text = _code_only(text)
+        h.update(text.encode())
     return h.hexdigest()
 
 

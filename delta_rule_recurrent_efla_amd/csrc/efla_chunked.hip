@@ -514,16 +514,21 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 //   U' = T Y                       (= U - W S with W = T diag(a) K, U = T diag(a) V)
 //   O^T = S^T Q^T + U'^T M^T       (read out after each update)
 //   S <- S + K^T U'
-// Two workgroup barriers per chunk split it into phases A and B:
-//   state waves    A: K S, Y; S^T Q^T            B: T Y, U'^T M^T, K^T U'; store O
-//   prep 0, 1      A: diagonal Gram blocks from  B: Gram tiles below the diagonal,
-//   ("solvers")       registers, a, (I+A_bb)^-1     column tiles of T
-//   prep 2..5      A: stage K, Q, V into LDS;    B: Q K^T tiles (M); load the
-//   ("loaders")       load the next chunk's K       next chunk's Q, V
+// Two workgroup barriers per chunk split it into phases A and B. While the
+// state waves run chunk c:
+//   state waves    A: K S, Y, U' = T Y           B: S^T Q^T, K^T U', U'^T M^T;
+//                                                    store O
+//   prep 0, 1      A: diagonal Gram blocks of    B: Gram tiles below the diagonal
+//   ("solvers")       c+1 from registers,            and the column tiles of T
+//                     (I+A_bb)^-1                    of c+1
+//   prep 2..5      A: stage K, Q, V of c+1;      B: the other Q K^T tiles of
+//   ("loaders")       one Q K^T tile of c;           c+1; a of c+2; load Q, V
+//                     load the keys of c+2           of c+2
 // Waves are placed on the SIMDs round robin: the two state waves and the two
 // solvers get a SIMD each, and every SIMD also runs one loader. Every global
 // load is issued as soon as its registers are free and consumed one chunk
-// later.
+// later; loads are never conditional (the last chunk is fetched again), so
+// the compiler keeps no copy at the loop latch.
 // K, Q, V, T, M and a are double-buffered in LDS; K^T and the columns of V
 // are read with ds_read_b64_tr_b16 straight from the row-major tiles.
 template <typename CT, int D, int C, int BV>
