@@ -28,6 +28,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 EXACT = 0
 EULER = 1
+RK4 = 2      # one-step RK4 of the ODE, collapsed to a scalar (rank 1)
+ORDER2 = 3   # the same series cut after the second-order term
 
 _lib = None
 

@@ -23,9 +23,20 @@
  * The state S is d_k x d_v, row index = key dimension (the write k v^T fixes
  * that orientation). Heads are independent; each is run token by token.
  *
- * Also exposed, for tests only: the explicit-Euler coefficient (alpha = beta,
- * the delta rule the note contrasts with, 关键设计 item 1) and the Frobenius
- * norm of the state after every step.
+ * The same rank-1 step also runs with three other coefficients (one scalar c
+ * in place of alpha; everything else unchanged):
+ *   - explicit Euler, c = beta: the delta rule the note contrasts with
+ *     (关键设计 item 1);
+ *   - one-step RK4 (jsqmd.com article "EFLA注意力机制：优化挑战与训练策略解析",
+ *     section 5.3): the printed matrix polynomial in A = k k^T collapses,
+ *     because A^n = lambda^(n-1) A, to c = beta (1 - x/2 + x^2/6 - x^3/24)
+ *     with x = beta lambda, for both the transition and the input term;
+ *   - second order (same section names it without writing it out; the plain
+ *     reading is the same series cut after the A^2 term):
+ *     c = beta (1 - x/2).
+ * No floor applies to lambda in these three: none of them divides by it.
+ * Also exposed, for tests only: the Frobenius norm of the state after every
+ * step.
  *
  * Parity pins live in the test suite: the worked example printed in the note
  * (section 一个完整示例), scipy's matrix exponential of the augmented ODE
@@ -40,6 +51,8 @@
 
 #define EFLA_ORACLE_EXACT 0
 #define EFLA_ORACLE_EULER 1
+#define EFLA_ORACLE_RK4 2
+#define EFLA_ORACLE_ORDER2 3
 
 /* Exact-flow coefficient with the 1e-12 floor on lambda (training-strategy
  * section of the papernotes note; rank-1 collapse in 关键设计 item 2). */
@@ -48,9 +61,15 @@ double efla_oracle_alpha(double beta, double lam) {
   return -expm1(-beta * lamc) / lamc;
 }
 
+/* The scalar of the rank-1 step for each mode (see the header comment). */
 double efla_oracle_coef(int mode, double beta, double lam) {
-  if (mode == EFLA_ORACLE_EULER) return beta;
-  return efla_oracle_alpha(beta, lam);
+  double x = beta * lam;
+  switch (mode) {
+    case EFLA_ORACLE_EULER: return beta;
+    case EFLA_ORACLE_RK4: return beta * (1.0 - x / 2.0 + x * x / 6.0 - x * x * x / 24.0);
+    case EFLA_ORACLE_ORDER2: return beta * (1.0 - x / 2.0);
+    default: return efla_oracle_alpha(beta, lam);
+  }
 }
 
 /* One token on one head. S is d_k x d_v row-major, updated in place.
