@@ -37,6 +37,10 @@ STATUS_NAMES = {
     6: "EFLA_ERR_HIP",
 }
 
+# Step coefficient rules (efla_coef): the exact flow, explicit Euler (the
+# delta rule), one classical RK4 step and the series cut at second order.
+COEFS = {"exact": 0, "euler": 1, "rk4": 2, "order2": 3}
+
 SUPPORTED_HEAD_DIMS = (16, 32, 64, 128)
 SUPPORTED_CHUNKS = (16, 32, 64)
 
@@ -67,9 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.efla_fwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.efla_fwd_chunked.restype = i
         lib.efla_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                         i, i, i, i, i, i, i, vp]
+                                         i, i, i, i, i, i, i, i, vp]
         lib.efla_fwd_recurrent_step.restype = i
-        lib.efla_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        lib.efla_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
         lib.efla_status_string.restype = ctypes.c_char_p
         lib.efla_status_string.argtypes = [i]
         _lib = lib
@@ -105,6 +109,14 @@ def _require(t: torch.Tensor, name: str, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _coef(coef) -> int:
+    if isinstance(coef, str):
+        if coef not in COEFS:
+            raise ValueError(f"unknown coefficient rule {coef!r}; one of {sorted(COEFS)}")
+        return COEFS[coef]
+    return int(coef)
+
+
 def efla_fwd_chunked_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int, chunk: int,
                                      dtype: torch.dtype) -> int:
     return int(load_library().efla_fwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk,
@@ -114,12 +126,13 @@ def efla_fwd_chunked_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int,
 def efla_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                      s0: Optional[torch.Tensor] = None, chunk: int = 64,
                      o: Optional[torch.Tensor] = None, s_final: Optional[torch.Tensor] = None,
-                     return_state: bool = True, stream=None
+                     return_state: bool = True, stream=None, coef="exact"
                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked EFLA forward. q, k: [B,H,T,d]; v: [B,H,T,d]; beta: [B,H,T]
     (all fp32 or all bf16, contiguous, on one GPU); s0: [B,H,d,d] fp32 or None.
     Returns (o [B,H,T,d] in the input dtype, S_T [B,H,d,d] fp32 or None).
-    ``s_final`` may be passed (and may be ``s0`` itself to advance in place)."""
+    ``s_final`` may be passed (and may be ``s0`` itself to advance in place).
+    ``coef`` picks the step scalar: "exact" (EFLA), "euler", "rk4", "order2"."""
     lib = load_library()
     dev = q.device
     if q.dim() != 4:
@@ -149,16 +162,18 @@ def efla_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
     st = lib.efla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
                               _ptr(s_final), _ptr(ws), ws_bytes, B, H, T, d, dv, int(chunk),
-                              _DTYPES[dt], _stream(dev, stream))
+                              _coef(coef), _DTYPES[dt], _stream(dev, stream))
     _raise(st)
     return o, s_final
 
 
 def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             beta: torch.Tensor, state: torch.Tensor,
-                            o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                            o: Optional[torch.Tensor] = None, stream=None,
+                            coef="exact") -> torch.Tensor:
     """One token per head: q, k, v [B,H,d]; beta [B,H]; state [B,H,d,d] fp32,
-    advanced in place. Returns o [B,H,d] = S_t^T q_t in the input dtype."""
+    advanced in place. Returns o [B,H,d] = S_t^T q_t in the input dtype.
+    ``coef`` as in efla_fwd_chunked."""
     lib = load_library()
     dev = q.device
     if q.dim() != 3:
@@ -180,6 +195,7 @@ def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     else:
         _require(o, "o", dt, dev)
     st = lib.efla_fwd_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(state),
-                                     _ptr(o), B, H, d, dv, _DTYPES[dt], _stream(dev, stream))
+                                     _ptr(o), B, H, d, dv, _coef(coef), _DTYPES[dt],
+                                     _stream(dev, stream))
     _raise(st)
     return o

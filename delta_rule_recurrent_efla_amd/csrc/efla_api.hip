@@ -10,11 +10,11 @@
 hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v,
                                         const void* beta, const float* s0, void* o,
                                         float* s_final, void* workspace, int NH, int T, int d,
-                                        int chunk, int is_bf16, hipStream_t stream);
+                                        int chunk, int coef, int is_bf16, hipStream_t stream);
 size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16);
 hipError_t efla_internal_launch_decode(const void* q, const void* k, const void* v,
                                        const void* beta, float* state, void* o, int NH, int d,
-                                       int is_bf16, hipStream_t stream);
+                                       int coef, int is_bf16, hipStream_t stream);
 
 namespace {
 
@@ -23,6 +23,11 @@ bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr
 bool elem_aligned(const void* p, efla_dtype dt) {
   const uintptr_t m = dt == EFLA_DTYPE_F32 ? 3u : 1u;
   return (reinterpret_cast<uintptr_t>(p) & m) == 0;
+}
+
+bool coef_ok(efla_coef c) {
+  return c == EFLA_COEF_EXACT || c == EFLA_COEF_EULER || c == EFLA_COEF_RK4 ||
+         c == EFLA_COEF_ORDER2;
 }
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -51,11 +56,11 @@ extern "C" efla_status efla_fwd_chunked(const void* q, const void* k, const void
                                         const void* beta, const float* s0, void* o,
                                         float* s_final, void* workspace, size_t workspace_bytes,
                                         int B, int H, int T, int d_k, int d_v, int chunk,
-                                        efla_dtype dt, void* stream) {
+                                        efla_coef coef, efla_dtype dt, void* stream) {
   if (!q || !k || !v || !beta || !o) return EFLA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || T < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
   if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
-  if (!chunked_supported(d_k, chunk, dt)) return EFLA_ERR_UNSUPPORTED;
+  if (!chunked_supported(d_k, chunk, dt) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s0) ||
       !aligned16(s_final) || !aligned16(workspace) || !elem_aligned(beta, dt))
@@ -63,25 +68,26 @@ extern "C" efla_status efla_fwd_chunked(const void* q, const void* k, const void
   const size_t need = efla_fwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk, dt);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return EFLA_ERR_WORKSPACE;
   const hipError_t e = efla_internal_launch_chunked(q, k, v, beta, s0, o, s_final, workspace,
-                                                    B * H, T, d_k, chunk, dt == EFLA_DTYPE_BF16,
+                                                    B * H, T, d_k, chunk, (int)coef,
+                                                    dt == EFLA_DTYPE_BF16,
                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }
 
 extern "C" efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
                                                const void* beta, float* state, void* o, int B,
-                                               int H, int d_k, int d_v, efla_dtype dt,
-                                               void* stream) {
+                                               int H, int d_k, int d_v, efla_coef coef,
+                                               efla_dtype dt, void* stream) {
   if (!q || !k || !v || !beta || !state || !o) return EFLA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
   if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
-  if (!head_dim_ok(d_k)) return EFLA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d_k) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
   if ((long long)B * H > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) ||
       !elem_aligned(beta, dt))
     return EFLA_ERR_MISALIGNED;
   const hipError_t e = efla_internal_launch_decode(q, k, v, beta, state, o, B * H, d_k,
-                                                   dt == EFLA_DTYPE_BF16,
+                                                   (int)coef, dt == EFLA_DTYPE_BF16,
                                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }
@@ -91,7 +97,7 @@ extern "C" const char* efla_status_string(efla_status s) {
     case EFLA_OK: return "EFLA_OK";
     case EFLA_ERR_NULL_POINTER: return "EFLA_ERR_NULL_POINTER: a required pointer is NULL";
     case EFLA_ERR_BAD_SHAPE: return "EFLA_ERR_BAD_SHAPE: B, H, T < 1, sizes too large, or d_k != d_v";
-    case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported";
+    case EFLA_ERR_UNSUPPORTED: return "EFLA_ERR_UNSUPPORTED: head dim, chunk size, dtype or coefficient not supported";
     case EFLA_ERR_MISALIGNED: return "EFLA_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
     case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace too small";
     case EFLA_ERR_HIP: return "EFLA_ERR_HIP: the HIP runtime reported a launch error";

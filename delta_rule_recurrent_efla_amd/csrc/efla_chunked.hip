@@ -61,6 +61,7 @@ struct ChunkedArgs {
   int nseg;
   const float* seg_s0;
   float* seg_out;
+  int coef;  // step coefficient rule (gate_coef)
 };
 
 template <typename CT>
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
             ss += x * x;
           }
           ss = group_sum<VPR>(ss);
-          if (cv == 0) sm.alpha[r] = gate_alpha(to_f32(breg[j]), ss);
+          if (cv == 0) sm.alpha[r] = gate_coef(a.coef, to_f32(breg[j]), ss);
         }
       }
 #pragma unroll
@@ -1095,7 +1096,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
       for (int j = 1; j < NLK; ++j) l = lp == j ? lam[j] : l;
       const int nval = min(C, T - chunk * C);
-      if (lp < NLK && arow < C) alpha[arow] = arow < nval ? gate_alpha(to_f32(breg), l) : 0.f;
+      if (lp < NLK && arow < C) alpha[arow] = arow < nval ? gate_coef(a.coef, to_f32(breg), l) : 0.f;
     };
     auto load_qv = [&](int chunk) {
       const int t0 = chunk * C;
@@ -1450,8 +1451,8 @@ size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, in
 hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v,
                                         const void* beta, const float* s0, void* o,
                                         float* s_final, void* workspace, int NH, int T, int d,
-                                        int chunk, int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr};
+                                        int chunk, int coef, int is_bf16, hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef};
   if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, workspace, stream);
   return efla::dispatch_d<float>(a, NH, d, chunk, workspace, stream);
 }

@@ -4,6 +4,7 @@
 //
 // Per head, with S the fp32 state [d_k, d_v]:
 //   lambda = k.k,  a = -expm1(-beta*max(lambda,1e-12)) / max(lambda,1e-12)
+//                  (or the Euler / RK4 / second-order scalar: gate_coef)
 //   p = S^T k,  r = S^T q                  (one read pass over S)
 //   u = a (v - p)                          (S_new = S + k u^T)
 //   o = S_new^T q = r + (k.q) u
@@ -25,6 +26,7 @@ struct DecodeArgs {
   float* state;
   void* o;
   int nvt;
+  int coef;  // step coefficient rule (gate_coef)
 };
 
 template <typename CT, int D, int VB>
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
       pj += sp[x][j >> 2][j & 3];
       rj += sr[x][j >> 2][j & 3];
     }
-    const float al = gate_alpha(to_f32(((const CT*)a.beta)[head]), slam);
+    const float al = gate_coef(a.coef, to_f32(((const CT*)a.beta)[head]), slam);
     const float u = al * (sv[j] - pj);
     su[j] = u;
     ((CT*)a.o)[(size_t)head * D + v0 + j] = from_f32<CT>(rj + skq * u);
@@ -135,8 +137,8 @@ static hipError_t dispatch_decode(const DecodeArgs& a, int NH, int d, hipStream_
 
 hipError_t efla_internal_launch_decode(const void* q, const void* k, const void* v,
                                        const void* beta, float* state, void* o, int NH, int d,
-                                       int is_bf16, hipStream_t stream) {
-  efla::DecodeArgs a{q, k, v, beta, state, o, 1};
+                                       int coef, int is_bf16, hipStream_t stream) {
+  efla::DecodeArgs a{q, k, v, beta, state, o, 1, coef};
   if (is_bf16) return efla::dispatch_decode<efla::bf16>(a, NH, d, stream);
   return efla::dispatch_decode<float>(a, NH, d, stream);
 }

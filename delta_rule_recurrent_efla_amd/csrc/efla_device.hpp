@@ -32,6 +32,21 @@ __device__ __forceinline__ float gate_alpha(float beta, float lam) {
   return -expm1f(-beta * lamc) / lamc;
 }
 
+// Scalar c of the rank-1 step S_t = (I - c k k^T) S_{t-1} + c k v^T for each
+// step rule, x = beta lambda (the efla_coef values of the C interface):
+//   0 exact flow (above); 1 explicit Euler, c = beta (papernotes note,
+//   关键设计 item 1); 2 one classical RK4 step, c = beta (1 - x/2 + x^2/6 -
+//   x^3/24), the matrix polynomial of the jsqmd.com article, section 5.3,
+//   collapsed by A^n = lambda^(n-1) A; 3 that series cut after the
+//   second-order term, c = beta (1 - x/2).
+__device__ __forceinline__ float gate_coef(int coef, float beta, float lam) {
+  if (coef == 0) return gate_alpha(beta, lam);
+  if (coef == 1) return beta;
+  const float x = beta * lam;
+  if (coef == 2) return beta * (1.f + x * (-0.5f + x * (1.f / 6.f - x * (1.f / 24.f))));
+  return beta * (1.f - 0.5f * x);
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
 // every lane of a group receiving the group's sum. Within a 16-lane row the
 // exchange uses DPP (quad permutes, then half-row and row mirrors).

@@ -45,11 +45,33 @@ extern "C" {
 
 typedef enum { EFLA_DTYPE_F32 = 0, EFLA_DTYPE_BF16 = 1 } efla_dtype;
 
+/*
+ * Scalar of the rank-1 step S_t = (I - c k k^T) S_{t-1} + c k v^T, with
+ * x = beta lambda, lambda = ||k||^2 (every choice keeps the same update form,
+ * so every kernel serves all four):
+ *   EXACT   c = -expm1(-beta lambda~)/lambda~, lambda~ = max(lambda, 1e-12):
+ *           the exact flow (papernotes note, 关键设计 item 2; default).
+ *   EULER   c = beta: one explicit Euler step, the delta rule (same note,
+ *           关键设计 item 1).
+ *   RK4     c = beta (1 - x/2 + x^2/6 - x^3/24): one classical RK4 step; the
+ *           matrix polynomial of the jsqmd.com article "EFLA注意力机制：优化挑战
+ *           与训练策略解析", section 5.3, collapsed by A^n = lambda^(n-1) A.
+ *   ORDER2  c = beta (1 - x/2): the same series cut after the second-order
+ *           term, the second-order approximation that section names.
+ * All four are evaluated in fp32. Only EXACT floors lambda.
+ */
+typedef enum {
+  EFLA_COEF_EXACT = 0,
+  EFLA_COEF_EULER = 1,
+  EFLA_COEF_RK4 = 2,
+  EFLA_COEF_ORDER2 = 3
+} efla_coef;
+
 typedef enum {
   EFLA_OK = 0,
   EFLA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   EFLA_ERR_BAD_SHAPE = 2,    /* B, H or T < 1, or d_k != d_v */
-  EFLA_ERR_UNSUPPORTED = 3,  /* head dim, chunk size or dtype outside the supported set */
+  EFLA_ERR_UNSUPPORTED = 3,  /* head dim, chunk size, dtype or coefficient outside the supported set */
   EFLA_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
   EFLA_ERR_WORKSPACE = 5,    /* workspace smaller than efla_fwd_chunked_workspace_bytes() */
   EFLA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
@@ -84,13 +106,14 @@ size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  *             and are overwritten; calls sharing one workspace must not
  *             overlap in time.
  *   chunk     tokens per chunk, one of 16, 32, 64. T need not be a multiple.
+ *   coef      step coefficient (efla_coef; EFLA_COEF_EXACT for EFLA itself).
  * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64};
  * fp32 with d = 128 needs chunk <= 32. Anything else: EFLA_ERR_UNSUPPORTED.
  */
 efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                              const float* s0, void* o, float* s_final, void* workspace,
                              size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
-                             int chunk, efla_dtype dt, void* stream);
+                             int chunk, efla_coef coef, efla_dtype dt, void* stream);
 
 /*
  * One token per head, token-serial (the recurrent decode form; section 整体框架
@@ -100,11 +123,13 @@ efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const 
  *   beta      [B, H], element type dt.
  *   state     [B, H, d_k, d_v] fp32; read, then overwritten with S_t.
  *   o         [B, H, d_v] output S_t^T q_t, element type dt.
+ *   coef      step coefficient (efla_coef), as in efla_fwd_chunked.
  * Supported: d in {16, 32, 64, 128}, fp32 or bf16.
  */
 efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
                                     const void* beta, float* state, void* o, int B, int H,
-                                    int d_k, int d_v, efla_dtype dt, void* stream);
+                                    int d_k, int d_v, efla_coef coef, efla_dtype dt,
+                                    void* stream);
 
 /* Static, human-readable name of a status code. Never NULL. */
 const char* efla_status_string(efla_status s);

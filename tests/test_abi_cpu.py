@@ -45,14 +45,14 @@ FAKE = 0x100000  # never dereferenced: every call below fails validation first
 
 
 def chunked(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, s0=None, o=FAKE, sf=None, ws=None, wsb=0,
-            B=1, H=1, T=8, dk=64, dv=64, chunk=64, dt=1):
-    return lib.efla_fwd_chunked(q, k, v, beta, s0, o, sf, ws, wsb, B, H, T, dk, dv, chunk, dt,
-                                None)
+            B=1, H=1, T=8, dk=64, dv=64, chunk=64, coef=0, dt=1):
+    return lib.efla_fwd_chunked(q, k, v, beta, s0, o, sf, ws, wsb, B, H, T, dk, dv, chunk, coef,
+                                dt, None)
 
 
 def step(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, state=FAKE, o=FAKE, B=1, H=1, dk=64, dv=64,
-         dt=1):
-    return lib.efla_fwd_recurrent_step(q, k, v, beta, state, o, B, H, dk, dv, dt, None)
+         coef=0, dt=1):
+    return lib.efla_fwd_recurrent_step(q, k, v, beta, state, o, B, H, dk, dv, coef, dt, None)
 
 
 def test_chunked_rejects_bad_arguments_before_launch():
@@ -70,6 +70,8 @@ def test_chunked_rejects_bad_arguments_before_launch():
     assert chunked(lib, chunk=128) == 3
     assert chunked(lib, dt=2) == 3
     assert chunked(lib, dk=128, dv=128, chunk=64, dt=0) == 3  # fp32, d=128 needs chunk <= 32
+    assert chunked(lib, coef=4) == 3
+    assert chunked(lib, coef=-1) == 3
     assert chunked(lib, q=FAKE + 8) == 4
     assert chunked(lib, o=FAKE + 4) == 4
     assert chunked(lib, s0=FAKE + 4) == 4
@@ -86,6 +88,7 @@ def test_step_rejects_bad_arguments_before_launch():
     assert step(lib, dv=16) == 2
     assert step(lib, dk=96, dv=96) == 3
     assert step(lib, dt=7) == 3
+    assert step(lib, coef=4) == 3
     assert step(lib, state=FAKE + 8) == 4
     assert step(lib, k=FAKE + 2) == 4
 
@@ -117,3 +120,11 @@ def test_segmented_call_checks_its_workspace_before_launch():
     assert chunked(lib, ws=None, wsb=0, **kw) == 5
     assert chunked(lib, ws=FAKE, wsb=need - 1, **kw) == 5
     assert chunked(lib, ws=FAKE + 8, wsb=need, **kw) == 4  # workspace must be 16-byte aligned
+
+
+def test_coefficient_names_match_the_header():
+    text = open(os.path.join(ROOT, "include", "efla.h")).read()
+    for name, value in efla.COEFS.items():
+        assert f"EFLA_COEF_{name.upper()} = {value}" in text
+    with pytest.raises(ValueError):
+        efla._coef("heun")

@@ -203,6 +203,69 @@ def test_decode_steps(efla, dt, d):
     assert normwise(od, o_ref) <= tol and normwise(st.cpu(), s_ref) <= tol
 
 
+# ------------------------------------------------------------ step rules
+# The Euler, one-step RK4 and second-order scalars run through the same
+# kernels as the exact flow. Keys are kept short enough (x = beta ||k||^2 <
+# 1.7) that all three stay stable, so their outputs are comparable at the
+# same bars. fp32 d=16 C=64 takes the 4-wave kernel, the rest the pipelined
+# one; the last shape takes the time-segmented path.
+RULES = {"euler": oracle.EULER, "rk4": oracle.RK4, "order2": oracle.ORDER2}
+RULE_CASES = [("bf16", 128, 64, 1, 3, 197), ("f32", 64, 32, 2, 2, 101), ("bf16", 32, 16, 2, 3, 53),
+              ("f32", 16, 64, 1, 2, 133), ("bf16", 128, 64, 1, 2, 8229)]
+
+
+@pytest.mark.parametrize("rule", sorted(RULES))
+@pytest.mark.parametrize("dt,d,c,B,H,T", RULE_CASES)
+def test_chunked_step_rules(efla, rule, dt, d, c, B, H, T):
+    ws = efla.efla_fwd_chunked_workspace_bytes(B, H, T, d, d, c, DT[dt])
+    note(f"[rule {rule}] dtype={dt} d={d} chunk={c} B={B} H={H} T={T} workspace={ws}")
+    x = efla_inputs.random_case(5150 + d + T, B=B, H=H, T=T, d=d, dtype=dt, k_lo=0.3, k_hi=1.3,
+                                s0_std=0.3)
+    g = to_dev(x)
+    o, sT = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=c, coef=rule)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"], mode=RULES[rule],
+                              nthreads=8)
+    tol = TOL[DT[dt]]
+    eo, es = normwise(o.float().cpu(), o_ref), normwise(sT.cpu(), s_ref)
+    note(f"   err o={eo:.3e} S_T={es:.3e} (tol {tol})")
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.parametrize("rule", sorted(RULES))
+@pytest.mark.parametrize("dt,d", [("f32", 32), ("bf16", 128)])
+def test_decode_step_rules(efla, rule, dt, d):
+    note(f"[decode rule {rule}] dtype={dt} d={d}")
+    steps = 10
+    x = efla_inputs.random_case(640 + d, B=2, H=3, T=steps, d=d, dtype=dt, k_lo=0.3, k_hi=1.3,
+                                s0_std=0.5)
+    g = to_dev(x)
+    st = g["s0"].clone()
+    outs = [efla.efla_fwd_recurrent_step(g["q"][:, :, i].contiguous(), g["k"][:, :, i].contiguous(),
+                                         g["v"][:, :, i].contiguous(),
+                                         g["beta"][:, :, i].contiguous(), st, coef=rule)
+            for i in range(steps)]
+    od = torch.stack(outs, 2).float().cpu()
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"], mode=RULES[rule])
+    tol = TOL[DT[dt]]
+    assert normwise(od, o_ref) <= tol and normwise(st.cpu(), s_ref) <= tol
+
+
+def test_step_rules_are_told_apart(efla):
+    """Each rule's fp32 output matches its own oracle at 1e-4 while the
+    oracle puts it at least 1e-2 (normwise) away from the exact flow, so the
+    parity check above would catch a rule that never reached the kernels."""
+    x = efla_inputs.random_case(8080, B=1, H=2, T=96, d=64, dtype="f32", k_lo=0.8, k_hi=1.3)
+    g = to_dev(x)
+    r_ex, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], None)
+    for rule, mode in RULES.items():
+        o_r, _ = efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], None, chunk=32, coef=rule)
+        r_r, _ = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], None, mode=mode)
+        e, gap = normwise(o_r.cpu(), r_r), normwise(torch.from_numpy(r_r), r_ex)
+        note(f"   {rule}: err vs own oracle {e:.3e}, oracle gap to exact {gap:.3e}")
+        assert e <= 1e-4 and gap >= 1e-2
+
+
 # ------------------------------------------------------------ properties
 def test_single_token_chunked_equals_decode(efla):
     x = efla_inputs.random_case(5, B=2, H=4, T=1, d=128, dtype="f32", s0_std=0.5)
