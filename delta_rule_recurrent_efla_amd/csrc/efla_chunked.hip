@@ -770,6 +770,13 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) uf[cc][f] = MM::template acc<NB>(u[cc], f);
+        // T Y only reads registers once its fragments are in, so the
+        // compiler would sink it below the barrier into phase B; consuming
+        // U' here keeps it in phase A
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) asm volatile("" : "+v"(uf[cc][f]));
       }
       __syncthreads();
       // ---- phase B: O^T = S^T Q^T (S before this chunk's update, Q from
@@ -1067,23 +1074,40 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     const CT* bg = (const CT*)a.beta + tok0;
     Vec kreg[NLK], qreg[NLK], vreg[NLV];
     CT breg;
+    // Loads go through buffer descriptors that start at the chunk's first
+    // token and end with this sequence piece: rows past T read as zeros, so
+    // the ragged tail needs no clamping and no masking. The per-lane byte
+    // offsets are the same for every chunk.
+    auto chunk_rsrc = [&](const CT* base, int chunk, int col0) {
+      const long long tok = (long long)chunk * C;
+      return buf_rsrc(base + tok * D + col0, ((long long)(T - tok) * D - col0) * (long long)sizeof(CT));
+    };
+    unsigned koff[NLK], voff[NLV];
+#pragma unroll
+    for (int j = 0; j < NLK; ++j) {
+      const int idx = lt + NLT * j;
+      koff[j] = (unsigned)(((idx / VPR) * D + (idx % VPR) * VE) * (int)sizeof(CT));
+    }
+#pragma unroll
+    for (int j = 0; j < NLV; ++j) {
+      const int idx = lt + NLT * j;
+      voff[j] = (unsigned)(((idx / VPRV) * D + (idx % VPRV) * VE) * (int)sizeof(CT));
+    }
     // Row-sum layout of the key slots: slot j, lane (q, p) = (lane / VPR,
     // lane % VPR) holds piece p of row (64 w' + NLT j) / VPR + q of this wave
     // w'. Lane (q, p < NLK) computes a for slot p's row q and loads its beta.
     const int lw = lt >> 6;        // loader wave 0..3
     const int lq = lane / VPR, lp = lane % VPR;
     const int arow = (64 * lw + NLT * lp) / VPR + lq;  // row of this lane's a (when lp < NLK)
-    // coalesced 16-byte loads of one chunk; rows past T are clamped here and
-    // zeroed when staged
+    // coalesced 16-byte loads of one chunk
     auto load_k = [&](int chunk) {
-      const int t0 = chunk * C;
+      const auto rk = chunk_rsrc(kg, chunk, 0);
 #pragma unroll
-      for (int j = 0; j < NLK; ++j) {
-        const int idx = lt + NLT * j;
-        const int r = idx / VPR, cv = idx % VPR;
-        if (idx < C * VPR) kreg[j] = *(const Vec*)(kg + (size_t)min(t0 + r, T - 1) * D + cv * VE);
-      }
-      breg = bg[min(t0 + min(arow, C - 1), T - 1)];
+      for (int j = 0; j < NLK; ++j)
+        if (lt + NLT * j < C * VPR) buf_load(rk, koff[j], kreg[j]);
+      const long long tok = (long long)chunk * C;
+      buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
+               (unsigned)(min(arow, C - 1) * (int)sizeof(CT)), breg);
     };
     // lambda = ||k||^2 per row by a DPP row sum over the row's VPR lanes, then
     // a = -expm1(-beta lambda)/lambda for the chunk whose keys are in kreg, into
@@ -1099,19 +1123,14 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       if (lp < NLK && arow < C) alpha[arow] = arow < nval ? gate_coef(a.coef, to_f32(breg), l) : 0.f;
     };
     auto load_qv = [&](int chunk) {
-      const int t0 = chunk * C;
+      const auto rq = chunk_rsrc(qg, chunk, 0);
+      const auto rv = chunk_rsrc(vg, chunk, v0);
 #pragma unroll
-      for (int j = 0; j < NLK; ++j) {
-        const int idx = lt + NLT * j;
-        const int r = idx / VPR, cv = idx % VPR;
-        if (idx < C * VPR) qreg[j] = *(const Vec*)(qg + (size_t)min(t0 + r, T - 1) * D + cv * VE);
-      }
+      for (int j = 0; j < NLK; ++j)
+        if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
 #pragma unroll
-      for (int j = 0; j < NLV; ++j) {
-        const int idx = lt + NLT * j;
-        const int r = idx / VPRV, cv = idx % VPRV;
-        if (idx < C * VPRV) vreg[j] = *(const Vec*)(vg + (size_t)min(t0 + r, T - 1) * D + v0 + cv * VE);
-      }
+      for (int j = 0; j < NLV; ++j)
+        if (lt + NLT * j < C * VPRV) buf_load(rv, voff[j], vreg[j]);
     };
     auto loader = [&](auto pwc) {
       constexpr int PW = decltype(pwc)::value;  // loader 0..3
@@ -1170,37 +1189,24 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         asm volatile("" : "+v"(li), "+v"(g));
         // ---- phase A: stage chunk n (keys, queries, value slice)
         if (act) {
-          const int nval = min(C, T - n * C);
-          auto stage = [&](auto fullc) {
-            constexpr bool FULL = decltype(fullc)::value;  // no rows past T
+          // rows past T arrived as zeros
 #pragma unroll
-            for (int j = 0; j < NLK; ++j) {
-              const int idx = lt + NLT * j;
-              if (idx < C * VPR) {
-                const int r = idx / VPR, cv = idx % VPR;
-                Vec kk = kreg[j], qq = qreg[j];
-                if constexpr (!FULL) {
-                  if (r >= nval) kk = qq = Vec{};
-                }
-                st_perm(&B.K[r][0], cv * VE, kk);
-                st_perm(&B.Q[r][0], cv * VE, qq);
-              }
+          for (int j = 0; j < NLK; ++j) {
+            const int idx = lt + NLT * j;
+            if (idx < C * VPR) {
+              const int r = idx / VPR, cv = idx % VPR;
+              st_perm(&B.K[r][0], cv * VE, kreg[j]);
+              st_perm(&B.Q[r][0], cv * VE, qreg[j]);
             }
+          }
 #pragma unroll
-            for (int j = 0; j < NLV; ++j) {
-              const int idx = lt + NLT * j;
-              if (idx < C * VPRV) {
-                const int r = idx / VPRV, cv = idx % VPRV;
-                Vec vv = vreg[j];
-                if constexpr (!FULL) {
-                  if (r >= nval) vv = Vec{};
-                }
-                *(Vec*)&B.V[r][cv * VE] = vv;  // 16-byte aligned rows
-              }
+          for (int j = 0; j < NLV; ++j) {
+            const int idx = lt + NLT * j;
+            if (idx < C * VPRV) {
+              const int r = idx / VPRV, cv = idx % VPRV;
+              *(Vec*)&B.V[r][cv * VE] = vreg[j];  // 16-byte aligned rows
             }
-          };
-          if (nval == C) stage(std::true_type{});
-          else stage(std::false_type{});
+          }
         }
         // first M job of the chunk whose state pass runs now
         if constexpr (NA > 0) {

@@ -47,6 +47,27 @@ __device__ __forceinline__ float gate_coef(int coef, float beta, float lam) {
   return beta * (1.f - 0.5f * x);
 }
 
+// Raw buffer access (gfx9 buffer descriptor, stride 0, range checked): a load
+// whose per-lane byte offset is at or past `bytes` returns zeros and touches
+// no memory. Descriptors are wave-uniform (scalar registers); per-lane offsets
+// are 32-bit, so loads need no 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, bf16x8& v) {
+  v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, floatx4& v) {
+  v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, bf16& v) {
+  v = __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, unsigned off, float& v) {
+  v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
 // every lane of a group receiving the group's sum. Within a 16-lane row the
 // exchange uses DPP (quad permutes, then half-row and row mirrors).
