@@ -65,6 +65,11 @@ def _load():
     lib.efla_oracle_fwd.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp,
                                     ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int]
+    lib.efla_oracle_coef_grad.restype = None
+    lib.efla_oracle_coef_grad.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, dp, dp]
+    lib.efla_oracle_bwd.restype = ctypes.c_int
+    lib.efla_oracle_bwd.argtypes = [ctypes.c_int] + [dp] * 12 + [
+        ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -135,3 +140,42 @@ def fwd(q, k, v, beta, s0=None, mode: int = EXACT, nthreads: int = 1,
     if want_norms:
         return o, sf, sn
     return o, sf
+
+
+def coef_grad(mode: int, beta: float, lam: float):
+    """(dc/dbeta, dc/dlambda) of the step scalar."""
+    gb, gl = ctypes.c_double(), ctypes.c_double()
+    _load().efla_oracle_coef_grad(int(mode), float(beta), float(lam), ctypes.byref(gb),
+                                  ctypes.byref(gl))
+    return gb.value, gl.value
+
+
+def bwd(q, k, v, beta, dout, s0=None, dsT=None, mode: int = EXACT, nthreads: int = 1):
+    """Reverse-mode gradients of L(o, S_T) through the sequential fp64 forward.
+
+    q, k: [..., T, dk]; v, dout: [..., T, dv]; beta: [..., T]; s0, dsT:
+    [..., dk, dv] or None (zeros). Returns (dq, dk, dv, dbeta, ds0) as float64
+    arrays (ds0 has the shape of one state per head)."""
+    q, k, v, beta, dout = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(dout)
+    lead = beta.shape[:-1]
+    T = beta.shape[-1]
+    dk_ = k.shape[-1]
+    dv_ = v.shape[-1]
+    nh = int(np.prod(lead)) if len(lead) else 1
+    assert q.shape == lead + (T, dk_) and k.shape == lead + (T, dk_)
+    assert v.shape == lead + (T, dv_) and dout.shape == lead + (T, dv_)
+    s0a = None if s0 is None else _f64(s0)
+    dsa = None if dsT is None else _f64(dsT)
+    for x in (s0a, dsa):
+        assert x is None or x.shape == lead + (dk_, dv_)
+    dq = np.zeros(lead + (T, dk_))
+    dkk = np.zeros(lead + (T, dk_))
+    dvv = np.zeros(lead + (T, dv_))
+    db = np.zeros(lead + (T,))
+    ds0 = np.zeros(lead + (dk_, dv_))
+    rc = _load().efla_oracle_bwd(int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0a),
+                                 _ptr(dout), _ptr(dsa), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(db),
+                                 _ptr(ds0), nh, T, dk_, dv_, int(nthreads))
+    if rc != 0:
+        raise ValueError("efla_oracle_bwd rejected the sizes")
+    return dq, dkk, dvv, db, ds0

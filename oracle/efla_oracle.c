@@ -175,3 +175,181 @@ int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
   free(jobs);
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward (reverse mode through the token-serial forward above). The pages
+ * give no gradient formulas: this is the derivative of the forward as it
+ * stands, written step by step. With u_t = c_t (v_t - S_{t-1}^T k_t),
+ * S_t = S_{t-1} + k_t u_t^T, o_t = S_t^T q_t, and G_t the gradient of the
+ * loss with respect to S_t (starting from the given dS_T), walking t down:
+ *   G    += q_t do_t^T,        dq_t  = S_t do_t
+ *   du    = G^T k_t,           dk_t  = G u_t - c_t S_{t-1} du
+ *   dv_t  = c_t du,            dc_t  = du . (v_t - S_{t-1}^T k_t)
+ *   G_{t-1} = G - c_t k_t du^T
+ * and the scalar's chain rule: dbeta_t = dc_t dc/dbeta, dk_t += 2 dc_t
+ * (dc/dlambda) k_t.
+ */
+
+/* dc/dbeta and dc/dlambda of efla_oracle_coef. */
+void efla_oracle_coef_grad(int mode, double beta, double lam, double* dbeta, double* dlam) {
+  double x = beta * lam;
+  switch (mode) {
+    case EFLA_ORACLE_EULER:
+      *dbeta = 1.0;
+      *dlam = 0.0;
+      return;
+    case EFLA_ORACLE_RK4:
+      *dbeta = 1.0 - x + x * x / 2.0 - x * x * x / 6.0;
+      *dlam = beta * beta * (-0.5 + x / 3.0 - x * x / 8.0);
+      return;
+    case EFLA_ORACLE_ORDER2:
+      *dbeta = 1.0 - x;
+      *dlam = -beta * beta / 2.0;
+      return;
+    default: {
+      double lamc = lam > 1e-12 ? lam : 1e-12;
+      double xc = beta * lamc;
+      *dbeta = exp(-xc);
+      if (!(lam > 1e-12)) {
+        *dlam = 0.0; /* the floor makes the coefficient constant in lambda */
+      } else if (fabs(xc) < 1e-3) {
+        /* (beta e^{-x} - c)/lambda = beta^2 sum_{n>=1} (-1)^n n x^{n-1}/(n+1)! */
+        *dlam = beta * beta * (-0.5 + xc / 3.0 - xc * xc / 8.0 + xc * xc * xc / 30.0);
+      } else {
+        *dlam = (beta * exp(-xc) - efla_oracle_alpha(beta, lam)) / lamc;
+      }
+    }
+  }
+}
+
+typedef struct {
+  int mode;
+  const double *q, *k, *v, *beta, *s0, *dout, *dsT;
+  double *dq, *dk, *dv, *dbeta, *ds0;
+  long nh, T;
+  int dk_, dv_;
+  long h_begin, h_end;
+} oracle_bwd_job;
+
+static void bwd_head(const oracle_bwd_job* J, long h) {
+  const long T = J->T;
+  const int dk = J->dk_, dv = J->dv_;
+  const size_t ss = (size_t)dk * dv;
+  /* every state S_0..S_T of the forward */
+  double* St = (double*)malloc(sizeof(double) * ss * (size_t)(T + 1));
+  if (J->s0) memcpy(St, J->s0 + (size_t)h * ss, sizeof(double) * ss);
+  else memset(St, 0, sizeof(double) * ss);
+  for (long t = 0; t < T; ++t) {
+    memcpy(St + (size_t)(t + 1) * ss, St + (size_t)t * ss, sizeof(double) * ss);
+    efla_oracle_step(J->mode, J->q + ((size_t)h * T + t) * dk, J->k + ((size_t)h * T + t) * dk,
+                     J->v + ((size_t)h * T + t) * dv, J->beta[(size_t)h * T + t],
+                     St + (size_t)(t + 1) * ss, NULL, dk, dv);
+  }
+  double* G = (double*)malloc(sizeof(double) * ss);
+  if (J->dsT) memcpy(G, J->dsT + (size_t)h * ss, sizeof(double) * ss);
+  else memset(G, 0, sizeof(double) * ss);
+  double* du = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* u = (double*)malloc(sizeof(double) * (size_t)dv);
+  double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (long t = T - 1; t >= 0; --t) {
+    const double* q = J->q + ((size_t)h * T + t) * dk;
+    const double* k = J->k + ((size_t)h * T + t) * dk;
+    const double* v = J->v + ((size_t)h * T + t) * dv;
+    const double* dout = J->dout + ((size_t)h * T + t) * dv;
+    double* dq = J->dq + ((size_t)h * T + t) * dk;
+    double* dkk = J->dk + ((size_t)h * T + t) * dk;
+    double* dvv = J->dv + ((size_t)h * T + t) * dv;
+    const double* Sp = St + (size_t)t * ss;       /* S_{t-1} */
+    const double* Sn = St + (size_t)(t + 1) * ss; /* S_t */
+    const double b = J->beta[(size_t)h * T + t];
+    double lam = 0.0;
+    for (int i = 0; i < dk; ++i) lam += k[i] * k[i];
+    const double c = efla_oracle_coef(J->mode, b, lam);
+    /* read-out of S_t */
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] += q[i] * dout[j];
+    for (int i = 0; i < dk; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j < dv; ++j) acc += Sn[(size_t)i * dv + j] * dout[j];
+      dq[i] = acc;
+    }
+    /* u = c (v - S_{t-1}^T k) */
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += Sp[(size_t)i * dv + j] * k[i];
+      p[j] = v[j] - acc;
+      u[j] = c * p[j];
+    }
+    double dc = 0.0;
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += G[(size_t)i * dv + j] * k[i];
+      du[j] = acc;
+      dvv[j] = c * acc;
+      dc += acc * p[j];
+    }
+    for (int i = 0; i < dk; ++i) {
+      double a1 = 0.0, a2 = 0.0;
+      for (int j = 0; j < dv; ++j) {
+        a1 += G[(size_t)i * dv + j] * u[j];
+        a2 += Sp[(size_t)i * dv + j] * du[j];
+      }
+      dkk[i] = a1 - c * a2;
+    }
+    double gb, gl;
+    efla_oracle_coef_grad(J->mode, b, lam, &gb, &gl);
+    J->dbeta[(size_t)h * T + t] = dc * gb;
+    for (int i = 0; i < dk; ++i) dkk[i] += 2.0 * dc * gl * k[i];
+    /* G_{t-1} = G - c k du^T */
+    for (int i = 0; i < dk; ++i)
+      for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] -= c * k[i] * du[j];
+  }
+  if (J->ds0) memcpy(J->ds0 + (size_t)h * ss, G, sizeof(double) * ss);
+  free(St);
+  free(G);
+  free(du);
+  free(u);
+  free(p);
+}
+
+static void* bwd_range(void* arg) {
+  const oracle_bwd_job* J = (const oracle_bwd_job*)arg;
+  for (long h = J->h_begin; h < J->h_end; ++h) bwd_head(J, h);
+  return NULL;
+}
+
+/*
+ * Gradients of a loss L(o, S_T) given dout = dL/do [nh, T, dv] and dsT =
+ * dL/dS_T [nh, dk, dv] (NULL: zero). Outputs dq, dk [nh, T, dk], dv [nh, T, dv],
+ * dbeta [nh, T], ds0 [nh, dk, dv] (NULL: not written). s0 NULL means zeros.
+ * Returns 0, or -1 on bad sizes.
+ */
+int efla_oracle_bwd(int mode, const double* q, const double* k, const double* v,
+                    const double* beta, const double* s0, const double* dout, const double* dsT,
+                    double* dq, double* dk, double* dv, double* dbeta, double* ds0, long nh, long T,
+                    int dk_, int dv_, int nthreads) {
+  if (nh < 0 || T < 0 || dk_ < 1 || dv_ < 1) return -1;
+  if (nh == 0) return 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > nh) nthreads = (int)nh;
+  oracle_bwd_job base = {mode, q, k, v, beta, s0, dout, dsT, dq, dk, dv, dbeta, ds0,
+                         nh, T, dk_, dv_, 0, nh};
+  if (nthreads == 1) {
+    bwd_range(&base);
+    return 0;
+  }
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  oracle_bwd_job* jobs = (oracle_bwd_job*)malloc(sizeof(oracle_bwd_job) * (size_t)nthreads);
+  long per = nh / nthreads, rem = nh % nthreads, h = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = base;
+    jobs[i].h_begin = h;
+    h += per + (i < rem ? 1 : 0);
+    jobs[i].h_end = h;
+    pthread_create(&th[i], NULL, bwd_range, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  return 0;
+}
