@@ -74,6 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          i, i, i, i, i, i, i, i, vp]
         lib.efla_fwd_recurrent_step.restype = i
         lib.efla_fwd_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+        lib.efla_bwd_chunked_workspace_bytes.restype = sz
+        lib.efla_bwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        lib.efla_bwd_chunked.restype = i
+        lib.efla_bwd_chunked.argtypes = [vp] * 13 + [sz] + [i] * 8 + [vp]
         lib.efla_status_string.restype = ctypes.c_char_p
         lib.efla_status_string.argtypes = [i]
         _lib = lib
@@ -199,3 +203,47 @@ def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                      _stream(dev, stream))
     _raise(st)
     return o
+
+
+def efla_bwd_chunked_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int, chunk: int,
+                                     dtype: torch.dtype) -> int:
+    return int(load_library().efla_bwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk,
+                                                               _DTYPES[dtype]))
+
+
+def efla_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                     dout: torch.Tensor, s0: Optional[torch.Tensor] = None,
+                     ds_final: Optional[torch.Tensor] = None, chunk: int = 64, coef="exact",
+                     want_ds0: bool = True, stream=None):
+    """Backward of efla_fwd_chunked for a loss L(o, S_T): given dout = dL/do
+    [B,H,T,d] (input dtype) and ds_final = dL/dS_T [B,H,d,d] fp32 or None,
+    returns (dq, dk, dv, dbeta, ds0) with dq, dk, dv, dbeta in the input dtype
+    and ds0 fp32 (None unless want_ds0)."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("dout", dout)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta, dout")
+    for name, t in (("s0", s0), ("ds_final", ds_final)):
+        if t is not None:
+            _require(t, name, torch.float32, dev)
+            if t.shape != (B, H, d, d):
+                raise ValueError(f"{name} must be [B, H, d_k, d_v]")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    db = torch.empty_like(beta)
+    ds0 = torch.empty((B, H, d, d), dtype=torch.float32, device=dev) if want_ds0 else None
+    ws_bytes = int(lib.efla_bwd_chunked_workspace_bytes(B, H, T, d, d, chunk, _DTYPES[dt]))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    st = lib.efla_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(dout),
+                              _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(ds0),
+                              _ptr(ws), ws_bytes, B, H, T, d, d, int(chunk), _coef(coef),
+                              _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
+    return dq, dk, dv, db, ds0

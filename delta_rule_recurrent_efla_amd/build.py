@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libefla.so")
 
-SOURCES = ["efla_api.hip", "efla_chunked.hip", "efla_decode.hip"]
+SOURCES = ["efla_api.hip", "efla_chunked.hip", "efla_decode.hip", "efla_backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

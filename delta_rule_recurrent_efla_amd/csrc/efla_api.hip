@@ -16,6 +16,12 @@ hipError_t efla_internal_launch_decode(const void* q, const void* k, const void*
                                        const void* beta, float* state, void* o, int NH, int d,
                                        int coef, int is_bf16, hipStream_t stream);
 
+size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16);
+hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v, const void* beta,
+                                    const float* s0, const void* dout, const float* dsT, void* dq, void* dk,
+                                    void* dv, void* dbeta, float* ds0, void* workspace, int NH, int T, int d,
+                                    int chunk, int coef, int is_bf16, hipStream_t stream);
+
 namespace {
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -89,6 +95,37 @@ extern "C" efla_status efla_fwd_recurrent_step(const void* q, const void* k, con
   const hipError_t e = efla_internal_launch_decode(q, k, v, beta, state, o, B * H, d_k,
                                                    (int)coef, dt == EFLA_DTYPE_BF16,
                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
+}
+
+extern "C" size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                                  efla_dtype dt) {
+  if (B < 1 || H < 1 || T < 1 || d_k != d_v) return 0;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return 0;
+  if (!chunked_supported(d_k, chunk, dt)) return 0;
+  if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return 0;
+  return efla_internal_bwd_workspace_bytes(B * H, T, d_k, chunk, dt == EFLA_DTYPE_BF16);
+}
+
+extern "C" efla_status efla_bwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                        const float* s0, const void* dout, const float* ds_final, void* dq,
+                                        void* dk, void* dv, void* dbeta, float* ds0, void* workspace,
+                                        size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                                        int chunk, efla_coef coef, efla_dtype dt, void* stream) {
+  if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta) return EFLA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || T < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
+  if (!chunked_supported(d_k, chunk, dt) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(s0) ||
+      !aligned16(ds_final) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ds0) ||
+      !aligned16(workspace) || !elem_aligned(beta, dt) || !elem_aligned(dbeta, dt))
+    return EFLA_ERR_MISALIGNED;
+  const size_t need = efla_bwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk, dt);
+  if (need == 0 || workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+  const hipError_t e = efla_internal_launch_bwd(q, k, v, beta, s0, dout, ds_final, dq, dk, dv, dbeta, ds0,
+                                                workspace, B * H, T, d_k, chunk, (int)coef,
+                                                dt == EFLA_DTYPE_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }
 

@@ -1,0 +1,580 @@
+// Backward of the chunk-parallel EFLA forward for gfx950: gradients of a loss
+// of o and S_T with respect to q, k, v, beta and S0.
+//
+// The pages give no gradient formulas (papernotes.org note "Exact Flow Linear
+// Attention: Exact Solution from Continuous-Time Dynamics" states the forward;
+// its 实验 sections train with it). This is reverse mode through the chunk
+// form of the forward (整体框架: WY/UT chunks). Per chunk with start state S,
+// D = diag(c) (the step scalars), A = strictly-lower(D K K^T),
+// T = (I + A)^{-1}, Yh = V - K S, U = T D Yh, M = lower-incl-diag(Q K^T):
+//   forward   O = Q S + M U,  S' = S + K^T U
+//   backward  dU = M^T dO + K dS',  G = T^T dU,  dV = D G
+//             dS = dS' + Q^T dO - K^T D G
+//             dM = lower-incl-diag(dO U^T),  E = strictly-lower(-G U^T)
+//             dc = rowsum(G * Yh) + rowsum(E * K K^T)
+//             dQ = dO S^T + dM K
+//             dK = dM^T Q + U dS'^T - D G S^T + D E K + E^T D K + 2 dc c_lambda k
+//             dbeta = dc c_beta
+// Four launches:
+//   1. the forward again (pipelined kernel, pass mode 2): the state at the
+//      start of every chunk;
+//   2. efla_bwd_prep_kernel, one workgroup per (head, chunk): c, c_beta,
+//      c_lambda, K K^T, T (by forward substitution in fp32), T^T and M^T;
+//   3. efla_bwd_state_kernel, one workgroup per (head, 64-column slice),
+//      chunks last to first: the dS recurrence (the only serial part), dV,
+//      G and the dS' of every chunk;
+//   4. efla_bwd_grad_kernel, one workgroup per (head, chunk): dq, dk, dbeta.
+// Arithmetic is fp32 throughout (v_mfma_f32_16x16x4_f32), for bf16 inputs too.
+
+#include <hip/hip_runtime.h>
+
+#include "efla_device.hpp"
+
+namespace efla {
+
+// acc += A B over k in [0, 16 nkb) for one 16x16 tile. fa(kb) returns
+// A(row li, 16 kb + 4 g + e), e = 0..3; fb(kb) returns B(16 kb + 4 g + e,
+// col li). Step e of block kb lets lane (g, li) supply k = 16 kb + 4 g + e to
+// v_mfma_f32_16x16x4_f32 (whose k index is g), so a row-major A and a
+// column-major B each give their four values as one 16-byte read. The result
+// holds rows 4 g + e, column li.
+template <class FA, class FB>
+__device__ __forceinline__ floatx4 mm16(floatx4 acc, int nkb, FA fa, FB fb) {
+  for (int kb = 0; kb < nkb; ++kb) {
+    const floatx4 a = fa(kb), b = fb(kb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ float ld1(const bf16* p) { return (float)*p; }
+
+// dc/dbeta and dc/dlambda of gate_coef, in fp32.
+__device__ __forceinline__ void gate_coef_grad(int coef, float beta, float lam, float& db, float& dl) {
+  if (coef == 1) {
+    db = 1.f;
+    dl = 0.f;
+    return;
+  }
+  const float x = beta * lam;
+  if (coef == 2) {
+    db = 1.f + x * (-1.f + x * (0.5f - x * (1.f / 6.f)));
+    dl = beta * beta * (-0.5f + x * (1.f / 3.f - x * (1.f / 8.f)));
+    return;
+  }
+  if (coef == 3) {
+    db = 1.f - x;
+    dl = -0.5f * beta * beta;
+    return;
+  }
+  const float lamc = fmaxf(lam, 1e-12f);
+  const float xc = beta * lamc;
+  const float ex = expf(-xc);
+  db = ex;
+  if (!(lam > 1e-12f)) {
+    dl = 0.f;  // the floor makes the scalar constant in lambda
+  } else if (fabsf(xc) < 0.1f) {
+    // (beta e^{-x} - c)/lambda = beta^2 sum_{n>=1} (-1)^n n x^{n-1}/(n+1)!
+    dl = beta * beta *
+         (-0.5f + xc * (1.f / 3.f + xc * (-1.f / 8.f + xc * (1.f / 30.f + xc * (-1.f / 144.f + xc * (1.f / 840.f))))));
+  } else {
+    dl = (beta * ex - gate_alpha(beta, lam)) / lamc;
+  }
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *beta, *dout;
+  const float *s0, *dsT;
+  void *dq, *dk, *dv, *dbeta;
+  float* ds0;
+  int T, nc, coef;
+  // workspace (fp32)
+  const float* sc;  // [head][chunk][d_v][d_k] state at the start of each chunk
+  float* dsc;       // [head][chunk][d_k][d_v] gradient of the state at each chunk's end
+  float* gw;        // [head][nc C][d_v] G rows
+  float *al, *fb, *fl;        // [head][nc C] c, dc/dbeta, dc/dlambda (0 past T)
+  float *gram, *tn, *tt, *mt;  // [head][chunk][C][C]: K K^T, T, T^T, M^T
+};
+
+// ---------------------------------------------------------------------------
+// 2. Per (head, chunk): scalars, K K^T, T = (I + A)^{-1}, T^T, M^T.
+template <typename CT, int D, int C>
+__global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
+  constexpr int LD = D + 4, LC = C + 4;
+  __shared__ __attribute__((aligned(16))) float Kf[C][LD];
+  __shared__ __attribute__((aligned(16))) float Qf[C][LD];
+  __shared__ __attribute__((aligned(16))) float Am[C][LC];  // strictly-lower D K K^T
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
+  const int t0 = ch * C, nval = min(C, a.T - t0);
+  const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
+  const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
+  for (int i = tid; i < C * D; i += 256) {
+    const int r = i / D, col = i % D;
+    Kf[r][col] = r < nval ? ld1(kg + (size_t)r * D + col) : 0.f;
+    Qf[r][col] = r < nval ? ld1(qg + (size_t)r * D + col) : 0.f;
+  }
+  __syncthreads();
+  const size_t rb = (size_t)h * a.nc * C + t0;  // row base of this chunk
+  __shared__ float cs[C];
+  if (tid < C) {
+    float lam = 0.f;
+    for (int col = 0; col < D; ++col) lam = fmaf(Kf[tid][col], Kf[tid][col], lam);
+    float c = 0.f, db = 0.f, dl = 0.f;
+    if (tid < nval) {
+      const float b = ld1((const CT*)a.beta + (size_t)h * a.T + t0 + tid);
+      c = gate_coef(a.coef, b, lam);
+      gate_coef_grad(a.coef, b, lam, db, dl);
+    }
+    cs[tid] = c;
+    a.al[rb + tid] = c;
+    a.fb[rb + tid] = db;
+    a.fl[rb + tid] = dl;
+  }
+  __syncthreads();
+  const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+  constexpr int NT = C / 16;
+  for (int tl = w; tl < NT * NT; tl += 4) {
+    const int I = tl / NT, J = tl % NT;
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    // K K^T and Q K^T tiles (I, J): B(k, j) = K[16J + j][k], a row of K
+    const floatx4 gk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Kf[16 * I + li][16 * kb + 4 * g]; },
+                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
+    const floatx4 qk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Qf[16 * I + li][16 * kb + 4 * g]; },
+                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * I + 4 * g + e, j = 16 * J + li;
+      a.gram[mb + (size_t)i * C + j] = gk[e];
+      Am[i][j] = j < i ? cs[i] * gk[e] : 0.f;
+      // M[i][j] = q_i . k_j for j <= i; stored transposed: M^T[j][i]
+      a.mt[mb + (size_t)j * C + i] = j <= i ? qk[e] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    // column lane of T = (I + A)^{-1} by forward substitution: row i of
+    // (I + A) t = e_lane gives t_i = [i == lane] - sum_{m<i} A[i][m] t_m
+    if (lane < C) {
+      float t[C];
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int m4 = 0; m4 < i; m4 += 4) {
+          const floatx4 a4 = *(const floatx4*)&Am[i][m4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m4 + e < i) s = fmaf(-a4[e], t[m4 + e], s);
+        }
+        t[i] = s;
+      }
+      // lane holds column `lane` of T: row `lane` of T^T, and T[i][lane]
+#pragma unroll
+      for (int i4 = 0; i4 < C; i4 += 4)
+        *(floatx4*)&a.tt[mb + (size_t)lane * C + i4] = floatx4{t[i4], t[i4 + 1], t[i4 + 2], t[i4 + 3]};
+#pragma unroll
+      for (int i = 0; i < C; ++i) a.tn[mb + (size_t)i * C + lane] = t[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Per (head, BV-column slice), chunks last to first: the dS recurrence.
+// Wave w < BV/16 owns columns 16 w .. 16 w + 15 of the slice; its d_k x 16
+// block of dS stays in MFMA accumulator registers.
+template <int D, int C, int BV>
+struct StateSmem {
+  static constexpr int LD = D + 4, LC = C + 4;
+  float Kf[C][LD];    // K rows
+  float KT[D][LC];    // K^T
+  float QT[D][LC];    // Q^T
+  float MT[C][LC];    // M^T
+  float TT[C][LC];    // T^T
+  float dOT[BV][LC];  // dO^T (slice columns)
+  float al[C];
+};
+
+template <typename CT, int D, int C, int BV>
+__global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
+  using Sm = StateSmem<D, C, BV>;
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  constexpr int NKT = D / 16, NB = C / 16, NW = BV / 16;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nvt = D / BV;
+  const int h = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * BV;
+  const int col = v0 + 16 * w + li;  // this lane's state column (when w < NW)
+  const bool owner = w < NW;
+  floatx4 ds[NKT];
+#pragma unroll
+  for (int rt = 0; rt < NKT; ++rt) ds[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (owner && a.dsT) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[rt][e] = a.dsT[((size_t)h * D + 16 * rt + 4 * g + e) * D + col];
+  }
+  const CT* kg = (const CT*)a.k + (size_t)h * a.T * D;
+  const CT* qg = (const CT*)a.q + (size_t)h * a.T * D;
+  const CT* dog = (const CT*)a.dout + (size_t)h * a.T * D;
+  for (int ch = a.nc - 1; ch >= 0; --ch) {
+    const int t0 = ch * C, nval = min(C, a.T - t0);
+    const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+    // dS' of this chunk (natural layout [d_k][d_v])
+    if (owner) {
+      float* dst = a.dsc + ((size_t)h * a.nc + ch) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+    }
+    __syncthreads();  // the previous chunk's reads of LDS are done
+    for (int i = tid; i < C * D; i += 256) {
+      const int r = i / D, c = i % D;
+      const float kv = r < nval ? ld1(kg + (size_t)(t0 + r) * D + c) : 0.f;
+      const float qv = r < nval ? ld1(qg + (size_t)(t0 + r) * D + c) : 0.f;
+      sm.Kf[r][c] = kv;
+      sm.KT[c][r] = kv;
+      sm.QT[c][r] = qv;
+    }
+    for (int i = tid; i < C * BV; i += 256) {
+      const int r = i / BV, c = i % BV;
+      sm.dOT[c][r] = r < nval ? ld1(dog + (size_t)(t0 + r) * D + v0 + c) : 0.f;
+    }
+    for (int i = tid; i < C * C; i += 256) {
+      const int r = i / C, c = i % C;
+      sm.MT[r][c] = a.mt[mb + i];
+      sm.TT[r][c] = a.tt[mb + i];
+    }
+    if (tid < C) sm.al[tid] = a.al[(size_t)h * a.nc * C + t0 + tid];
+    __syncthreads();
+    if (owner) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      // dU = M^T dO + K dS'
+      floatx4 du[NB];
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = mm16(z, NB, [&](int kb) { return *(const floatx4*)&sm.MT[16 * I + li][16 * kb + 4 * g]; },
+                           [&](int kb) { return *(const floatx4*)&sm.dOT[16 * w + li][16 * kb + 4 * g]; });
+#pragma unroll
+        for (int rt = 0; rt < NKT; ++rt) {
+          const floatx4 a4 = *(const floatx4*)&sm.Kf[16 * I + li][16 * rt + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], ds[rt][e], acc, 0, 0, 0);
+        }
+        du[I] = acc;
+      }
+      // G = T^T dU; D G is dV
+      floatx4 dy[NB];
+      float* grow = a.gw + ((size_t)h * a.nc * C + t0) * D;
+      CT* dvg = (CT*)a.dv + ((size_t)h * a.T + t0) * D;
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = z;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          const floatx4 a4 = *(const floatx4*)&sm.TT[16 * I + li][16 * kb + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], du[kb][e], acc, 0, 0, 0);
+        }
+        const floatx4 al4 = *(const floatx4*)&sm.al[16 * I + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * I + 4 * g + e;
+          grow[(size_t)r * D + col] = acc[e];
+          dy[I][e] = al4[e] * acc[e];
+          if (r < nval) dvg[(size_t)r * D + col] = from_f32<CT>(dy[I][e]);
+        }
+      }
+      // dS = dS' + Q^T dO - K^T D G
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) {
+        floatx4 acc = mm16(ds[rt], NB, [&](int kb) { return *(const floatx4*)&sm.QT[16 * rt + li][16 * kb + 4 * g]; },
+                           [&](int kb) { return *(const floatx4*)&sm.dOT[16 * w + li][16 * kb + 4 * g]; });
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+          const floatx4 a4 = *(const floatx4*)&sm.KT[16 * rt + li][16 * kb + 4 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-a4[e], dy[kb][e], acc, 0, 0, 0);
+        }
+        ds[rt] = acc;
+      }
+    }
+  }
+  if (owner && a.ds0) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ds0[((size_t)h * D + 16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 4. Per (head, chunk): dq, dk, dbeta from S, dS', G and the chunk's inputs.
+template <int D, int C>
+struct GradSmem {
+  static constexpr int LD = D + 4, LC = C + 4;
+  float YT[D][LC];  // Yh^T = (V - K S)^T
+  float Uf[C][LD];  // U = T D Yh
+  float dM[C][LC];  // lower-incl-diag(dO U^T)
+  float E[C][LC];   // strictly-lower(-G U^T)
+  float al[C], dc[C];
+};
+
+template <typename CT, int D, int C>
+__global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
+  using Sm = GradSmem<D, C>;
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  constexpr int NKT = D / 16, NB = C / 16;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
+  const int t0 = ch * C, nval = min(C, a.T - t0);
+  const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+  const size_t rb = (size_t)h * a.nc * C + t0;
+  const float* S = a.sc + ((size_t)h * a.nc + ch) * D * D;    // [v][k]
+  const float* dS = a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
+  const float* G = a.gw + rb * D;                             // [row][v]
+  const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
+  const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
+  const CT* vg = (const CT*)a.v + ((size_t)h * a.T + t0) * D;
+  const CT* dog = (const CT*)a.dout + ((size_t)h * a.T + t0) * D;
+  // four consecutive row entries of an input, zero past T
+  auto row4 = [&](const CT* base, int r, int c) -> floatx4 {
+    if (r >= nval) return floatx4{0.f, 0.f, 0.f, 0.f};
+    const CT* p = base + (size_t)r * D + c;
+    return floatx4{ld1(p), ld1(p + 1), ld1(p + 2), ld1(p + 3)};
+  };
+  // four consecutive rows of one column of an input, zero past T
+  auto col4 = [&](const CT* base, int r, int c) -> floatx4 {
+    floatx4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = r + e < nval ? ld1(base + (size_t)(r + e) * D + c) : 0.f;
+    return x;
+  };
+  if (tid < C) sm.al[tid] = a.al[rb + tid];
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  // Yh^T tiles (v, i) = V[i][v] - sum_k S[k][v] K[i][k]: A(v, k) = S[k][v],
+  // a row of the stored S^T; B(k, i) = K[i][k], a row of K
+  for (int tl = w; tl < NKT * NB; tl += 4) {
+    const int I = tl / NB, J = tl % NB;  // I: v tile, J: row tile
+    floatx4 acc = mm16(z, NKT, [&](int kb) { return -*(const floatx4*)&S[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+                       [&](int kb) { return row4(kg, 16 * J + li, 16 * kb + 4 * g); });
+    const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v] for v = 16 I + 4 g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.YT[16 * I + 4 * g + e][16 * J + li] = acc[e] + vv[e];
+  }
+  __syncthreads();
+  // U = (T D) Yh: A(i, j) = T[i][j] c_j; B(j, v) = Yh[j][v], a row of Yh^T
+  const float* Tn = a.tn + mb;
+  for (int tl = w; tl < NB * NKT; tl += 4) {
+    const int I = tl / NKT, J = tl % NKT;  // I: row tile, J: v tile
+    const floatx4 acc = mm16(z, NB,
+                             [&](int kb) {
+                               const floatx4 t4 = *(const floatx4*)&Tn[(size_t)(16 * I + li) * C + 16 * kb + 4 * g];
+                               const floatx4 c4 = *(const floatx4*)&sm.al[16 * kb + 4 * g];
+                               return t4 * c4;
+                             },
+                             [&](int kb) { return *(const floatx4*)&sm.YT[16 * J + li][16 * kb + 4 * g]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Uf[16 * I + 4 * g + e][16 * J + li] = acc[e];
+  }
+  __syncthreads();
+  // dM = lower-incl-diag(dO U^T), E = strictly-lower(-G U^T): k = v;
+  // B(v, j) = U[j][v], a row of U
+  for (int tl = w; tl < NB * NB; tl += 4) {
+    const int I = tl / NB, J = tl % NB;
+    const floatx4 m = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
+                           [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
+    const floatx4 e4 = mm16(z, NKT, [&](int kb) { return -*(const floatx4*)&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+                            [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * I + 4 * g + e, j = 16 * J + li;
+      sm.dM[i][j] = j <= i ? m[e] : 0.f;
+      sm.E[i][j] = j < i ? e4[e] : 0.f;
+    }
+  }
+  __syncthreads();
+  // dc = rowsum(G * Yh) + rowsum(E * K K^T)
+  if (tid < C) {
+    const int i = tid;
+    const float* gr = a.gram + mb + (size_t)i * C;
+    float s = 0.f;
+    for (int v = 0; v < D; ++v) s = fmaf(G[(size_t)i * D + v], sm.YT[v][i], s);
+    for (int j = 0; j < i; ++j) s = fmaf(sm.E[i][j], gr[j], s);
+    sm.dc[i] = s;
+    if (i < nval) {
+      ((CT*)a.dbeta)[(size_t)h * a.T + t0 + i] = from_f32<CT>(s * a.fb[rb + i]);
+    }
+  }
+  __syncthreads();
+  // dQ and dK tiles (row tile I, key tile J)
+  CT* dqg = (CT*)a.dq + ((size_t)h * a.T + t0) * D;
+  CT* dkg = (CT*)a.dk + ((size_t)h * a.T + t0) * D;
+  for (int tl = w; tl < NB * NKT; tl += 4) {
+    const int I = tl / NKT, J = tl % NKT;
+    const int ci = 16 * J + li;  // key dimension of this lane's column
+    // dQ = dO S^T + dM K: B(v, k) = S[k][v], four v of column k of S^T (scalar reads);
+    // B(j, k) = K[j][k], four rows of one column of K
+    floatx4 dq = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
+                      [&](int kb) {
+                        floatx4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = S[(size_t)(16 * kb + 4 * g + e) * D + ci];
+                        return x;
+                      });
+    dq = mm16(dq, NB, [&](int kb) { return *(const floatx4*)&sm.dM[16 * I + li][16 * kb + 4 * g]; },
+              [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
+    // dK = dM^T Q + U dS'^T - D G S^T + D E K + E^T D K
+    floatx4 dk = mm16(z, NB,
+                      [&](int kb) {
+                        floatx4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = sm.dM[16 * kb + 4 * g + e][16 * I + li];
+                        return x;
+                      },
+                      [&](int kb) { return col4(qg, 16 * kb + 4 * g, ci); });
+    dk = mm16(dk, NKT, [&](int kb) { return *(const floatx4*)&sm.Uf[16 * I + li][16 * kb + 4 * g]; },
+              [&](int kb) { return *(const floatx4*)&dS[(size_t)ci * D + 16 * kb + 4 * g]; });
+    {
+      const float cr = sm.al[16 * I + li];  // row scale of this lane's A row
+      dk = mm16(dk, NKT, [&](int kb) { return -cr * *(const floatx4*)&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+                [&](int kb) {
+                  floatx4 x;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[e] = S[(size_t)(16 * kb + 4 * g + e) * D + ci];
+                  return x;
+                });
+      dk = mm16(dk, NB, [&](int kb) { return cr * *(const floatx4*)&sm.E[16 * I + li][16 * kb + 4 * g]; },
+                [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
+    }
+    dk = mm16(dk, NB,
+              [&](int kb) {
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int j = 16 * kb + 4 * g + e;
+                  x[e] = sm.E[j][16 * I + li] * sm.al[j];
+                }
+                return x;
+              },
+              [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + 4 * g + e;
+      if (r < nval) {
+        const float kv = ld1(kg + (size_t)r * D + ci);
+        dqg[(size_t)r * D + ci] = from_f32<CT>(dq[e]);
+        dkg[(size_t)r * D + ci] = from_f32<CT>(dk[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename CT, int D, int C>
+static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
+  constexpr int BV = D < 64 ? D : 64;
+  hipLaunchKernelGGL((efla_bwd_prep_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
+                     stream, a);
+  hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename CT, int D>
+static hipError_t bwd_chunk(const BwdArgs& a, int NH, int chunk, hipStream_t s) {
+  switch (chunk) {
+    case 16: return launch_bwd<CT, D, 16>(a, NH, s);
+    case 32: return launch_bwd<CT, D, 32>(a, NH, s);
+    case 64: return launch_bwd<CT, D, 64>(a, NH, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename CT>
+static hipError_t bwd_d(const BwdArgs& a, int NH, int d, int chunk, hipStream_t s) {
+  switch (d) {
+    case 16: return bwd_chunk<CT, 16>(a, NH, chunk, s);
+    case 32: return bwd_chunk<CT, 32>(a, NH, chunk, s);
+    case 64: return bwd_chunk<CT, 64>(a, NH, chunk, s);
+    case 128: return bwd_chunk<CT, 128>(a, NH, chunk, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace efla
+
+hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
+                                       const float* s0, float* s_chunks, int NH, int T, int d, int chunk,
+                                       int coef, int is_bf16, hipStream_t stream);
+bool efla_internal_states_supported(int d, int chunk, int is_bf16);
+
+// Chunk size the backward runs with for a requested forward chunk.
+static int bwd_chunk_for(int d, int chunk, int is_bf16) {
+  int c = chunk;
+  if (!efla_internal_states_supported(d, c, is_bf16)) c = 32;
+  if (!efla_internal_states_supported(d, c, is_bf16)) return 0;
+  return c;
+}
+
+size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16) {
+  const int c = bwd_chunk_for(d, chunk, is_bf16);
+  if (c == 0) return 0;
+  const size_t nc = (size_t)((T + c - 1) / c), Tp = nc * c;
+  const size_t per_head = 2 * nc * d * d + Tp * d + 3 * Tp + 4 * nc * c * c;
+  return (size_t)NH * per_head * sizeof(float);
+}
+
+hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v, const void* beta,
+                                    const float* s0, const void* dout, const float* dsT, void* dq, void* dk,
+                                    void* dv, void* dbeta, float* ds0, void* workspace, int NH, int T, int d,
+                                    int chunk, int coef, int is_bf16, hipStream_t stream) {
+  const int c = bwd_chunk_for(d, chunk, is_bf16);
+  if (c == 0) return hipErrorInvalidValue;
+  const size_t nc = (size_t)((T + c - 1) / c), Tp = nc * c;
+  float* p = (float*)workspace;
+  efla::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.dout = dout;
+  a.s0 = s0;
+  a.dsT = dsT;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dbeta = dbeta;
+  a.ds0 = ds0;
+  a.T = T;
+  a.nc = (int)nc;
+  a.coef = coef;
+  float* sc = p;
+  p += (size_t)NH * nc * d * d;
+  a.sc = sc;
+  a.dsc = p;
+  p += (size_t)NH * nc * d * d;
+  a.gw = p;
+  p += (size_t)NH * Tp * d;
+  a.al = p;
+  p += (size_t)NH * Tp;
+  a.fb = p;
+  p += (size_t)NH * Tp;
+  a.fl = p;
+  p += (size_t)NH * Tp;
+  a.gram = p;
+  p += (size_t)NH * nc * c * c;
+  a.tn = p;
+  p += (size_t)NH * nc * c * c;
+  a.tt = p;
+  p += (size_t)NH * nc * c * c;
+  a.mt = p;
+  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, NH, T, d, c, coef, is_bf16, stream);
+  if (e != hipSuccess) return e;
+  return is_bf16 ? efla::bwd_d<efla::bf16>(a, NH, d, c, stream) : efla::bwd_d<float>(a, NH, d, c, stream);
+}

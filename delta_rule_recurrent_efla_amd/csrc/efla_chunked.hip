@@ -62,6 +62,9 @@ struct ChunkedArgs {
   const float* seg_s0;
   float* seg_out;
   int coef;  // step coefficient rule (gate_coef)
+  // pass mode 2 of the pipelined kernel (states for the backward): the state
+  // at the start of every chunk, [head][chunk][d_v][d_k] fp32 (transposed)
+  float* s_chunks;
 };
 
 template <typename CT>
@@ -605,7 +608,7 @@ __device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
 }
 __device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
 
-template <typename CT, int D, int C, int BV, int NSW, bool SUMMARY>
+template <typename CT, int D, int C, int BV, int NSW, int PM>
 __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
@@ -643,9 +646,13 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   const int vh = L / a.nvt;  // virtual head
   const int v0 = (L % a.nvt) * BV;
   int hd = vh, t_begin = 0, T = a.T;
-  // SUMMARY (mode 1): no outputs; odd virtual heads start from S = I with
-  // zero values. Both are compile-time off in the other modes.
-  constexpr bool outs = !SUMMARY;
+  // Pass mode PM: 0 outputs (one pass, or one segment of a time-segmented
+  // pass); 1 segment summaries: no outputs, odd virtual heads start from
+  // S = I with zero values; 2 chunk-start states for the backward, no
+  // outputs. All compile-time.
+  constexpr bool SUMMARY = PM == 1;
+  constexpr bool SAVE = PM == 2;
+  constexpr bool outs = PM == 0;
   bool ident = false;
   const float* s0p = a.s0 ? a.s0 + (size_t)hd * D * D : nullptr;
   float* sfp = a.s_final ? a.s_final + (size_t)hd * D * D : nullptr;
@@ -711,6 +718,16 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       //      requested first, the Q fragments (for phase B) while the K S
       //      products run, then the T fragments
       if (act) {
+        if constexpr (SAVE) {
+          // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 16
+          // contiguous bytes of the transposed state
+          float* dst = a.s_chunks + ((size_t)hd * nchunks + c) * D * D;
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+            for (int rt = 0; rt < NKT; ++rt)
+              *(floatx4*)&dst[(size_t)(v0 + 16 * (w * CPW + cc) + li) * D + 16 * rt + 4 * g] = sacc[cc][rt];
+        }
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
@@ -1376,7 +1393,7 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
       m1.seg_len = sp.seg_len;
       m1.nseg = sp.nseg - 1;
       m1.seg_out = seg_out;
-      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, true>),
+      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 1>),
                          dim3((unsigned)(NH * (sp.nseg - 1) * 2 * a.nvt)), dim3(64 * (NSW + 6)), 0,
                          stream, m1);
       hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0,
@@ -1386,11 +1403,11 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
       m2.seg_len = sp.seg_len;
       m2.nseg = sp.nseg;
       m2.seg_s0 = seg_s0;
-      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, false>),
+      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 0>),
                          dim3((unsigned)(NH * sp.nseg * a.nvt)), dim3(64 * (NSW + 6)), 0, stream, m2);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, false>), grid, dim3(64 * (NSW + 6)), 0,
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 0>), grid, dim3(64 * (NSW + 6)), 0,
                        stream, a);
   } else {
     static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");
@@ -1458,7 +1475,64 @@ hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void
                                         const void* beta, const float* s0, void* o,
                                         float* s_final, void* workspace, int NH, int T, int d,
                                         int chunk, int coef, int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef};
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef, nullptr};
   if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, workspace, stream);
   return efla::dispatch_d<float>(a, NH, d, chunk, workspace, stream);
+}
+
+// Pass mode 2 of the pipelined kernel: one plain pass that stores the state at
+// the start of every chunk (for the backward). Only where the pipelined kernel
+// serves the shape.
+namespace efla {
+template <typename CT, int D, int C>
+static hipError_t launch_states(const ChunkedArgs& in, int NH, hipStream_t stream) {
+  if constexpr (pipelined<CT, D, C>()) {
+    constexpr int BV = D < 64 ? D : 64;
+    constexpr int NSW = EFLA_PIPE_STATE_WAVES;
+    ChunkedArgs a = in;
+    a.nvt = D / BV;
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 2>), dim3((unsigned)(NH * a.nvt)),
+                       dim3(64 * (NSW + 6)), 0, stream, a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename CT, int D>
+static hipError_t states_chunk(const ChunkedArgs& a, int NH, int chunk, hipStream_t s) {
+  switch (chunk) {
+    case 16: return launch_states<CT, D, 16>(a, NH, s);
+    case 32: return launch_states<CT, D, 32>(a, NH, s);
+    case 64:
+      if constexpr (sizeof(CT) == 4 && D == 128) return hipErrorInvalidValue;
+      else return launch_states<CT, D, 64>(a, NH, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename CT>
+static hipError_t states_d(const ChunkedArgs& a, int NH, int d, int chunk, hipStream_t s) {
+  switch (d) {
+    case 16: return states_chunk<CT, 16>(a, NH, chunk, s);
+    case 32: return states_chunk<CT, 32>(a, NH, chunk, s);
+    case 64: return states_chunk<CT, 64>(a, NH, chunk, s);
+    case 128: return states_chunk<CT, 128>(a, NH, chunk, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace efla
+
+bool efla_internal_states_supported(int d, int chunk, int is_bf16) {
+  if (d != 16 && d != 32 && d != 64 && d != 128) return false;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return false;
+  return is_bf16 ? efla::pipelined_d<efla::bf16>(d, chunk) : efla::pipelined_d<float>(d, chunk);
+}
+
+hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
+                                       const float* s0, float* s_chunks, int NH, int T, int d, int chunk,
+                                       int coef, int is_bf16, hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, nullptr, nullptr, T, 1, 0, 0, 1, nullptr, nullptr, coef, s_chunks};
+  if (is_bf16) return efla::states_d<efla::bf16>(a, NH, d, chunk, stream);
+  return efla::states_d<float>(a, NH, d, chunk, stream);
 }

@@ -131,6 +131,46 @@ efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
                                     int d_k, int d_v, efla_coef coef, efla_dtype dt,
                                     void* stream);
 
+/*
+ * Bytes of device workspace efla_bwd_chunked needs: per head, the state at
+ * the start and the state gradient at the end of every chunk (2 nchunks d^2
+ * fp32), one d-wide fp32 row per token, three scalars per token and four
+ * C x C fp32 matrices per chunk. Never 0 for supported sizes; 0 for
+ * unsupported ones.
+ */
+size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
+                                        efla_dtype dt);
+
+/*
+ * Backward of efla_fwd_chunked: the gradients of a loss L(o, S_T) with
+ * respect to q, k, v, beta and s0, given dout = dL/do and ds_final = dL/dS_T.
+ * The pages give no gradient formulas; this is reverse mode through the
+ * forward as defined above (the chunk form of section 整体框架 of the
+ * papernotes note, with the step scalar of coef and its derivatives in beta
+ * and lambda; the exact flow's lambda floor makes its scalar constant in
+ * lambda below 1e-12).
+ *   q, k, v, beta, s0, chunk, coef, dt   exactly as passed to the forward.
+ *   dout      [B, H, T, d_v], element type dt.
+ *   ds_final  [B, H, d_k, d_v] fp32, or NULL for zero.
+ *   dq, dk    [B, H, T, d_k], dv [B, H, T, d_v], dbeta [B, H, T]: outputs,
+ *             element type dt (RNE from fp32). They must not alias inputs.
+ *   ds0       [B, H, d_k, d_v] fp32 output dL/dS0, or NULL to skip it.
+ *   workspace, workspace_bytes   caller-owned, 16-byte aligned, at least
+ *             efla_bwd_chunked_workspace_bytes() bytes (required); contents
+ *             on entry do not matter; calls sharing one must not overlap.
+ * The forward is recomputed inside (the chunk-start states go to the
+ * workspace); arithmetic is fp32 for both input types. Supported sizes are
+ * the forward's; where the forward's pipelined kernel does not serve the
+ * chunk size, the backward runs with chunk 32 (same result up to rounding).
+ * Errors as for efla_fwd_chunked; a missing or short workspace is
+ * EFLA_ERR_WORKSPACE.
+ */
+efla_status efla_bwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                             const float* s0, const void* dout, const float* ds_final, void* dq,
+                             void* dk, void* dv, void* dbeta, float* ds0, void* workspace,
+                             size_t workspace_bytes, int B, int H, int T, int d_k, int d_v, int chunk,
+                             efla_coef coef, efla_dtype dt, void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* efla_status_string(efla_status s);
 

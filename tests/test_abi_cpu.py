@@ -128,3 +128,39 @@ def test_coefficient_names_match_the_header():
         assert f"EFLA_COEF_{name.upper()} = {value}" in text
     with pytest.raises(ValueError):
         efla._coef("heun")
+
+
+
+def bwd(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, s0=None, dout=FAKE, dsT=None, dq=FAKE, dk=FAKE,
+        dv=FAKE, db=FAKE, ds0=None, ws=FAKE, wsb=1 << 40, B=1, H=1, T=8, dk_=64, dv_=64, chunk=64,
+        coef=0, dt=1):
+    return lib.efla_bwd_chunked(q, k, v, beta, s0, dout, dsT, dq, dk, dv, db, ds0, ws, wsb, B, H, T,
+                                dk_, dv_, chunk, coef, dt, None)
+
+
+def test_backward_rejects_bad_arguments_before_launch():
+    lib = efla.load_library()
+    assert bwd(lib, dout=None) == 1
+    assert bwd(lib, db=None) == 1
+    assert bwd(lib, B=0) == 2
+    assert bwd(lib, dv_=32) == 2
+    assert bwd(lib, chunk=48) == 3
+    assert bwd(lib, coef=5) == 3
+    assert bwd(lib, dq=FAKE + 4) == 4
+    assert bwd(lib, db=FAKE + 1) == 4
+    assert bwd(lib, ws=None) == 5
+    assert bwd(lib, wsb=16) == 5
+
+
+def test_backward_workspace_query():
+    lib = efla.load_library()
+    # bf16, d = 128, C = 64: per head 2 nc d^2 + Tp d + 3 Tp + 4 nc C^2 floats
+    nc, Tp = 2, 128
+    per = 2 * nc * 128 * 128 + Tp * 128 + 3 * Tp + 4 * nc * 64 * 64
+    assert lib.efla_bwd_chunked_workspace_bytes(1, 3, 100, 128, 128, 64, 1) == 3 * per * 4
+    # fp32 with C = 64 runs the backward with chunk 32
+    nc, Tp = 4, 128
+    per = 2 * nc * 64 * 64 + Tp * 64 + 3 * Tp + 4 * nc * 32 * 32
+    assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 64, 64, 64, 0) == per * 4
+    assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 128, 128, 64, 0) == 0
+    assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 48, 48, 64, 1) == 0
