@@ -188,6 +188,38 @@ def bench_other_workloads(efla, torch, efla_inputs, skip: str, steps=10, warmup=
     return out
 
 
+def alg_bytes_bwd(w) -> int:
+    """Algorithmic bytes of the backward: read q, k, v, beta, dout; write dq,
+    dk, dv, dbeta (per head-token (8d + 2) elements); read S0 and dS_T and
+    write dS0 (3 d^2 fp32 per head). The recomputed forward and the
+    workspace round trips are not counted."""
+    es = 2 if w.dtype == "bf16" else 4
+    return w.head_tokens * (8 * w.d + 2) * es + w.B * w.H * 3 * w.d * w.d * 4
+
+
+def bench_backward(efla, torch, efla_inputs, w, steps=10, warmup=3):
+    """Whole efla_bwd_chunked call (forward recompute included) on workload w."""
+    x = efla_inputs.make_inputs(w)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    gen = torch.Generator().manual_seed(4242)
+    dout = torch.randn(g["v"].shape, generator=gen).to(w.torch_dtype).cuda()
+    dsT = torch.randn((w.B, w.H, w.d, w.d), generator=gen).cuda()
+
+    def bwd():
+        efla.efla_bwd_chunked(g["q"], g["k"], g["v"], g["beta"], dout, g["s0"], dsT, chunk=w.chunk)
+
+    _, per = time_launches(bwd, steps, warmup, torch.cuda.current_stream())
+    per.sort()
+    med = per[len(per) // 2]
+    nbytes = alg_bytes_bwd(w)
+    ws = efla.efla_bwd_chunked_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.chunk, w.torch_dtype)
+    return {"workload": w.name, "ms_per_call_median": med,
+            "head_tokens_per_s": w.head_tokens / (med * 1e-3),
+            "alg_bytes": nbytes, "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "workspace_bytes": ws,
+            "note": "includes the recomputed forward; fp32 arithmetic"}
+
+
 def bench_decode(efla, torch, efla_inputs, steps=256):
     w = efla_inputs.WORKLOADS["layer340m_d128"]
     x = efla_inputs.make_inputs(w)
@@ -228,6 +260,7 @@ def main():
     ap.add_argument("--workload", default="layer1p3b_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the per-launch times of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -293,6 +326,8 @@ def main():
     }
     if not args.no_decode:
         res["decode"] = bench_decode(efla, torch, efla_inputs)
+    if not args.no_backward:
+        res["backward"] = bench_backward(efla, torch, efla_inputs, w)
     if not args.no_others:
         res["other_workloads"] = bench_other_workloads(efla, torch, efla_inputs, w.name)
     if args.copy_calibration:

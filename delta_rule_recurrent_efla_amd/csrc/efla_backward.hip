@@ -50,6 +50,9 @@ __device__ __forceinline__ floatx4 mm16(floatx4 acc, int nkb, FA fa, FB fb) {
 
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 __device__ __forceinline__ float ld1(const bf16* p) { return (float)*p; }
+// four consecutive elements (8- or 16-byte aligned)
+__device__ __forceinline__ floatx4 ld4(const float* p) { return *(const floatx4*)p; }
+__device__ __forceinline__ floatx4 ld4(const bf16* p) { return __builtin_convertvector(*(const bf16x4*)p, floatx4); }
 
 // dc/dbeta and dc/dlambda of gate_coef, in fp32.
 __device__ __forceinline__ void gate_coef_grad(int coef, float beta, float lam, float& db, float& dl) {
@@ -92,6 +95,7 @@ struct BwdArgs {
   int T, nc, coef;
   // workspace (fp32)
   const float* sc;  // [head][chunk][d_v][d_k] state at the start of each chunk
+  const float* scn; // the same states, [head][chunk][d_k][d_v]
   float* dsc;       // [head][chunk][d_k][d_v] gradient of the state at each chunk's end
   float* gw;        // [head][nc C][d_v] G rows
   float *al, *fb, *fl;        // [head][nc C] c, dc/dbeta, dc/dlambda (0 past T)
@@ -104,17 +108,20 @@ template <typename CT, int D, int C>
 __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   constexpr int LD = D + 4, LC = C + 4;
   __shared__ __attribute__((aligned(16))) float Kf[C][LD];
-  __shared__ __attribute__((aligned(16))) float Qf[C][LD];
-  __shared__ __attribute__((aligned(16))) float Am[C][LC];  // strictly-lower D K K^T
+  // Q rows, then (after the Q K^T tiles) strictly-lower D K K^T, C x LC
+  constexpr int LQ = LD > LC ? LD : LC;
+  __shared__ __attribute__((aligned(16))) float Qf[C][LQ];
+  auto Am = [&](int i, int j) -> float& { return Qf[0][i * LC + j]; };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
   const int t0 = ch * C, nval = min(C, a.T - t0);
   const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
   const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
-  for (int i = tid; i < C * D; i += 256) {
-    const int r = i / D, col = i % D;
-    Kf[r][col] = r < nval ? ld1(kg + (size_t)r * D + col) : 0.f;
-    Qf[r][col] = r < nval ? ld1(qg + (size_t)r * D + col) : 0.f;
+  for (int i = tid; i < C * D / 4; i += 256) {
+    const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
+    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+    *(floatx4*)&Kf[r][c4] = r < nval ? ld4(kg + (size_t)r * D + c4) : z4;
+    *(floatx4*)&Qf[r][c4] = r < nval ? ld4(qg + (size_t)r * D + c4) : z4;
   }
   __syncthreads();
   const size_t rb = (size_t)h * a.nc * C + t0;  // row base of this chunk
@@ -136,21 +143,29 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
   const size_t mb = ((size_t)h * a.nc + ch) * C * C;
   constexpr int NT = C / 16;
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  // Q K^T tiles (I, J): B(k, j) = K[16J + j][k], a row of K
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
-    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-    // K K^T and Q K^T tiles (I, J): B(k, j) = K[16J + j][k], a row of K
-    const floatx4 gk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Kf[16 * I + li][16 * kb + 4 * g]; },
-                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
     const floatx4 qk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Qf[16 * I + li][16 * kb + 4 * g]; },
                             [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
-      a.gram[mb + (size_t)i * C + j] = gk[e];
-      Am[i][j] = j < i ? cs[i] * gk[e] : 0.f;
       // M[i][j] = q_i . k_j for j <= i; stored transposed: M^T[j][i]
       a.mt[mb + (size_t)j * C + i] = j <= i ? qk[e] : 0.f;
+    }
+  }
+  __syncthreads();  // Q is dead: its space takes A
+  for (int tl = w; tl < NT * NT; tl += 4) {
+    const int I = tl / NT, J = tl % NT;
+    const floatx4 gk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Kf[16 * I + li][16 * kb + 4 * g]; },
+                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * I + 4 * g + e, j = 16 * J + li;
+      a.gram[mb + (size_t)i * C + j] = gk[e];
+      Am(i, j) = j < i ? cs[i] * gk[e] : 0.f;
     }
   }
   __syncthreads();
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
         float s = (i == lane) ? 1.f : 0.f;
 #pragma unroll
         for (int m4 = 0; m4 < i; m4 += 4) {
-          const floatx4 a4 = *(const floatx4*)&Am[i][m4];
+          const floatx4 a4 = *(const floatx4*)&Am(i, m4);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (m4 + e < i) s = fmaf(-a4[e], t[m4 + e], s);
@@ -220,9 +235,40 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
   const CT* kg = (const CT*)a.k + (size_t)h * a.T * D;
   const CT* qg = (const CT*)a.q + (size_t)h * a.T * D;
   const CT* dog = (const CT*)a.dout + (size_t)h * a.T * D;
-  for (int ch = a.nc - 1; ch >= 0; --ch) {
+  // The next chunk's inputs (chunks run last to first) are requested into
+  // registers while this chunk computes, then written to LDS.
+  constexpr int NLK = (C * D / 4 + 255) / 256, NLO = (C * BV / 4 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
+  floatx4 rk[NLK], rq[NLK], ro[NLO], rm[NLM], rt4[NLM];
+  float ral = 0.f;
+  auto fetch = [&](int ch) {
     const int t0 = ch * C, nval = min(C, a.T - t0);
     const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NLK; ++j) {
+      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      const bool ok = i < C * D / 4 && r < nval;
+      rk[j] = ok ? ld4(kg + (size_t)(t0 + r) * D + c4) : z4;
+      rq[j] = ok ? ld4(qg + (size_t)(t0 + r) * D + c4) : z4;
+    }
+#pragma unroll
+    for (int j = 0; j < NLO; ++j) {
+      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
+      ro[j] = (i < C * BV / 4 && r < nval) ? ld4(dog + (size_t)(t0 + r) * D + v0 + c4) : z4;
+    }
+#pragma unroll
+    for (int j = 0; j < NLM; ++j) {
+      const int i = tid + 256 * j;
+      if (i < C * C / 4) {
+        rm[j] = ld4(a.mt + mb + 4 * (size_t)i);
+        rt4[j] = ld4(a.tt + mb + 4 * (size_t)i);
+      }
+    }
+    if (tid < C) ral = a.al[(size_t)h * a.nc * C + t0 + tid];
+  };
+  fetch(a.nc - 1);
+  for (int ch = a.nc - 1; ch >= 0; --ch) {
+    const int t0 = ch * C, nval = min(C, a.T - t0);
     // dS' of this chunk (natural layout [d_k][d_v])
     if (owner) {
       float* dst = a.dsc + ((size_t)h * a.nc + ch) * D * D;
@@ -232,24 +278,38 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = ds[rt][e];
     }
     __syncthreads();  // the previous chunk's reads of LDS are done
-    for (int i = tid; i < C * D; i += 256) {
-      const int r = i / D, c = i % D;
-      const float kv = r < nval ? ld1(kg + (size_t)(t0 + r) * D + c) : 0.f;
-      const float qv = r < nval ? ld1(qg + (size_t)(t0 + r) * D + c) : 0.f;
-      sm.Kf[r][c] = kv;
-      sm.KT[c][r] = kv;
-      sm.QT[c][r] = qv;
+#pragma unroll
+    for (int j = 0; j < NLK; ++j) {
+      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      if (i < C * D / 4) {
+        *(floatx4*)&sm.Kf[r][c4] = rk[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.KT[c4 + e][r] = rk[j][e];
+          sm.QT[c4 + e][r] = rq[j][e];
+        }
+      }
     }
-    for (int i = tid; i < C * BV; i += 256) {
-      const int r = i / BV, c = i % BV;
-      sm.dOT[c][r] = r < nval ? ld1(dog + (size_t)(t0 + r) * D + v0 + c) : 0.f;
+#pragma unroll
+    for (int j = 0; j < NLO; ++j) {
+      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
+      if (i < C * BV / 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dOT[c4 + e][r] = ro[j][e];
+      }
     }
-    for (int i = tid; i < C * C; i += 256) {
-      const int r = i / C, c = i % C;
-      sm.MT[r][c] = a.mt[mb + i];
-      sm.TT[r][c] = a.tt[mb + i];
+#pragma unroll
+    for (int j = 0; j < NLM; ++j) {
+      const int i = tid + 256 * j, r = i / (C / 4), c4 = 4 * (i % (C / 4));
+      if (i < C * C / 4) {
+        *(floatx4*)&sm.MT[r][c4] = rm[j];
+        *(floatx4*)&sm.TT[r][c4] = rt4[j];
+      }
     }
-    if (tid < C) sm.al[tid] = a.al[(size_t)h * a.nc * C + t0 + tid];
+    if (tid < C) sm.al[tid] = ral;
+    // always issued (the first chunk's again at the end): a conditional load
+    // would make the compiler copy the registers at the loop latch
+    fetch(ch > 0 ? ch - 1 : 0);
     __syncthreads();
     if (owner) {
       const floatx4 z = {0.f, 0.f, 0.f, 0.f};
@@ -314,10 +374,16 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // 4. Per (head, chunk): dq, dk, dbeta from S, dS', G and the chunk's inputs.
+// Every MFMA operand is a 16-byte read: rows of K, dO, V, G and of the two
+// stored layouts of S and dS' from global memory (L2), the rest from LDS.
 template <int D, int C>
 struct GradSmem {
   static constexpr int LD = D + 4, LC = C + 4;
-  float YT[D][LC];  // Yh^T = (V - K S)^T
+  union {
+    float YT[D][LC];  // Yh^T = (V - K S)^T, until U and dc are formed
+    float KT[D][LC];  // then K^T
+  };
+  float QT[D][LC];  // Q^T
   float Uf[C][LD];  // U = T D Yh
   float dM[C][LC];  // lower-incl-diag(dO U^T)
   float E[C][LC];   // strictly-lower(-G U^T)
@@ -325,17 +391,18 @@ struct GradSmem {
 };
 
 template <typename CT, int D, int C>
-__global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   using Sm = GradSmem<D, C>;
   __shared__ __attribute__((aligned(16))) Sm sm;
-  constexpr int NKT = D / 16, NB = C / 16;
+  constexpr int NKT = D / 16, NB = C / 16, NWV = 8;  // waves
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
   const int t0 = ch * C, nval = min(C, a.T - t0);
   const size_t mb = ((size_t)h * a.nc + ch) * C * C;
   const size_t rb = (size_t)h * a.nc * C + t0;
-  const float* S = a.sc + ((size_t)h * a.nc + ch) * D * D;    // [v][k]
+  const float* St = a.sc + ((size_t)h * a.nc + ch) * D * D;   // [v][k]
+  const float* Sn = a.scn + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
   const float* dS = a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
   const float* G = a.gw + rb * D;                             // [row][v]
   const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
@@ -344,39 +411,39 @@ __global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
   const CT* dog = (const CT*)a.dout + ((size_t)h * a.T + t0) * D;
   // four consecutive row entries of an input, zero past T
   auto row4 = [&](const CT* base, int r, int c) -> floatx4 {
-    if (r >= nval) return floatx4{0.f, 0.f, 0.f, 0.f};
-    const CT* p = base + (size_t)r * D + c;
-    return floatx4{ld1(p), ld1(p + 1), ld1(p + 2), ld1(p + 3)};
+    return r < nval ? ld4(base + (size_t)r * D + c) : floatx4{0.f, 0.f, 0.f, 0.f};
   };
-  // four consecutive rows of one column of an input, zero past T
-  auto col4 = [&](const CT* base, int r, int c) -> floatx4 {
-    floatx4 x;
+  // X^T of a C x D input into LDS (zero rows past T)
+  auto stage_t = [&](float (*XT)[Sm::LC], const CT* base) {
+    for (int i = tid; i < C * D / 4; i += 64 * NWV) {
+      const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      const floatx4 x = row4(base, r, c4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = r + e < nval ? ld1(base + (size_t)(r + e) * D + c) : 0.f;
-    return x;
+      for (int e = 0; e < 4; ++e) XT[c4 + e][r] = x[e];
+    }
   };
   if (tid < C) sm.al[tid] = a.al[rb + tid];
+  stage_t(sm.QT, qg);
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  // Yh^T tiles (v, i) = V[i][v] - sum_k S[k][v] K[i][k]: A(v, k) = S[k][v],
-  // a row of the stored S^T; B(k, i) = K[i][k], a row of K
-  for (int tl = w; tl < NKT * NB; tl += 4) {
+  // Yh^T tiles (v, i) = V[i][v] - sum_k S[k][v] K[i][k]: A(v, k) = S[k][v], a
+  // row of S^T; B(k, i) = K[i][k], a row of K
+  for (int tl = w; tl < NKT * NB; tl += NWV) {
     const int I = tl / NB, J = tl % NB;  // I: v tile, J: row tile
-    floatx4 acc = mm16(z, NKT, [&](int kb) { return -*(const floatx4*)&S[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+    floatx4 acc = mm16(z, NKT, [&](int kb) { return -ld4(&St[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
                        [&](int kb) { return row4(kg, 16 * J + li, 16 * kb + 4 * g); });
-    const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v] for v = 16 I + 4 g + e
+    const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v], v = 16 I + 4 g + e
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.YT[16 * I + 4 * g + e][16 * J + li] = acc[e] + vv[e];
   }
   __syncthreads();
   // U = (T D) Yh: A(i, j) = T[i][j] c_j; B(j, v) = Yh[j][v], a row of Yh^T
   const float* Tn = a.tn + mb;
-  for (int tl = w; tl < NB * NKT; tl += 4) {
+  for (int tl = w; tl < NB * NKT; tl += NWV) {
     const int I = tl / NKT, J = tl % NKT;  // I: row tile, J: v tile
     const floatx4 acc = mm16(z, NB,
                              [&](int kb) {
-                               const floatx4 t4 = *(const floatx4*)&Tn[(size_t)(16 * I + li) * C + 16 * kb + 4 * g];
-                               const floatx4 c4 = *(const floatx4*)&sm.al[16 * kb + 4 * g];
-                               return t4 * c4;
+                               return ld4(&Tn[(size_t)(16 * I + li) * C + 16 * kb + 4 * g]) *
+                                      *(const floatx4*)&sm.al[16 * kb + 4 * g];
                              },
                              [&](int kb) { return *(const floatx4*)&sm.YT[16 * J + li][16 * kb + 4 * g]; });
 #pragma unroll
@@ -385,11 +452,11 @@ __global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   // dM = lower-incl-diag(dO U^T), E = strictly-lower(-G U^T): k = v;
   // B(v, j) = U[j][v], a row of U
-  for (int tl = w; tl < NB * NB; tl += 4) {
+  for (int tl = w; tl < NB * NB; tl += NWV) {
     const int I = tl / NB, J = tl % NB;
     const floatx4 m = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
                            [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
-    const floatx4 e4 = mm16(z, NKT, [&](int kb) { return -*(const floatx4*)&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+    const floatx4 e4 = mm16(z, NKT, [&](int kb) { return -ld4(&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
                             [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -399,36 +466,36 @@ __global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // dc = rowsum(G * Yh) + rowsum(E * K K^T)
-  if (tid < C) {
-    const int i = tid;
-    const float* gr = a.gram + mb + (size_t)i * C;
+  // dc = rowsum(G * Yh) + rowsum(E * K K^T): four lanes per row
+  {
+    const int i = tid >> 2, part = tid & 3;
     float s = 0.f;
-    for (int v = 0; v < D; ++v) s = fmaf(G[(size_t)i * D + v], sm.YT[v][i], s);
-    for (int j = 0; j < i; ++j) s = fmaf(sm.E[i][j], gr[j], s);
-    sm.dc[i] = s;
-    if (i < nval) {
-      ((CT*)a.dbeta)[(size_t)h * a.T + t0 + i] = from_f32<CT>(s * a.fb[rb + i]);
+    if (i < C) {
+      for (int v = part; v < D; v += 4) s = fmaf(G[(size_t)i * D + v], sm.YT[v][i], s);
+      const float* gr = a.gram + mb + (size_t)i * C;
+      for (int j = part; j < i; j += 4) s = fmaf(sm.E[i][j], gr[j], s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (i < C && part == 0) {
+      sm.dc[i] = s;
+      if (i < nval) ((CT*)a.dbeta)[(size_t)h * a.T + t0 + i] = from_f32<CT>(s * a.fb[rb + i]);
     }
   }
+  __syncthreads();  // Yh^T is dead: its space takes K^T
+  stage_t(sm.KT, kg);
   __syncthreads();
   // dQ and dK tiles (row tile I, key tile J)
   CT* dqg = (CT*)a.dq + ((size_t)h * a.T + t0) * D;
   CT* dkg = (CT*)a.dk + ((size_t)h * a.T + t0) * D;
-  for (int tl = w; tl < NB * NKT; tl += 4) {
+  for (int tl = w; tl < NB * NKT; tl += NWV) {
     const int I = tl / NKT, J = tl % NKT;
     const int ci = 16 * J + li;  // key dimension of this lane's column
-    // dQ = dO S^T + dM K: B(v, k) = S[k][v], four v of column k of S^T (scalar reads);
-    // B(j, k) = K[j][k], four rows of one column of K
+    // dQ = dO S^T + dM K: B(v, k) = S[k][v], a row of S; B(j, k) = K[j][k], a row of K^T
     floatx4 dq = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
-                      [&](int kb) {
-                        floatx4 x;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = S[(size_t)(16 * kb + 4 * g + e) * D + ci];
-                        return x;
-                      });
+                      [&](int kb) { return ld4(&Sn[(size_t)ci * D + 16 * kb + 4 * g]); });
     dq = mm16(dq, NB, [&](int kb) { return *(const floatx4*)&sm.dM[16 * I + li][16 * kb + 4 * g]; },
-              [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
+              [&](int kb) { return *(const floatx4*)&sm.KT[ci][16 * kb + 4 * g]; });
     // dK = dM^T Q + U dS'^T - D G S^T + D E K + E^T D K
     floatx4 dk = mm16(z, NB,
                       [&](int kb) {
@@ -437,37 +504,30 @@ __global__ __launch_bounds__(256) void efla_bwd_grad_kernel(BwdArgs a) {
                         for (int e = 0; e < 4; ++e) x[e] = sm.dM[16 * kb + 4 * g + e][16 * I + li];
                         return x;
                       },
-                      [&](int kb) { return col4(qg, 16 * kb + 4 * g, ci); });
+                      [&](int kb) { return *(const floatx4*)&sm.QT[ci][16 * kb + 4 * g]; });
     dk = mm16(dk, NKT, [&](int kb) { return *(const floatx4*)&sm.Uf[16 * I + li][16 * kb + 4 * g]; },
-              [&](int kb) { return *(const floatx4*)&dS[(size_t)ci * D + 16 * kb + 4 * g]; });
+              [&](int kb) { return ld4(&dS[(size_t)ci * D + 16 * kb + 4 * g]); });
     {
       const float cr = sm.al[16 * I + li];  // row scale of this lane's A row
-      dk = mm16(dk, NKT, [&](int kb) { return -cr * *(const floatx4*)&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]; },
+      dk = mm16(dk, NKT, [&](int kb) { return -cr * ld4(&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
+                [&](int kb) { return ld4(&Sn[(size_t)ci * D + 16 * kb + 4 * g]); });
+      dk = mm16(dk, NB,
                 [&](int kb) {
                   floatx4 x;
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) x[e] = S[(size_t)(16 * kb + 4 * g + e) * D + ci];
+                  for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * kb + 4 * g + e;
+                    x[e] = cr * sm.E[16 * I + li][j] + sm.E[j][16 * I + li] * sm.al[j];
+                  }
                   return x;
-                });
-      dk = mm16(dk, NB, [&](int kb) { return cr * *(const floatx4*)&sm.E[16 * I + li][16 * kb + 4 * g]; },
-                [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
+                },
+                [&](int kb) { return *(const floatx4*)&sm.KT[ci][16 * kb + 4 * g]; });
     }
-    dk = mm16(dk, NB,
-              [&](int kb) {
-                floatx4 x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int j = 16 * kb + 4 * g + e;
-                  x[e] = sm.E[j][16 * I + li] * sm.al[j];
-                }
-                return x;
-              },
-              [&](int kb) { return col4(kg, 16 * kb + 4 * g, ci); });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 16 * I + 4 * g + e;
       if (r < nval) {
-        const float kv = ld1(kg + (size_t)r * D + ci);
+        const float kv = sm.KT[ci][r];
         dqg[(size_t)r * D + ci] = from_f32<CT>(dq[e]);
         dkg[(size_t)r * D + ci] = from_f32<CT>(dk[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
       }
@@ -482,7 +542,7 @@ static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
   hipLaunchKernelGGL((efla_bwd_prep_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
   hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
                      stream, a);
-  hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -510,8 +570,8 @@ static hipError_t bwd_d(const BwdArgs& a, int NH, int d, int chunk, hipStream_t 
 }  // namespace efla
 
 hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
-                                       const float* s0, float* s_chunks, int NH, int T, int d, int chunk,
-                                       int coef, int is_bf16, hipStream_t stream);
+                                       const float* s0, float* s_chunks, float* s_chunks_n, int NH, int T,
+                                       int d, int chunk, int coef, int is_bf16, hipStream_t stream);
 bool efla_internal_states_supported(int d, int chunk, int is_bf16);
 
 // Chunk size the backward runs with for a requested forward chunk.
@@ -526,7 +586,7 @@ size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is
   const int c = bwd_chunk_for(d, chunk, is_bf16);
   if (c == 0) return 0;
   const size_t nc = (size_t)((T + c - 1) / c), Tp = nc * c;
-  const size_t per_head = 2 * nc * d * d + Tp * d + 3 * Tp + 4 * nc * c * c;
+  const size_t per_head = 3 * nc * d * d + Tp * d + 3 * Tp + 4 * nc * c * c;
   return (size_t)NH * per_head * sizeof(float);
 }
 
@@ -556,7 +616,10 @@ hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v,
   a.coef = coef;
   float* sc = p;
   p += (size_t)NH * nc * d * d;
+  float* scn = p;
+  p += (size_t)NH * nc * d * d;
   a.sc = sc;
+  a.scn = scn;
   a.dsc = p;
   p += (size_t)NH * nc * d * d;
   a.gw = p;
@@ -574,7 +637,7 @@ hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v,
   a.tt = p;
   p += (size_t)NH * nc * c * c;
   a.mt = p;
-  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, NH, T, d, c, coef, is_bf16, stream);
+  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, scn, NH, T, d, c, coef, is_bf16, stream);
   if (e != hipSuccess) return e;
   return is_bf16 ? efla::bwd_d<efla::bf16>(a, NH, d, c, stream) : efla::bwd_d<float>(a, NH, d, c, stream);
 }

@@ -64,7 +64,9 @@ struct ChunkedArgs {
   int coef;  // step coefficient rule (gate_coef)
   // pass mode 2 of the pipelined kernel (states for the backward): the state
   // at the start of every chunk, [head][chunk][d_v][d_k] fp32 (transposed)
+  // and [head][chunk][d_k][d_v] (natural)
   float* s_chunks;
+  float* s_chunks_n;
 };
 
 template <typename CT>
@@ -722,11 +724,16 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 16
           // contiguous bytes of the transposed state
           float* dst = a.s_chunks + ((size_t)hd * nchunks + c) * D * D;
+          float* dsn = a.s_chunks_n + ((size_t)hd * nchunks + c) * D * D;
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
-            for (int rt = 0; rt < NKT; ++rt)
-              *(floatx4*)&dst[(size_t)(v0 + 16 * (w * CPW + cc) + li) * D + 16 * rt + 4 * g] = sacc[cc][rt];
+            for (int rt = 0; rt < NKT; ++rt) {
+              const int col = v0 + 16 * (w * CPW + cc) + li;
+              *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
+            }
         }
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
@@ -1475,7 +1482,7 @@ hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void
                                         const void* beta, const float* s0, void* o,
                                         float* s_final, void* workspace, int NH, int T, int d,
                                         int chunk, int coef, int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef, nullptr};
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef, nullptr, nullptr};
   if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, workspace, stream);
   return efla::dispatch_d<float>(a, NH, d, chunk, workspace, stream);
 }
@@ -1530,9 +1537,10 @@ bool efla_internal_states_supported(int d, int chunk, int is_bf16) {
 }
 
 hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
-                                       const float* s0, float* s_chunks, int NH, int T, int d, int chunk,
-                                       int coef, int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, nullptr, nullptr, T, 1, 0, 0, 1, nullptr, nullptr, coef, s_chunks};
+                                       const float* s0, float* s_chunks, float* s_chunks_n, int NH, int T,
+                                       int d, int chunk, int coef, int is_bf16, hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, nullptr, nullptr, T, 1, 0, 0, 1, nullptr, nullptr, coef, s_chunks,
+                      s_chunks_n};
   if (is_bf16) return efla::states_d<efla::bf16>(a, NH, d, chunk, stream);
   return efla::states_d<float>(a, NH, d, chunk, stream);
 }

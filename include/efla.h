@@ -133,9 +133,9 @@ efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace efla_bwd_chunked needs: per head, the state at
- * the start and the state gradient at the end of every chunk (2 nchunks d^2
- * fp32), one d-wide fp32 row per token, three scalars per token and four
- * C x C fp32 matrices per chunk. Never 0 for supported sizes; 0 for
+ * the start of every chunk in two layouts and the state gradient at the end
+ * of every chunk (3 nchunks d^2 fp32), one d-wide fp32 row per token, three
+ * scalars per token and four C x C fp32 matrices per chunk. Never 0 for supported sizes; 0 for
  * unsupported ones.
  */
 size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,

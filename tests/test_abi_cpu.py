@@ -154,13 +154,13 @@ def test_backward_rejects_bad_arguments_before_launch():
 
 def test_backward_workspace_query():
     lib = efla.load_library()
-    # bf16, d = 128, C = 64: per head 2 nc d^2 + Tp d + 3 Tp + 4 nc C^2 floats
+    # bf16, d = 128, C = 64: per head 3 nc d^2 + Tp d + 3 Tp + 4 nc C^2 floats
     nc, Tp = 2, 128
-    per = 2 * nc * 128 * 128 + Tp * 128 + 3 * Tp + 4 * nc * 64 * 64
+    per = 3 * nc * 128 * 128 + Tp * 128 + 3 * Tp + 4 * nc * 64 * 64
     assert lib.efla_bwd_chunked_workspace_bytes(1, 3, 100, 128, 128, 64, 1) == 3 * per * 4
     # fp32 with C = 64 runs the backward with chunk 32
     nc, Tp = 4, 128
-    per = 2 * nc * 64 * 64 + Tp * 64 + 3 * Tp + 4 * nc * 32 * 32
+    per = 3 * nc * 64 * 64 + Tp * 64 + 3 * Tp + 4 * nc * 32 * 32
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 64, 64, 64, 0) == per * 4
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 128, 128, 64, 0) == 0
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 48, 48, 64, 1) == 0
