@@ -48,6 +48,37 @@ __device__ __forceinline__ floatx4 mm16(floatx4 acc, int nkb, FA fa, FB fb) {
   return acc;
 }
 
+// acc += A B over k in [0, KD) for one 16x16 tile, with the operands given
+// as fa(k0) = A(row li, k0 .. k0 + 3) and fb(k0) = B(k0 .. k0 + 3, col li).
+// BF (bf16 inputs, KD a multiple of 32): v_mfma_f32_16x16x32_bf16 with lane
+// (g, li) supplying k = 32 kb + 4 g + {0..3} and 32 kb + 16 + 4 g + {0..3}
+// (the same slots for A and B), operands rounded to bf16; otherwise the fp32
+// product of mm16.
+template <int KD, bool BF, class FA, class FB>
+__device__ __forceinline__ floatx4 mmk(floatx4 acc, FA fa, FB fb) {
+  const int g = (threadIdx.x & 63) >> 4;
+  if constexpr (BF && KD % 32 == 0) {
+#pragma unroll 2
+    for (int kb = 0; kb < KD / 32; ++kb) {
+      const int k0 = 32 * kb + 4 * g;
+      const bf16x4 a0 = __builtin_convertvector(fa(k0), bf16x4), a1 = __builtin_convertvector(fa(k0 + 16), bf16x4);
+      const bf16x4 b0 = __builtin_convertvector(fb(k0), bf16x4), b1 = __builtin_convertvector(fb(k0 + 16), bf16x4);
+      const bf16x8 a8 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 b8 = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+    }
+    return acc;
+  } else {
+    for (int kb = 0; kb < KD / 16; ++kb) {
+      const int k0 = 16 * kb + 4 * g;
+      const floatx4 a = fa(k0), b = fb(k0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+}
+
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 __device__ __forceinline__ float ld1(const bf16* p) { return (float)*p; }
 // four consecutive elements (8- or 16-byte aligned)
@@ -395,6 +426,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   using Sm = GradSmem<D, C>;
   __shared__ __attribute__((aligned(16))) Sm sm;
   constexpr int NKT = D / 16, NB = C / 16, NWV = 8;  // waves
+  constexpr bool BF = sizeof(CT) == 2;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
@@ -429,8 +461,8 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   // row of S^T; B(k, i) = K[i][k], a row of K
   for (int tl = w; tl < NKT * NB; tl += NWV) {
     const int I = tl / NB, J = tl % NB;  // I: v tile, J: row tile
-    floatx4 acc = mm16(z, NKT, [&](int kb) { return -ld4(&St[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
-                       [&](int kb) { return row4(kg, 16 * J + li, 16 * kb + 4 * g); });
+    floatx4 acc = mmk<D, BF>(z, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); },
+                       [&](int k0) { return row4(kg, 16 * J + li, k0); });
     const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v], v = 16 I + 4 g + e
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.YT[16 * I + 4 * g + e][16 * J + li] = acc[e] + vv[e];
@@ -440,12 +472,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   const float* Tn = a.tn + mb;
   for (int tl = w; tl < NB * NKT; tl += NWV) {
     const int I = tl / NKT, J = tl % NKT;  // I: row tile, J: v tile
-    const floatx4 acc = mm16(z, NB,
-                             [&](int kb) {
-                               return ld4(&Tn[(size_t)(16 * I + li) * C + 16 * kb + 4 * g]) *
-                                      *(const floatx4*)&sm.al[16 * kb + 4 * g];
+    const floatx4 acc = mmk<C, BF>(z,
+                             [&](int k0) {
+                               return ld4(&Tn[(size_t)(16 * I + li) * C + k0]) *
+                                      *(const floatx4*)&sm.al[k0];
                              },
-                             [&](int kb) { return *(const floatx4*)&sm.YT[16 * J + li][16 * kb + 4 * g]; });
+                             [&](int k0) { return *(const floatx4*)&sm.YT[16 * J + li][k0]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.Uf[16 * I + 4 * g + e][16 * J + li] = acc[e];
   }
@@ -454,10 +486,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   // B(v, j) = U[j][v], a row of U
   for (int tl = w; tl < NB * NB; tl += NWV) {
     const int I = tl / NB, J = tl % NB;
-    const floatx4 m = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
-                           [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
-    const floatx4 e4 = mm16(z, NKT, [&](int kb) { return -ld4(&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
-                            [&](int kb) { return *(const floatx4*)&sm.Uf[16 * J + li][16 * kb + 4 * g]; });
+    const floatx4 m = mmk<D, BF>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); },
+                           [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+    const floatx4 e4 = mmk<D, BF>(z, [&](int k0) { return -ld4(&G[(size_t)(16 * I + li) * D + k0]); },
+                            [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
@@ -492,36 +524,36 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
     const int I = tl / NKT, J = tl % NKT;
     const int ci = 16 * J + li;  // key dimension of this lane's column
     // dQ = dO S^T + dM K: B(v, k) = S[k][v], a row of S; B(j, k) = K[j][k], a row of K^T
-    floatx4 dq = mm16(z, NKT, [&](int kb) { return row4(dog, 16 * I + li, 16 * kb + 4 * g); },
-                      [&](int kb) { return ld4(&Sn[(size_t)ci * D + 16 * kb + 4 * g]); });
-    dq = mm16(dq, NB, [&](int kb) { return *(const floatx4*)&sm.dM[16 * I + li][16 * kb + 4 * g]; },
-              [&](int kb) { return *(const floatx4*)&sm.KT[ci][16 * kb + 4 * g]; });
+    floatx4 dq = mmk<D, BF>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); },
+                      [&](int k0) { return ld4(&Sn[(size_t)ci * D + k0]); });
+    dq = mmk<C, BF>(dq, [&](int k0) { return *(const floatx4*)&sm.dM[16 * I + li][k0]; },
+              [&](int k0) { return *(const floatx4*)&sm.KT[ci][k0]; });
     // dK = dM^T Q + U dS'^T - D G S^T + D E K + E^T D K
-    floatx4 dk = mm16(z, NB,
-                      [&](int kb) {
+    floatx4 dk = mmk<C, BF>(z,
+                      [&](int k0) {
                         floatx4 x;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = sm.dM[16 * kb + 4 * g + e][16 * I + li];
+                        for (int e = 0; e < 4; ++e) x[e] = sm.dM[k0 + e][16 * I + li];
                         return x;
                       },
-                      [&](int kb) { return *(const floatx4*)&sm.QT[ci][16 * kb + 4 * g]; });
-    dk = mm16(dk, NKT, [&](int kb) { return *(const floatx4*)&sm.Uf[16 * I + li][16 * kb + 4 * g]; },
-              [&](int kb) { return ld4(&dS[(size_t)ci * D + 16 * kb + 4 * g]); });
+                      [&](int k0) { return *(const floatx4*)&sm.QT[ci][k0]; });
+    dk = mmk<D, BF>(dk, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * I + li][k0]; },
+              [&](int k0) { return ld4(&dS[(size_t)ci * D + k0]); });
     {
       const float cr = sm.al[16 * I + li];  // row scale of this lane's A row
-      dk = mm16(dk, NKT, [&](int kb) { return -cr * ld4(&G[(size_t)(16 * I + li) * D + 16 * kb + 4 * g]); },
-                [&](int kb) { return ld4(&Sn[(size_t)ci * D + 16 * kb + 4 * g]); });
-      dk = mm16(dk, NB,
-                [&](int kb) {
+      dk = mmk<D, BF>(dk, [&](int k0) { return -cr * ld4(&G[(size_t)(16 * I + li) * D + k0]); },
+                [&](int k0) { return ld4(&Sn[(size_t)ci * D + k0]); });
+      dk = mmk<C, BF>(dk,
+                [&](int k0) {
                   floatx4 x;
 #pragma unroll
                   for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * kb + 4 * g + e;
+                    const int j = k0 + e;
                     x[e] = cr * sm.E[16 * I + li][j] + sm.E[j][16 * I + li] * sm.al[j];
                   }
                   return x;
                 },
-                [&](int kb) { return *(const floatx4*)&sm.KT[ci][16 * kb + 4 * g]; });
+                [&](int k0) { return *(const floatx4*)&sm.KT[ci][k0]; });
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
