@@ -403,6 +403,187 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
   }
 }
 
+// bf16 form of the same pass (bf16 inputs, C and d multiples of 32): the
+// chunk's operands sit in LDS as bf16 and every product is
+// v_mfma_f32_16x16x32_bf16. Lane (g, li) supplies k = 32 kb + 4 g + {0..3}
+// and 32 kb + 16 + 4 g + {0..3}: for an operand held in accumulators these
+// are rows 4 g + e of tiles 2 kb and 2 kb + 1, so dS', dU and D G feed the
+// next product without lane exchange. T and M are rounded to bf16, as in the
+// forward; accumulation and the dS state stay fp32.
+template <int D, int C, int BV>
+struct StateSmemBf {
+  static constexpr int LD = D + 8, LC = C + 8;
+  bf16 Kf[C][LD];
+  bf16 KT[D][LC];
+  bf16 QT[D][LC];
+  bf16 MT[C][LC];
+  bf16 TT[C][LC];
+  bf16 dOT[BV][LC];
+  float al[C];
+};
+
+__device__ __forceinline__ bf16x8 pk8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 cv4(floatx4 x) { return __builtin_convertvector(x, bf16x4); }
+
+template <int D, int C, int BV>
+__global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
+  using Sm = StateSmemBf<D, C, BV>;
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  constexpr int NKT = D / 16, NB = C / 16, NW = BV / 16;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nvt = D / BV;
+  const int h = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * BV;
+  const int col = v0 + 16 * w + li;
+  const bool owner = w < NW;
+  floatx4 ds[NKT];
+#pragma unroll
+  for (int rt = 0; rt < NKT; ++rt) ds[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (owner && a.dsT) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[rt][e] = a.dsT[((size_t)h * D + 16 * rt + 4 * g + e) * D + col];
+  }
+  const bf16* kg = (const bf16*)a.k + (size_t)h * a.T * D;
+  const bf16* qg = (const bf16*)a.q + (size_t)h * a.T * D;
+  const bf16* dog = (const bf16*)a.dout + (size_t)h * a.T * D;
+  constexpr int NLK = (C * D / 4 + 255) / 256, NLO = (C * BV / 4 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
+  bf16x4 rk[NLK], rq[NLK], ro[NLO];
+  floatx4 rm[NLM], rt4[NLM];
+  float ral = 0.f;
+  auto fetch = [&](int ch) {
+    const int t0 = ch * C, nval = min(C, a.T - t0);
+    const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+    const bf16x4 z4 = {};
+#pragma unroll
+    for (int j = 0; j < NLK; ++j) {
+      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      const bool ok = i < C * D / 4 && r < nval;
+      rk[j] = ok ? *(const bf16x4*)(kg + (size_t)(t0 + r) * D + c4) : z4;
+      rq[j] = ok ? *(const bf16x4*)(qg + (size_t)(t0 + r) * D + c4) : z4;
+    }
+#pragma unroll
+    for (int j = 0; j < NLO; ++j) {
+      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
+      ro[j] = (i < C * BV / 4 && r < nval) ? *(const bf16x4*)(dog + (size_t)(t0 + r) * D + v0 + c4) : z4;
+    }
+#pragma unroll
+    for (int j = 0; j < NLM; ++j) {
+      const int i = tid + 256 * j;
+      if (i < C * C / 4) {
+        rm[j] = ld4(a.mt + mb + 4 * (size_t)i);
+        rt4[j] = ld4(a.tt + mb + 4 * (size_t)i);
+      }
+    }
+    if (tid < C) ral = a.al[(size_t)h * a.nc * C + t0 + tid];
+  };
+  auto ld_a = [&](const bf16* row, int kb) {  // A(row, 32 kb + 4 g + ..) and (.. + 16)
+    return pk8(*(const bf16x4*)(row + 32 * kb + 4 * g), *(const bf16x4*)(row + 32 * kb + 16 + 4 * g));
+  };
+  fetch(a.nc - 1);
+  for (int ch = a.nc - 1; ch >= 0; --ch) {
+    const int t0 = ch * C, nval = min(C, a.T - t0);
+    if (owner) {
+      float* dst = a.dsc + ((size_t)h * a.nc + ch) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NLK; ++j) {
+      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      if (i < C * D / 4) {
+        *(bf16x4*)&sm.Kf[r][c4] = rk[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.KT[c4 + e][r] = rk[j][e];
+          sm.QT[c4 + e][r] = rq[j][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NLO; ++j) {
+      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
+      if (i < C * BV / 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dOT[c4 + e][r] = ro[j][e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NLM; ++j) {
+      const int i = tid + 256 * j, r = i / (C / 4), c4 = 4 * (i % (C / 4));
+      if (i < C * C / 4) {
+        *(bf16x4*)&sm.MT[r][c4] = cv4(rm[j]);
+        *(bf16x4*)&sm.TT[r][c4] = cv4(rt4[j]);
+      }
+    }
+    if (tid < C) sm.al[tid] = ral;
+    fetch(ch > 0 ? ch - 1 : 0);  // always issued (see the fp32 form)
+    __syncthreads();
+    if (owner) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      const bf16* dorow = &sm.dOT[16 * w + li][0];
+      // dU = M^T dO + K dS'
+      floatx4 du[NB];
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = z;
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.MT[16 * I + li][0], kb), ld_a(dorow, kb), acc, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKT / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.Kf[16 * I + li][0], kb),
+                                                        pk8(cv4(ds[2 * kb]), cv4(ds[2 * kb + 1])), acc, 0, 0, 0);
+        du[I] = acc;
+      }
+      // G = T^T dU; D G is dV
+      floatx4 dy[NB];
+      float* grow = a.gw + ((size_t)h * a.nc * C + t0) * D;
+      bf16* dvg = (bf16*)a.dv + ((size_t)h * a.T + t0) * D;
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = z;
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.TT[16 * I + li][0], kb),
+                                                        pk8(cv4(du[2 * kb]), cv4(du[2 * kb + 1])), acc, 0, 0, 0);
+        const floatx4 al4 = *(const floatx4*)&sm.al[16 * I + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * I + 4 * g + e;
+          grow[(size_t)r * D + col] = acc[e];
+          dy[I][e] = al4[e] * acc[e];
+          if (r < nval) dvg[(size_t)r * D + col] = (bf16)dy[I][e];
+        }
+      }
+      // dS = dS' + Q^T dO - K^T D G
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) {
+        floatx4 acc = ds[rt];
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.QT[16 * rt + li][0], kb), ld_a(dorow, kb), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.KT[16 * rt + li][0], kb),
+                                                        pk8(cv4(-dy[2 * kb]), cv4(-dy[2 * kb + 1])), acc, 0, 0, 0);
+        }
+        ds[rt] = acc;
+      }
+    }
+  }
+  if (owner && a.ds0) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ds0[((size_t)h * D + 16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 4. Per (head, chunk): dq, dk, dbeta from S, dS', G and the chunk's inputs.
 // Every MFMA operand is a 16-byte read: rows of K, dO, V, G and of the two
@@ -572,8 +753,13 @@ template <typename CT, int D, int C>
 static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
   constexpr int BV = D < 64 ? D : 64;
   hipLaunchKernelGGL((efla_bwd_prep_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
-                     stream, a);
+  if constexpr (sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0) {
+    hipLaunchKernelGGL((efla_bwd_state_kernel_bf<D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
+                       stream, a);
+  }
   hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
