@@ -79,6 +79,37 @@ __device__ __forceinline__ floatx4 mmk(floatx4 acc, FA fa, FB fb) {
   }
 }
 
+// bf16 operand fragments of mmk's layout for all KD / 32 blocks, formed once
+// and reused across tiles: out[kb] holds f(32 kb + 4 g .. + 3) and
+// f(32 kb + 16 + 4 g .. + 3).
+template <int KD, class F>
+__device__ __forceinline__ void bf_frags(bf16x8* out, F f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int kb = 0; kb < KD / 32; ++kb) {
+    const bf16x4 x0 = __builtin_convertvector(f(32 * kb + 4 * g), bf16x4);
+    const bf16x4 x1 = __builtin_convertvector(f(32 * kb + 16 + 4 * g), bf16x4);
+    out[kb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+// acc += A B with B (fb == nullptr: A) given as precomputed fragments
+template <int KD, class FA>
+__device__ __forceinline__ floatx4 mm_fb(floatx4 acc, FA fa, const bf16x8* bfr) {
+  bf16x8 afr[KD / 32];
+  bf_frags<KD>(afr, fa);
+#pragma unroll
+  for (int kb = 0; kb < KD / 32; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[kb], bfr[kb], acc, 0, 0, 0);
+  return acc;
+}
+template <int KD, class FB>
+__device__ __forceinline__ floatx4 mm_fa(floatx4 acc, const bf16x8* afr, FB fb) {
+  bf16x8 bfr[KD / 32];
+  bf_frags<KD>(bfr, fb);
+#pragma unroll
+  for (int kb = 0; kb < KD / 32; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[kb], bfr[kb], acc, 0, 0, 0);
+  return acc;
+}
+
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 __device__ __forceinline__ float ld1(const bf16* p) { return (float)*p; }
 // four consecutive elements (8- or 16-byte aligned)
@@ -640,10 +671,20 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   // Yh^T tiles (v, i) = V[i][v] - sum_k S[k][v] K[i][k]: A(v, k) = S[k][v], a
   // row of S^T; B(k, i) = K[i][k], a row of K
+  // with bf16 products each wave keeps one v tile I (NWV is a multiple of
+  // NKT) and forms its S^T fragments once
+  constexpr bool BFK = BF && D % 32 == 0 && C % 32 == 0;
+  bf16x8 stf[BFK ? D / 32 : 1];
+  if constexpr (BFK) bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * (w % NKT) + li) * D + k0]); });
   for (int tl = w; tl < NKT * NB; tl += NWV) {
-    const int I = tl / NB, J = tl % NB;  // I: v tile, J: row tile
-    floatx4 acc = mmk<D, BF>(z, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); },
+    const int I = tl % NKT, J = tl / NKT;  // I: v tile, J: row tile
+    floatx4 acc;
+    if constexpr (BFK) {
+      acc = mm_fa<D>(z, stf, [&](int k0) { return row4(kg, 16 * J + li, k0); });
+    } else {
+      acc = mmk<D, BF>(z, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); },
                        [&](int k0) { return row4(kg, 16 * J + li, k0); });
+    }
     const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v], v = 16 I + 4 g + e
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.YT[16 * I + 4 * g + e][16 * J + li] = acc[e] + vv[e];
@@ -701,9 +742,55 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   // dQ and dK tiles (row tile I, key tile J)
   CT* dqg = (CT*)a.dq + ((size_t)h * a.T + t0) * D;
   CT* dkg = (CT*)a.dk + ((size_t)h * a.T + t0) * D;
+  // with bf16 products each wave keeps one key tile J and forms the
+  // fragments of its rows of S, dS', K^T and Q^T once
+  bf16x8 snf[BFK ? D / 32 : 1], dsf[BFK ? D / 32 : 1], ktf[BFK ? C / 32 : 1], qtf[BFK ? C / 32 : 1];
+  if constexpr (BFK) {
+    const int cj = 16 * (w % NKT) + li;
+    bf_frags<D>(snf, [&](int k0) { return ld4(&Sn[(size_t)cj * D + k0]); });
+    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+    bf_frags<C>(ktf, [&](int k0) { return *(const floatx4*)&sm.KT[cj][k0]; });
+    bf_frags<C>(qtf, [&](int k0) { return *(const floatx4*)&sm.QT[cj][k0]; });
+  }
   for (int tl = w; tl < NB * NKT; tl += NWV) {
-    const int I = tl / NKT, J = tl % NKT;
+    const int J = tl % NKT, I = tl / NKT;
     const int ci = 16 * J + li;  // key dimension of this lane's column
+    if constexpr (BFK) {
+      const float cr = sm.al[16 * I + li];
+      floatx4 dq = mm_fb<D>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); }, snf);
+      dq = mm_fb<C>(dq, [&](int k0) { return *(const floatx4*)&sm.dM[16 * I + li][k0]; }, ktf);
+      floatx4 dk = mm_fb<C>(z,
+                            [&](int k0) {
+                              floatx4 x;
+#pragma unroll
+                              for (int e = 0; e < 4; ++e) x[e] = sm.dM[k0 + e][16 * I + li];
+                              return x;
+                            },
+                            qtf);
+      dk = mm_fb<D>(dk, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * I + li][k0]; }, dsf);
+      dk = mm_fb<D>(dk, [&](int k0) { return -cr * ld4(&G[(size_t)(16 * I + li) * D + k0]); }, snf);
+      dk = mm_fb<C>(dk,
+                    [&](int k0) {
+                      floatx4 x;
+#pragma unroll
+                      for (int e = 0; e < 4; ++e) {
+                        const int j = k0 + e;
+                        x[e] = cr * sm.E[16 * I + li][j] + sm.E[j][16 * I + li] * sm.al[j];
+                      }
+                      return x;
+                    },
+                    ktf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + 4 * g + e;
+        if (r < nval) {
+          const float kv = sm.KT[ci][r];
+          dqg[(size_t)r * D + ci] = from_f32<CT>(dq[e]);
+          dkg[(size_t)r * D + ci] = from_f32<CT>(dk[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
+        }
+      }
+      continue;
+    }
     // dQ = dO S^T + dM K: B(v, k) = S[k][v], a row of S; B(j, k) = K[j][k], a row of K^T
     floatx4 dq = mmk<D, BF>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); },
                       [&](int k0) { return ld4(&Sn[(size_t)ci * D + k0]); });
