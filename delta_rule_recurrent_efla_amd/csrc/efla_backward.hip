@@ -169,11 +169,13 @@ struct BwdArgs {
 template <typename CT, int D, int C>
 __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   constexpr int LD = D + 4, LC = C + 4;
-  __shared__ __attribute__((aligned(16))) float Kf[C][LD];
-  // Q rows, then (after the Q K^T tiles) strictly-lower D K K^T, C x LC
   constexpr int LQ = LD > LC ? LD : LC;
+  // K rows, then (after the Gram tiles) T, C x LC
+  __shared__ __attribute__((aligned(16))) float Kf[C][LQ];
+  // Q rows, then (after the Q K^T tiles) strictly-lower D K K^T, C x LC
   __shared__ __attribute__((aligned(16))) float Qf[C][LQ];
   auto Am = [&](int i, int j) -> float& { return Qf[0][i * LC + j]; };
+  auto Ts = [&](int i, int j) -> float& { return Kf[0][i * LC + j]; };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
   const int t0 = ch * C, nval = min(C, a.T - t0);
@@ -209,8 +211,10 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   // Q K^T tiles (I, J): B(k, j) = K[16J + j][k], a row of K
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
-    const floatx4 qk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Qf[16 * I + li][16 * kb + 4 * g]; },
-                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
+    // bf16 inputs: products of bf16 values are exact in fp32, so the bf16 MFMA
+    // gives the same K K^T and Q K^T as the fp32 one
+    const floatx4 qk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Qf[16 * I + li][k0]; },
+                                               [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
@@ -221,8 +225,8 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   __syncthreads();  // Q is dead: its space takes A
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
-    const floatx4 gk = mm16(z, D / 16, [&](int kb) { return *(const floatx4*)&Kf[16 * I + li][16 * kb + 4 * g]; },
-                            [&](int kb) { return *(const floatx4*)&Kf[16 * J + li][16 * kb + 4 * g]; });
+    const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Kf[16 * I + li][k0]; },
+                                               [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
@@ -230,31 +234,60 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
       Am(i, j) = j < i ? cs[i] * gk[e] : 0.f;
     }
   }
-  __syncthreads();
-  if (w == 0) {
-    // column lane of T = (I + A)^{-1} by forward substitution: row i of
-    // (I + A) t = e_lane gives t_i = [i == lane] - sum_{m<i} A[i][m] t_m
-    if (lane < C) {
-      float t[C];
+  __syncthreads();  // K is dead: its space takes T
+  // T = (I + A)^{-1} by blocks. Diagonal blocks: lane (b, c) solves column c
+  // of (I + A_bb) t = e_c by forward substitution in fp32 (all blocks at once)
+  if (w == 0 && lane < C) {
+    const int bb = lane >> 4, c = lane & 15;
+    float t[16];
 #pragma unroll
-      for (int i = 0; i < C; ++i) {
-        float s = (i == lane) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float sum = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int m4 = 0; m4 < i; m4 += 4) {
-          const floatx4 a4 = *(const floatx4*)&Am(i, m4);
+      for (int m4 = 0; m4 < r; m4 += 4) {
+        const floatx4 a4 = *(const floatx4*)&Am(16 * bb + r, 16 * bb + m4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (m4 + e < i) s = fmaf(-a4[e], t[m4 + e], s);
-        }
-        t[i] = s;
+        for (int e = 0; e < 4; ++e)
+          if (m4 + e < r) sum = fmaf(-a4[e], t[m4 + e], sum);
       }
-      // lane holds column `lane` of T: row `lane` of T^T, and T[i][lane]
-#pragma unroll
-      for (int i4 = 0; i4 < C; i4 += 4)
-        *(floatx4*)&a.tt[mb + (size_t)lane * C + i4] = floatx4{t[i4], t[i4 + 1], t[i4 + 2], t[i4 + 3]};
-#pragma unroll
-      for (int i = 0; i < C; ++i) a.tn[mb + (size_t)i * C + lane] = t[i];
+      t[r] = sum;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ts(16 * bb + r, 16 * bb + c) = t[r];
+  }
+  // blocks above the diagonal are zero
+  for (int i = tid; i < C * C; i += 256)
+    if ((i % C) / 16 > (i / C) / 16) Ts(i / C, i % C) = 0.f;
+  __syncthreads();
+  // block rows below: T_ij = -T_ii sum_{j <= m < i} A_im T_mj, on fp32 MFMA;
+  // block row i needs the rows above it (one barrier per block row)
+  for (int i = 1; i < NT; ++i) {
+    const int j = w;  // block column of this wave
+    if (j < i) {
+      floatx4 p = z;
+      for (int k0 = 16 * j + 4 * g; k0 < 16 * i; k0 += 16) {
+        const floatx4 a4 = *(const floatx4*)&Am(16 * i + li, k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[e], Ts(k0 + e, 16 * j + li), p, 0, 0, 0);
+      }
+      // -T_ii P: B from the accumulator (rows 4 g + e of P)
+      const floatx4 t4 = *(const floatx4*)&Ts(16 * i + li, 16 * i + 4 * g);
+      floatx4 x = z;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x = __builtin_amdgcn_mfma_f32_16x16x4f32(-t4[e], p[e], x, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ts(16 * i + 4 * g + e, 16 * j + li) = x[e];
+    }
+    __syncthreads();
+  }
+  // T and T^T to the workspace
+  for (int i = tid; i < C * C / 4; i += 256) {
+    const int r = i / (C / 4), c4 = 4 * (i % (C / 4));
+    *(floatx4*)&a.tn[mb + (size_t)r * C + c4] = *(const floatx4*)&Ts(r, c4);
+    floatx4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = Ts(c4 + e, r);
+    *(floatx4*)&a.tt[mb + (size_t)r * C + c4] = x;
   }
 }
 
@@ -747,7 +780,14 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   bf16x8 snf[BFK ? D / 32 : 1], dsf[BFK ? D / 32 : 1], ktf[BFK ? C / 32 : 1], qtf[BFK ? C / 32 : 1];
   if constexpr (BFK) {
     const int cj = 16 * (w % NKT) + li;
-    bf_frags<D>(snf, [&](int k0) { return ld4(&Sn[(size_t)cj * D + k0]); });
+    // row cj of S from the transposed copy (once per wave: the natural copy is
+    // not written for this form)
+    bf_frags<D>(snf, [&](int k0) {
+      floatx4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = St[(size_t)(k0 + e) * D + cj];
+      return x;
+    });
     bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
     bf_frags<C>(ktf, [&](int k0) { return *(const floatx4*)&sm.KT[cj][k0]; });
     bf_frags<C>(qtf, [&](int k0) { return *(const floatx4*)&sm.QT[cj][k0]; });
@@ -942,7 +982,11 @@ hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v,
   a.tt = p;
   p += (size_t)NH * nc * c * c;
   a.mt = p;
-  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, scn, NH, T, d, c, coef, is_bf16, stream);
+  // the bf16 form of the gradient kernel (C and d multiples of 32) reads the
+  // transposed states only
+  const bool need_n = !(is_bf16 && c % 32 == 0 && d % 32 == 0);
+  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, need_n ? scn : nullptr, NH, T, d, c, coef,
+                                             is_bf16, stream);
   if (e != hipSuccess) return e;
   return is_bf16 ? efla::bwd_d<efla::bf16>(a, NH, d, c, stream) : efla::bwd_d<float>(a, NH, d, c, stream);
 }

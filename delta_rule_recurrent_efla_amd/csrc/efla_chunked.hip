@@ -64,7 +64,7 @@ struct ChunkedArgs {
   int coef;  // step coefficient rule (gate_coef)
   // pass mode 2 of the pipelined kernel (states for the backward): the state
   // at the start of every chunk, [head][chunk][d_v][d_k] fp32 (transposed)
-  // and [head][chunk][d_k][d_v] (natural)
+  // and, when s_chunks_n is not null, [head][chunk][d_k][d_v] (natural)
   float* s_chunks;
   float* s_chunks_n;
 };
@@ -731,8 +731,10 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (w * CPW + cc) + li;
               *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
+              if (a.s_chunks_n) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
+                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
+              }
             }
         }
 #pragma unroll
