@@ -739,12 +739,25 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   // dM = lower-incl-diag(dO U^T), E = strictly-lower(-G U^T): k = v;
   // B(v, j) = U[j][v], a row of U
+  // with bf16 products each wave keeps one row tile I and forms its dO and G
+  // fragments once
+  bf16x8 dof[BFK ? D / 32 : 1], gf[BFK ? D / 32 : 1];
+  if constexpr (BFK) {
+    bf_frags<D>(dof, [&](int k0) { return row4(dog, 16 * (w % NB) + li, k0); });
+    bf_frags<D>(gf, [&](int k0) { return -ld4(&G[(size_t)(16 * (w % NB) + li) * D + k0]); });
+  }
   for (int tl = w; tl < NB * NB; tl += NWV) {
-    const int I = tl / NB, J = tl % NB;
-    const floatx4 m = mmk<D, BF>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); },
-                           [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
-    const floatx4 e4 = mmk<D, BF>(z, [&](int k0) { return -ld4(&G[(size_t)(16 * I + li) * D + k0]); },
-                            [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+    const int I = tl % NB, J = tl / NB;
+    floatx4 m, e4;
+    if constexpr (BFK) {
+      m = mm_fa<D>(z, dof, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+      e4 = mm_fa<D>(z, gf, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+    } else {
+      m = mmk<D, BF>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); },
+                     [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+      e4 = mmk<D, BF>(z, [&](int k0) { return -ld4(&G[(size_t)(16 * I + li) * D + k0]); },
+                      [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
@@ -792,12 +805,31 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
     bf_frags<C>(ktf, [&](int k0) { return *(const floatx4*)&sm.KT[cj][k0]; });
     bf_frags<C>(qtf, [&](int k0) { return *(const floatx4*)&sm.QT[cj][k0]; });
   }
+  // K^T and Q^T now live in registers: their LDS takes the rows of dO and G
+  // (when C x (d + 4) fits in d x (C + 4), i.e. d >= C)
+  constexpr bool STAGE = BFK && D >= C;
+  float(*dOs)[D + 4] = reinterpret_cast<float(*)[D + 4]>(&sm.KT[0][0]);
+  float(*Gs)[D + 4] = reinterpret_cast<float(*)[D + 4]>(&sm.QT[0][0]);
+  if constexpr (STAGE) {
+    __syncthreads();
+    for (int i = tid; i < C * D / 4; i += 64 * NWV) {
+      const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      *(floatx4*)&dOs[r][c4] = row4(dog, r, c4);
+      *(floatx4*)&Gs[r][c4] = ld4(&G[(size_t)r * D + c4]);
+    }
+    __syncthreads();
+  }
   for (int tl = w; tl < NB * NKT; tl += NWV) {
     const int J = tl % NKT, I = tl / NKT;
     const int ci = 16 * J + li;  // key dimension of this lane's column
     if constexpr (BFK) {
       const float cr = sm.al[16 * I + li];
-      floatx4 dq = mm_fb<D>(z, [&](int k0) { return row4(dog, 16 * I + li, k0); }, snf);
+      floatx4 dq = mm_fb<D>(z,
+                            [&](int k0) {
+                              if constexpr (STAGE) return *(const floatx4*)&dOs[16 * I + li][k0];
+                              else return row4(dog, 16 * I + li, k0);
+                            },
+                            snf);
       dq = mm_fb<C>(dq, [&](int k0) { return *(const floatx4*)&sm.dM[16 * I + li][k0]; }, ktf);
       floatx4 dk = mm_fb<C>(z,
                             [&](int k0) {
@@ -808,7 +840,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
                             },
                             qtf);
       dk = mm_fb<D>(dk, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * I + li][k0]; }, dsf);
-      dk = mm_fb<D>(dk, [&](int k0) { return -cr * ld4(&G[(size_t)(16 * I + li) * D + k0]); }, snf);
+      dk = mm_fb<D>(dk,
+                    [&](int k0) {
+                      if constexpr (STAGE) return -cr * *(const floatx4*)&Gs[16 * I + li][k0];
+                      else return -cr * ld4(&G[(size_t)(16 * I + li) * D + k0]);
+                    },
+                    snf);
       dk = mm_fb<C>(dk,
                     [&](int k0) {
                       floatx4 x;
@@ -824,7 +861,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * I + 4 * g + e;
         if (r < nval) {
-          const float kv = sm.KT[ci][r];
+          const float kv = STAGE ? ld1(kg + (size_t)r * D + ci) : sm.KT[ci][r];
           dqg[(size_t)r * D + ci] = from_f32<CT>(dq[e]);
           dkg[(size_t)r * D + ci] = from_f32<CT>(dk[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
         }
