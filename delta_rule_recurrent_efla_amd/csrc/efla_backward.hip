@@ -701,6 +701,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   };
   if (tid < C) sm.al[tid] = a.al[rb + tid];
   stage_t(sm.QT, qg);
+  // K rows in the space U takes later (read by every Yh tile)
+  for (int i = tid; i < C * D / 4; i += 64 * NWV) {
+    const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
+    *(floatx4*)&sm.Uf[r][c4] = row4(kg, r, c4);
+  }
+  __syncthreads();
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   // Yh^T tiles (v, i) = V[i][v] - sum_k S[k][v] K[i][k]: A(v, k) = S[k][v], a
   // row of S^T; B(k, i) = K[i][k], a row of K
@@ -713,10 +719,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
     const int I = tl % NKT, J = tl / NKT;  // I: v tile, J: row tile
     floatx4 acc;
     if constexpr (BFK) {
-      acc = mm_fa<D>(z, stf, [&](int k0) { return row4(kg, 16 * J + li, k0); });
+      acc = mm_fa<D>(z, stf, [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
     } else {
       acc = mmk<D, BF>(z, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); },
-                       [&](int k0) { return row4(kg, 16 * J + li, k0); });
+                       [&](int k0) { return *(const floatx4*)&sm.Uf[16 * J + li][k0]; });
     }
     const floatx4 vv = row4(vg, 16 * J + li, 16 * I + 4 * g);  // V[row][v], v = 16 I + 4 g + e
 #pragma unroll
@@ -725,14 +731,25 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   // U = (T D) Yh: A(i, j) = T[i][j] c_j; B(j, v) = Yh[j][v], a row of Yh^T
   const float* Tn = a.tn + mb;
+  // with bf16 products each wave keeps one row tile I (NWV is a multiple of
+  // NB) and forms its T D fragments once
+  bf16x8 tdf[BFK ? C / 32 : 1];
+  if constexpr (BFK)
+    bf_frags<C>(tdf, [&](int k0) {
+      return ld4(&Tn[(size_t)(16 * (w % NB) + li) * C + k0]) * *(const floatx4*)&sm.al[k0];
+    });
   for (int tl = w; tl < NB * NKT; tl += NWV) {
-    const int I = tl / NKT, J = tl % NKT;  // I: row tile, J: v tile
-    const floatx4 acc = mmk<C, BF>(z,
-                             [&](int k0) {
-                               return ld4(&Tn[(size_t)(16 * I + li) * C + k0]) *
-                                      *(const floatx4*)&sm.al[k0];
-                             },
-                             [&](int k0) { return *(const floatx4*)&sm.YT[16 * J + li][k0]; });
+    const int I = tl % NB, J = tl / NB;  // I: row tile, J: v tile
+    floatx4 acc;
+    if constexpr (BFK) {
+      acc = mm_fa<C>(z, tdf, [&](int k0) { return *(const floatx4*)&sm.YT[16 * J + li][k0]; });
+    } else {
+      acc = mmk<C, BF>(z,
+                       [&](int k0) {
+                         return ld4(&Tn[(size_t)(16 * I + li) * C + k0]) * *(const floatx4*)&sm.al[k0];
+                       },
+                       [&](int k0) { return *(const floatx4*)&sm.YT[16 * J + li][k0]; });
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) sm.Uf[16 * I + 4 * g + e][16 * J + li] = acc[e];
   }
