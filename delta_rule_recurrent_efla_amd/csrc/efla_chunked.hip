@@ -742,7 +742,11 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
         Frag kf[NB][NFK];
-        floatx4 al[NB], vv[CPW][NB], y[CPW][NB];
+        floatx4 al[NB], y[CPW][NB];
+        // the value columns stay in their storage type until Y: converting
+        // them here would make the wave wait for every read before the first
+        // product (a transition run ignores them: its value buffer holds keys)
+        std::conditional_t<sizeof(CT) == 2, bf16x4, floatx4> vraw[CPW][NB];
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut)
 #pragma unroll
@@ -751,10 +755,16 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int ut = 0; ut < NB; ++ut) {
           al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc)
-            vv[cc][ut] = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f}
-                                            : to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc)));
+          for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc));
         }
+        // T of this chunk is ready since phase B of the previous one: its
+        // fragments are requested now so T Y finds them in registers
+        Frag tf[NB][NFB];
+        static_for<NB>([&](auto ub) {
+          constexpr int ut = decltype(ub)::value;
+#pragma unroll
+          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
+        });
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
@@ -768,18 +778,16 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
             if constexpr (outs) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
           }
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (vv[cc][ut] - p[cc]);
+          for (int cc = 0; cc < CPW; ++cc) {
+            const floatx4 vv = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
+            y[cc][ut] = al[ut] * (vv - p[cc]);
+          }
         }
-        Frag yf[CPW][NFB], tf[NB][NFB];
+        Frag yf[CPW][NFB];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFB; ++f) yf[cc][f] = MM::template acc<NB>(y[cc], f);
-        static_for<NB>([&](auto ub) {
-          constexpr int ut = decltype(ub)::value;
-#pragma unroll
-          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
-        });
         __builtin_amdgcn_sched_barrier(0);
         floatx4 u[CPW][NB];
         static_for<NB>([&](auto ub) {
