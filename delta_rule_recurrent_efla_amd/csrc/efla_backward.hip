@@ -155,7 +155,8 @@ struct BwdArgs {
   void *dq, *dk, *dv, *dbeta;
   float* ds0;
   int T, nc, coef;
-  // workspace (fp32)
+  // workspace (fp32, except sc and dsc in the bf16 form: bf16 inputs with C
+  // and d multiples of 32, where every use of them is a bf16 MFMA operand)
   const float* sc;  // [head][chunk][d_v][d_k] state at the start of each chunk
   const float* scn; // the same states, [head][chunk][d_k][d_v]
   float* dsc;       // [head][chunk][d_k][d_v] gradient of the state at each chunk's end
@@ -551,11 +552,11 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   for (int ch = a.nc - 1; ch >= 0; --ch) {
     const int t0 = ch * C, nval = min(C, a.T - t0);
     if (owner) {
-      float* dst = a.dsc + ((size_t)h * a.nc + ch) * D * D;
+      bf16* dst = (bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;
 #pragma unroll
       for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = (bf16)ds[rt][e];
     }
     __syncthreads();
 #pragma unroll
@@ -681,6 +682,8 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   const float* St = a.sc + ((size_t)h * a.nc + ch) * D * D;   // [v][k]
   const float* Sn = a.scn + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
   const float* dS = a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
+  const bf16* Stb = (const bf16*)a.sc + ((size_t)h * a.nc + ch) * D * D;   // bf16 form
+  const bf16* dSb = (const bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;  // bf16 form
   const float* G = a.gw + rb * D;                             // [row][v]
   const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
   const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   // NKT) and forms its S^T fragments once
   constexpr bool BFK = BF && D % 32 == 0 && C % 32 == 0;
   bf16x8 stf[BFK ? D / 32 : 1];
-  if constexpr (BFK) bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * (w % NKT) + li) * D + k0]); });
+  if constexpr (BFK) bf_frags<D>(stf, [&](int k0) { return -ld4(&Stb[(size_t)(16 * (w % NKT) + li) * D + k0]); });
   for (int tl = w; tl < NKT * NB; tl += NWV) {
     const int I = tl % NKT, J = tl / NKT;  // I: v tile, J: row tile
     floatx4 acc;
@@ -815,10 +818,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
     bf_frags<D>(snf, [&](int k0) {
       floatx4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = St[(size_t)(k0 + e) * D + cj];
+      for (int e = 0; e < 4; ++e) x[e] = ld1(&Stb[(size_t)(k0 + e) * D + cj]);
       return x;
     });
-    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+    bf_frags<D>(dsf, [&](int k0) { return ld4(&dSb[(size_t)cj * D + k0]); });
     bf_frags<C>(ktf, [&](int k0) { return *(const floatx4*)&sm.KT[cj][k0]; });
     bf_frags<C>(qtf, [&](int k0) { return *(const floatx4*)&sm.QT[cj][k0]; });
   }

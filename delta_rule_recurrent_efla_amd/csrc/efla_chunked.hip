@@ -63,8 +63,9 @@ struct ChunkedArgs {
   float* seg_out;
   int coef;  // step coefficient rule (gate_coef)
   // pass mode 2 of the pipelined kernel (states for the backward): the state
-  // at the start of every chunk, [head][chunk][d_v][d_k] fp32 (transposed)
-  // and, when s_chunks_n is not null, [head][chunk][d_k][d_v] (natural)
+  // at the start of every chunk, [head][chunk][d_v][d_k] (transposed; bf16
+  // for bf16 inputs with C and d multiples of 32, else fp32) and, when
+  // s_chunks_n is not null, [head][chunk][d_k][d_v] fp32 (natural)
   float* s_chunks;
   float* s_chunks_n;
 };
@@ -721,16 +722,21 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       //      products run, then the T fragments
       if (act) {
         if constexpr (SAVE) {
-          // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 16
-          // contiguous bytes of the transposed state
+          // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 4
+          // contiguous elements of the transposed state, stored as bf16 where
+          // the backward takes them only as bf16 MFMA operands (bf16 inputs,
+          // C and d multiples of 32), else as fp32
+          constexpr bool SBF = sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0;
           float* dst = a.s_chunks + ((size_t)hd * nchunks + c) * D * D;
+          bf16* dsb = (bf16*)a.s_chunks + ((size_t)hd * nchunks + c) * D * D;
           float* dsn = a.s_chunks_n + ((size_t)hd * nchunks + c) * D * D;
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (w * CPW + cc) + li;
-              *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
+              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(sacc[cc][rt]);
+              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
               if (a.s_chunks_n) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
