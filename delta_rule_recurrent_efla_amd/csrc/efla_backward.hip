@@ -473,17 +473,20 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
 // v_mfma_f32_16x16x32_bf16. Lane (g, li) supplies k = 32 kb + 4 g + {0..3}
 // and 32 kb + 16 + 4 g + {0..3}: for an operand held in accumulators these
 // are rows 4 g + e of tiles 2 kb and 2 kb + 1, so dS', dU and D G feed the
-// next product without lane exchange. T and M are rounded to bf16, as in the
-// forward; accumulation and the dS state stay fp32.
+// next product without lane exchange. K, Q and the dO slice are staged
+// row-major with 16-byte writes; the operands that run over their columns
+// (K^T, Q^T as A, dO as B) are read with ds_read_b64_tr_b16. Every row
+// stride is an odd multiple of 32 bytes, which keeps both the 16-byte writes
+// and the transposed reads free of bank conflicts. T and M are rounded to
+// bf16, as in the forward; accumulation and the dS state stay fp32.
 template <int D, int C, int BV>
 struct StateSmemBf {
-  static constexpr int LD = D + 8, LC = C + 8;
+  static constexpr int LD = D + 16, LO = BV + ((32 - 2 * BV % 64 + 64) % 64) / 2, LC = C + 8;
   bf16 Kf[C][LD];
-  bf16 KT[D][LC];
-  bf16 QT[D][LC];
+  bf16 Qf[C][LD];
+  bf16 dOf[C][LO];
   bf16 MT[C][LC];
   bf16 TT[C][LC];
-  bf16 dOT[BV][LC];
   float al[C];
 };
 
@@ -495,6 +498,7 @@ __device__ __forceinline__ bf16x4 cv4(floatx4 x) { return __builtin_convertvecto
 template <int D, int C, int BV>
 __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   using Sm = StateSmemBf<D, C, BV>;
+  static_assert((Sm::LD * 2) % 64 == 32 && (Sm::LO * 2) % 64 == 32, "row strides");
   __shared__ __attribute__((aligned(16))) Sm sm;
   constexpr int NKT = D / 16, NB = C / 16, NW = BV / 16;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
@@ -515,25 +519,26 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   const bf16* kg = (const bf16*)a.k + (size_t)h * a.T * D;
   const bf16* qg = (const bf16*)a.q + (size_t)h * a.T * D;
   const bf16* dog = (const bf16*)a.dout + (size_t)h * a.T * D;
-  constexpr int NLK = (C * D / 4 + 255) / 256, NLO = (C * BV / 4 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
-  bf16x4 rk[NLK], rq[NLK], ro[NLO];
+  // 16-byte pieces per thread: K and Q rows, the dO slice, M^T and T^T (fp32)
+  constexpr int NLK = (C * D / 8 + 255) / 256, NLO = (C * BV / 8 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
+  bf16x8 rk[NLK], rq[NLK], ro[NLO];
   floatx4 rm[NLM], rt4[NLM];
   float ral = 0.f;
   auto fetch = [&](int ch) {
     const int t0 = ch * C, nval = min(C, a.T - t0);
     const size_t mb = ((size_t)h * a.nc + ch) * C * C;
-    const bf16x4 z4 = {};
+    const bf16x8 z8 = {};
 #pragma unroll
     for (int j = 0; j < NLK; ++j) {
-      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
-      const bool ok = i < C * D / 4 && r < nval;
-      rk[j] = ok ? *(const bf16x4*)(kg + (size_t)(t0 + r) * D + c4) : z4;
-      rq[j] = ok ? *(const bf16x4*)(qg + (size_t)(t0 + r) * D + c4) : z4;
+      const int i = tid + 256 * j, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+      const bool ok = i < C * D / 8 && r < nval;
+      rk[j] = ok ? *(const bf16x8*)(kg + (size_t)(t0 + r) * D + c8) : z8;
+      rq[j] = ok ? *(const bf16x8*)(qg + (size_t)(t0 + r) * D + c8) : z8;
     }
 #pragma unroll
     for (int j = 0; j < NLO; ++j) {
-      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
-      ro[j] = (i < C * BV / 4 && r < nval) ? *(const bf16x4*)(dog + (size_t)(t0 + r) * D + v0 + c4) : z4;
+      const int i = tid + 256 * j, r = i / (BV / 8), c8 = 8 * (i % (BV / 8));
+      ro[j] = (i < C * BV / 8 && r < nval) ? *(const bf16x8*)(dog + (size_t)(t0 + r) * D + v0 + c8) : z8;
     }
 #pragma unroll
     for (int j = 0; j < NLM; ++j) {
@@ -561,23 +566,16 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < NLK; ++j) {
-      const int i = tid + 256 * j, r = i / (D / 4), c4 = 4 * (i % (D / 4));
-      if (i < C * D / 4) {
-        *(bf16x4*)&sm.Kf[r][c4] = rk[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sm.KT[c4 + e][r] = rk[j][e];
-          sm.QT[c4 + e][r] = rq[j][e];
-        }
+      const int i = tid + 256 * j, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+      if (i < C * D / 8) {
+        *(bf16x8*)&sm.Kf[r][c8] = rk[j];
+        *(bf16x8*)&sm.Qf[r][c8] = rq[j];
       }
     }
 #pragma unroll
     for (int j = 0; j < NLO; ++j) {
-      const int i = tid + 256 * j, r = i / (BV / 4), c4 = 4 * (i % (BV / 4));
-      if (i < C * BV / 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dOT[c4 + e][r] = ro[j][e];
-      }
+      const int i = tid + 256 * j, r = i / (BV / 8), c8 = 8 * (i % (BV / 8));
+      if (i < C * BV / 8) *(bf16x8*)&sm.dOf[r][c8] = ro[j];
     }
 #pragma unroll
     for (int j = 0; j < NLM; ++j) {
@@ -592,7 +590,21 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
     __syncthreads();
     if (owner) {
       const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      const bf16* dorow = &sm.dOT[16 * w + li][0];
+      // dO columns of this wave as B fragments (k = tokens)
+      bf16x8 dof[NB / 2];
+#pragma unroll
+      for (int kb = 0; kb < NB / 2; ++kb) dof[kb] = tr_frag<NB>(&sm.dOf[0][0], Sm::LO, kb, 16 * w);
+      // Q^T dO: no dependence on dS', so it runs ahead of the chain
+      floatx4 qd[NKT];
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) {
+        floatx4 acc = ds[rt];
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_frag<NB>(&sm.Qf[0][0], Sm::LD, kb, 16 * rt), dof[kb], acc,
+                                                        0, 0, 0);
+        qd[rt] = acc;
+      }
       // dU = M^T dO + K dS'
       floatx4 du[NB];
 #pragma unroll
@@ -600,7 +612,7 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
         floatx4 acc = z;
 #pragma unroll
         for (int kb = 0; kb < NB / 2; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.MT[16 * I + li][0], kb), ld_a(dorow, kb), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.MT[16 * I + li][0], kb), dof[kb], acc, 0, 0, 0);
 #pragma unroll
         for (int kb = 0; kb < NKT / 2; ++kb)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.Kf[16 * I + li][0], kb),
@@ -630,13 +642,11 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
       // dS = dS' + Q^T dO - K^T D G
 #pragma unroll
       for (int rt = 0; rt < NKT; ++rt) {
-        floatx4 acc = ds[rt];
+        floatx4 acc = qd[rt];
 #pragma unroll
-        for (int kb = 0; kb < NB / 2; ++kb) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.QT[16 * rt + li][0], kb), ld_a(dorow, kb), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&sm.KT[16 * rt + li][0], kb),
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_frag<NB>(&sm.Kf[0][0], Sm::LD, kb, 16 * rt),
                                                         pk8(cv4(-dy[2 * kb]), cv4(-dy[2 * kb + 1])), acc, 0, 0, 0);
-        }
         ds[rt] = acc;
       }
     }
