@@ -703,10 +703,13 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
   auto row4 = [&](const CT* base, int r, int c) -> floatx4 {
     return r < nval ? ld4(base + (size_t)r * D + c) : floatx4{0.f, 0.f, 0.f, 0.f};
   };
-  // X^T of a C x D input into LDS (zero rows past T)
+  // X^T of a C x D input into LDS (zero rows past T). Consecutive lanes take
+  // consecutive rows of X, so each transposed write of a wave covers
+  // consecutive words of one row of X^T (a lane per row of X would put a
+  // wave's writes on a few LDS banks).
   auto stage_t = [&](float (*XT)[Sm::LC], const CT* base) {
     for (int i = tid; i < C * D / 4; i += 64 * NWV) {
-      const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
+      const int r = i % C, c4 = 4 * (i / C);
       const floatx4 x = row4(base, r, c4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) XT[c4 + e][r] = x[e];
