@@ -946,6 +946,223 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// 4, bf16 form (bf16 inputs, C and d multiples of 32). Every tile the products
+// share sits in LDS as bf16 with column-permuted rows (the forward kernel's
+// layout): a fragment along a row is one 16-byte read and a fragment along a
+// column a pair of ds_read_b64_tr_b16. Each product is formed in the
+// orientation whose accumulator holds 4 consecutive columns of one row of the
+// tile it is stored to (8-byte writes). dc is summed from the fp32
+// accumulators of Yh and E as they are formed. With X = D E:
+//   Yh^T tiles  = (V - K S)^T         A = rows of K, B = -S^T rows
+//   U^T tiles   = Yh^T (T D)^T        A = rows of Yh^T, B = rows of T D
+//   dM, E       from U dO^T, -U G^T   A = rows of U, B = rows of dO, G
+//   dQ = dO S^T + dM K
+//   dK = dM^T Q + U dS'^T - D (G S^T) + X K + X^T K
+template <int D, int C>
+struct GradSmemBf {
+  static constexpr int LD = D + 16, LC = C + 16;  // row strides: 32 bytes mod 64
+  bf16 Kb[C][LD];
+  bf16 Qb[C][LD];
+  bf16 dOb[C][LD];
+  bf16 Gb[C][LD];
+  bf16 Ub[C][LD];  // U = T D Yh
+  union {
+    bf16 YTb[D][LC];  // Yh^T, until U is formed
+    struct {
+      bf16 dMb[C][LC];  // lower-incl-diag(dO U^T)
+      bf16 Xb[C][LC];   // D E
+    } m;
+  };
+  float al[C], dc[C];
+  float dcp[C][D / 16 + 1];   // rowsum(G * Yh) over one 16-column tile of v
+  float dcp2[C][C / 16 + 1];  // rowsum(E * K K^T) over one 16-column tile
+};
+
+template <int D, int C>
+__global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
+  using Sm = GradSmemBf<D, C>;
+  using MM = Mma<bf16>;
+  static_assert(D % 32 == 0 && C % 32 == 0, "bf16 form");
+  static_assert((Sm::LD * 2) % 64 == 32 && (Sm::LC * 2) % 64 == 32, "row strides");
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  constexpr int NKT = D / 16, NB = C / 16, NWV = 8, KD = D / 32, KC = C / 32;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
+  const int t0 = ch * C, nval = min(C, a.T - t0);
+  const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+  const size_t rb = (size_t)h * a.nc * C + t0;
+  const bf16* St = (const bf16*)a.sc + ((size_t)h * a.nc + ch) * D * D;   // [v][k]
+  const bf16* dS = (const bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
+  const float* G = a.gw + rb * D;                                         // [row][v]
+  const bf16* kg = (const bf16*)a.k + ((size_t)h * a.T + t0) * D;
+  const bf16* qg = (const bf16*)a.q + ((size_t)h * a.T + t0) * D;
+  const bf16* vg = (const bf16*)a.v + ((size_t)h * a.T + t0) * D;
+  const bf16* dog = (const bf16*)a.dout + ((size_t)h * a.T + t0) * D;
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  auto mma = [](bf16x8 x, bf16x8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0); };
+
+  // ---- K, Q, dO and G rows (zero past T), c
+  for (int i = tid; i < C * D / 8; i += 64 * NWV) {
+    const int r = i / (D / 8), c8 = 8 * (i % (D / 8));
+    bf16x8 kx = {}, qx = {}, ox = {}, gx = {};
+    if (r < nval) {
+      kx = *(const bf16x8*)(kg + (size_t)r * D + c8);
+      qx = *(const bf16x8*)(qg + (size_t)r * D + c8);
+      ox = *(const bf16x8*)(dog + (size_t)r * D + c8);
+      gx = pk8(cv4(ld4(G + (size_t)r * D + c8)), cv4(ld4(G + (size_t)r * D + c8 + 4)));
+    }
+    st_perm(&sm.Kb[r][0], c8, kx);
+    st_perm(&sm.Qb[r][0], c8, qx);
+    st_perm(&sm.dOb[r][0], c8, ox);
+    st_perm(&sm.Gb[r][0], c8, gx);
+  }
+  if (tid < C) sm.al[tid] = a.al[rb + tid];
+  __syncthreads();
+
+  // ---- Yh^T tiles (v tile I, token tile J): acc[e] = -(K S)[16 J + 4g + e][16 I + li];
+  //      then + V, rowsum(G * Yh) over the tile's 16 v, stored as rows of Yh^T
+  for (int I = w; I < NKT; I += NWV) {
+    bf16x8 stf[KD];
+    bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); });
+    for (int J = 0; J < NB; ++J) {
+      floatx4 acc = z;
+#pragma unroll
+      for (int kb = 0; kb < KD; ++kb) acc = mma(MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), stf[kb], acc);
+      floatx4 gy;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * J + 4 * g + e, v = 16 * I + li;
+        const bool ok = r < nval;
+        acc[e] += ok ? (float)vg[(size_t)r * D + v] : 0.f;
+        gy[e] = group_sum<16>(ok ? G[(size_t)r * D + v] * acc[e] : 0.f);
+      }
+      if (li < 4) sm.dcp[16 * J + 4 * g + li][I] = gy[li];
+      MM::store_tp(&sm.YTb[16 * I + li][0], J, acc);
+    }
+  }
+  __syncthreads();
+
+  // ---- U^T tiles (token tile I, v tile J): acc[e] = U[16 I + li][16 J + 4g + e];
+  //      B(j, i) = T[i][j] c_j, row i of T D, formed once per wave
+  {
+    const int I = w % NB;
+    const float* Tn = a.tn + mb;
+    bf16x8 tdf[KC];
+    bf_frags<C>(tdf, [&](int k0) {
+      return ld4(&Tn[(size_t)(16 * I + li) * C + k0]) * *(const floatx4*)&sm.al[k0];
+    });
+    for (int J = w / NB; J < NKT; J += NWV / NB) {
+      floatx4 acc = z;
+#pragma unroll
+      for (int kb = 0; kb < KC; ++kb) acc = mma(MM::template ldp<NB>(&sm.YTb[16 * J + li][0], kb), tdf[kb], acc);
+      MM::store_tp(&sm.Ub[16 * I + li][0], J, acc);
+    }
+  }
+  __syncthreads();
+
+  // ---- dM and E tiles (token tiles I >= J; the others are zero): acc[e] =
+  //      (dO U^T)[16 I + li][16 J + 4g + e], and the same with -G; X = D E;
+  //      rowsum(E * K K^T) over the tile's 16 columns
+  {
+    const int I = w % NB;
+    const float ci = sm.al[16 * I + li];
+    bf16x8 dof[KD], gf[KD];
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+      dof[kb] = MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb);
+      gf[kb] = MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb);
+    }
+    for (int J = w / NB; J < NB; J += NWV / NB) {
+      floatx4 m = z, e4 = z;
+      float s = 0.f;
+      if (J <= I) {
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+          const bf16x8 u = MM::template ldp<NKT>(&sm.Ub[16 * J + li][0], kb);
+          m = mma(u, dof[kb], m);
+          e4 = mma(u, gf[kb], e4);
+        }
+        const floatx4 gr = ld4(a.gram + mb + (size_t)(16 * I + li) * C + 16 * J + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * I + li, j = 16 * J + 4 * g + e;
+          m[e] = j <= i ? m[e] : 0.f;
+          e4[e] = j < i ? -e4[e] : 0.f;
+          s += e4[e] * gr[e];
+          e4[e] *= ci;
+        }
+      }
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (g == 0) sm.dcp2[16 * I + li][J] = s;
+      MM::store_tp(&sm.m.dMb[16 * I + li][0], J, m);
+      MM::store_tp(&sm.m.Xb[16 * I + li][0], J, e4);
+    }
+  }
+  __syncthreads();
+
+  // ---- dc, dbeta
+  if (tid < C) {
+    float s = 0.f;
+#pragma unroll
+    for (int I = 0; I < NKT; ++I) s += sm.dcp[tid][I];
+#pragma unroll
+    for (int J = 0; J < NB; ++J) s += sm.dcp2[tid][J];
+    sm.dc[tid] = s;
+    if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * a.fb[rb + tid]);
+  }
+  __syncthreads();
+
+  // ---- dQ and dK tiles (token tile I, key tile J): acc[e] at row 16 I + 4g + e,
+  //      column 16 J + li; wave w takes key tile J and forms the fragments of
+  //      row J of S, dS' (over v) and of columns J of K, Q (over tokens) once
+  bf16* dqg = (bf16*)a.dq + ((size_t)h * a.T + t0) * D;
+  bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
+  for (int J = w; J < NKT; J += NWV) {
+    const int cj = 16 * J + li;
+    bf16x8 snf[KD], dsf[KD], ktf[KC], qtf[KC];
+    bf_frags<D>(snf, [&](int k0) {
+      floatx4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = ld1(&St[(size_t)(k0 + e) * D + cj]);
+      return x;
+    });
+    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb) {
+      ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
+      qtf[kb] = tr_frag<NB, true>(&sm.Qb[0][0], Sm::LD, kb, 16 * J);
+    }
+    for (int I = 0; I < NB; ++I) {
+      floatx4 dq = z, dk = z, dg = z;
+#pragma unroll
+      for (int kb = 0; kb < KD; ++kb) {
+        dq = mma(MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb), snf[kb], dq);
+        dk = mma(MM::template ldp<NKT>(&sm.Ub[16 * I + li][0], kb), dsf[kb], dk);
+        dg = mma(MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb), snf[kb], dg);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KC; ++kb) {
+        dq = mma(MM::template ldp<NB>(&sm.m.dMb[16 * I + li][0], kb), ktf[kb], dq);
+        dk = mma(tr_frag<NB, true>(&sm.m.dMb[0][0], Sm::LC, kb, 16 * I), qtf[kb], dk);
+        dk = mma(MM::template ldp<NB>(&sm.m.Xb[16 * I + li][0], kb), ktf[kb], dk);
+        dk = mma(tr_frag<NB, true>(&sm.m.Xb[0][0], Sm::LC, kb, 16 * I), ktf[kb], dk);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + 4 * g + e;
+        if (r < nval) {
+          const float kv = (float)sm.Kb[r][MM::pcol(cj)];
+          dqg[(size_t)r * D + cj] = (bf16)dq[e];
+          dkg[(size_t)r * D + cj] = (bf16)(dk[e] - sm.al[r] * dg[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <typename CT, int D, int C>
 static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
   constexpr int BV = D < 64 ? D : 64;
@@ -957,7 +1174,11 @@ static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
     hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
                        stream, a);
   }
-  hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
+  if constexpr (sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0) {
+    hipLaunchKernelGGL((efla_bwd_grad_kernel_bf<D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -603,13 +603,6 @@ __host__ __device__ constexpr int t_first(int pw) {
   return f;
 }
 
-// 16-byte register vector of 8 (bf16) or 4 (fp32) consecutive columns
-// starting at c0 -> column-permuted LDS row.
-__device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
-  *(bf16x4*)(row + Mma<bf16>::pcol(c0)) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
-  *(bf16x4*)(row + Mma<bf16>::pcol(c0 + 4)) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
-}
-__device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
 
 template <typename CT, int D, int C, int BV, int NSW, int PM>
 __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {

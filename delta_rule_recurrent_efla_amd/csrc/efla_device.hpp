@@ -324,6 +324,14 @@ __device__ __forceinline__ floatx4 tr_frag(const float* base, int ld, int f, int
   return ldtr4<PERM>(base, ld, 16 * f + 4 * g, col0);
 }
 
+// 16-byte register vector of 8 (bf16) or 4 (fp32) consecutive columns
+// starting at c0 (a multiple of 8, or 4) -> column-permuted LDS row.
+__device__ __forceinline__ void st_perm(bf16* row, int c0, bf16x8 v) {
+  *(bf16x4*)(row + Mma<bf16>::pcol(c0)) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+  *(bf16x4*)(row + Mma<bf16>::pcol(c0 + 4)) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void st_perm(float* row, int c0, floatx4 v) { *(floatx4*)(row + c0) = v; }
+
 // Number of fragments covering NR 16-row tiles.
 template <typename CT, int NR>
 struct NFrag {
