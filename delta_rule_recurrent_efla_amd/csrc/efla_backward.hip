@@ -182,6 +182,9 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   const int t0 = ch * C, nval = min(C, a.T - t0);
   const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
   const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
+  // M^T and T^T are stored as bf16 where their only reader rounds them to bf16
+  // (the bf16 form of the state pass), else as fp32
+  constexpr bool MBF = sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0;
   for (int i = tid; i < C * D / 4; i += 256) {
     const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
     const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -209,18 +212,22 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   const size_t mb = ((size_t)h * a.nc + ch) * C * C;
   constexpr int NT = C / 16;
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  // Q K^T tiles (I, J): B(k, j) = K[16J + j][k], a row of K
+  // K Q^T tiles (J, I), i.e. M^T: A = rows of K, B(k, i) = Q[16I + i][k], a
+  // row of Q; lane (g, li) holds M^T[16J + 4g + e][16I + li], so a row of M^T
+  // is written by 16 consecutive lanes
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
     // bf16 inputs: products of bf16 values are exact in fp32, so the bf16 MFMA
     // gives the same K K^T and Q K^T as the fp32 one
-    const floatx4 qk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Qf[16 * I + li][k0]; },
-                                               [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; });
+    const floatx4 kq = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; },
+                                               [&](int k0) { return *(const floatx4*)&Qf[16 * I + li][k0]; });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * I + 4 * g + e, j = 16 * J + li;
-      // M[i][j] = q_i . k_j for j <= i; stored transposed: M^T[j][i]
-      a.mt[mb + (size_t)j * C + i] = j <= i ? qk[e] : 0.f;
+      const int j = 16 * J + 4 * g + e, i = 16 * I + li;
+      // M[i][j] = q_i . k_j for j <= i
+      const float m = j <= i ? kq[e] : 0.f;
+      if constexpr (MBF) ((bf16*)a.mt)[mb + (size_t)j * C + i] = (bf16)m;
+      else a.mt[mb + (size_t)j * C + i] = m;
     }
   }
   __syncthreads();  // Q is dead: its space takes A
@@ -288,7 +295,8 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
     floatx4 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = Ts(c4 + e, r);
-    *(floatx4*)&a.tt[mb + (size_t)r * C + c4] = x;
+    if constexpr (MBF) *(bf16x4*)&((bf16*)a.tt)[mb + (size_t)r * C + c4] = __builtin_convertvector(x, bf16x4);
+    else *(floatx4*)&a.tt[mb + (size_t)r * C + c4] = x;
   }
 }
 
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   // 16-byte pieces per thread: K and Q rows, the dO slice, M^T and T^T (fp32)
   constexpr int NLK = (C * D / 8 + 255) / 256, NLO = (C * BV / 8 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
   bf16x8 rk[NLK], rq[NLK], ro[NLO];
-  floatx4 rm[NLM], rt4[NLM];
+  bf16x4 rm[NLM], rt4[NLM];  // M^T and T^T, stored as bf16 for this form
   float ral = 0.f;
   auto fetch = [&](int ch) {
     const int t0 = ch * C, nval = min(C, a.T - t0);
@@ -544,8 +552,8 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
     for (int j = 0; j < NLM; ++j) {
       const int i = tid + 256 * j;
       if (i < C * C / 4) {
-        rm[j] = ld4(a.mt + mb + 4 * (size_t)i);
-        rt4[j] = ld4(a.tt + mb + 4 * (size_t)i);
+        rm[j] = *(const bf16x4*)((const bf16*)a.mt + mb + 4 * (size_t)i);
+        rt4[j] = *(const bf16x4*)((const bf16*)a.tt + mb + 4 * (size_t)i);
       }
     }
     if (tid < C) ral = a.al[(size_t)h * a.nc * C + t0 + tid];
@@ -581,8 +589,8 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
     for (int j = 0; j < NLM; ++j) {
       const int i = tid + 256 * j, r = i / (C / 4), c4 = 4 * (i % (C / 4));
       if (i < C * C / 4) {
-        *(bf16x4*)&sm.MT[r][c4] = cv4(rm[j]);
-        *(bf16x4*)&sm.TT[r][c4] = cv4(rt4[j]);
+        *(bf16x4*)&sm.MT[r][c4] = rm[j];
+        *(bf16x4*)&sm.TT[r][c4] = rt4[j];
       }
     }
     if (tid < C) sm.al[tid] = ral;
