@@ -217,7 +217,7 @@ def bench_backward(efla, torch, efla_inputs, w, steps=10, warmup=3):
             "head_tokens_per_s": w.head_tokens / (med * 1e-3),
             "alg_bytes": nbytes, "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "workspace_bytes": ws,
-            "note": "includes the recomputed forward; fp32 arithmetic"}
+            "note": "includes the recomputed forward; bf16 MFMA operands, fp32 accumulation"}
 
 
 def bench_decode(efla, torch, efla_inputs, steps=256):

@@ -710,9 +710,9 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       floatx4 oacc[CPW][NB];
       Frag sf[CPW][NFK], uf[CPW][NFB], kt[NKT][NFB], qf[NB][NFK];
       // ---- phase A: K S, Y = diag(a)(V - K S); U' = T Y (T of this chunk
-      //      is ready one phase early). All K fragments (and V, a) are
+      //      is ready one phase early). The K, V, a and T fragments are
       //      requested first, the Q fragments (for phase B) while the K S
-      //      products run, then the T fragments
+      //      products run
       if (act) {
         if constexpr (SAVE) {
           // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 4
