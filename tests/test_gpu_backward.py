@@ -133,3 +133,28 @@ def test_backward_is_deterministic(efla):
     torch.cuda.synchronize()
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+def test_backward_full_size_sampled_heads(efla):
+    """The 1.3B-layer shape at full size (128 heads x T = 4096, bf16, random
+    S0) in the launch configuration the bench times; the oracle's reverse mode
+    on three heads (each head's gradients depend only on its own inputs)."""
+    w = efla_inputs.WORKLOADS["layer1p3b_d128"]
+    note(f"[bwd full] {w.name}: B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} {w.dtype}")
+    x = efla_inputs.make_inputs(w)
+    dout, dsT = upstream(4242, w.B, w.H, w.T, w.d, w.dtype, True)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    got = efla.efla_bwd_chunked(dev["q"], dev["k"], dev["v"], dev["beta"], dout.cuda(), dev["s0"], dsT.cuda(),
+                                chunk=w.chunk)
+    torch.cuda.synchronize()
+    nh = w.B * w.H
+    heads = [0, nh // 2 + 3, nh - 1]
+    flat = lambda t: t.reshape((nh,) + tuple(t.shape[2:]))
+    sel = lambda t: flat(t)[heads]
+    ref = oracle.bwd(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]), sel(dout), sel(x["s0"]), sel(dsT),
+                     nthreads=3)
+    errs = {}
+    for name, gv, rv in zip(("dq", "dk", "dv", "dbeta", "ds0"), got, ref):
+        errs[name] = normwise(sel(gv.float().cpu()), rv)
+    note("   heads " + str(heads) + ": " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
