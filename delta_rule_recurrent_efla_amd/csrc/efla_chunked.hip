@@ -517,10 +517,15 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 // inverses, T = (I + A)^{-1} with A = strictly-lower(diag(a) K K^T) (full,
 // lower triangular) and M = lower-incl-diag(Q K^T); the state pass then needs
 // no WY factor:
-//   Y  = diag(a) (V - K S)
-//   U' = T Y                       (= U - W S with W = T diag(a) K, U = T diag(a) V)
+//   Y  = V - K S
+//   U' = T diag(a) Y               (= U - W S with W = T diag(a) K, U = T diag(a) V)
 //   O^T = S^T Q^T + U'^T M^T       (read out after each update)
 //   S <- S + K^T U'
+// The state waves hold N = -S and the solvers store T' = -T diag(a) (a applied
+// in fp32), so Y = V + K N comes out of the MFMAs with the values as the
+// accumulator's start, -U' = T' Y, N <- N + K^T (-U') and
+// -O^T = N^T Q^T + (-U')^T M^T: no per-element gate or subtraction in the
+// serial pass. Outputs and states are negated back when stored.
 // Two workgroup barriers per chunk split it into phases A and B. While the
 // state waves run chunk c:
 //   state waves    A: K S, Y, U' = T Y           B: S^T Q^T, K^T U', U'^T M^T;
@@ -562,7 +567,7 @@ struct __attribute__((aligned(16))) PipeSmem {
   CT An[2][C][CP];        // -(K K^T) blocks below the diagonal, permuted, one copy per solver
   float Adt[NB][17][20];  // fp32 diagonal blocks of A, transposed; the 17th row
                           // staggers the blocks over the LDS banks
-  CT Td[NB][16][TDS];     // (I + A_bb)^{-1}, natural layout
+  CT Td[NB][16][TDS];     // (I + A_bb)^{-1}, transposed: row c holds column c
 };
 
 template <typename CT, int D, int C, int BV>
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
+            sacc[c][rt][e] = -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
     }
     if (SUMMARY && owner && ident) {
 #pragma unroll
@@ -696,7 +701,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (w * CPW + c) + li) ? 1.f : 0.f;
+            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (w * CPW + c) + li) ? -1.f : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -709,10 +714,9 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
       const auto& B = sm.buf[c & 1];
       floatx4 oacc[CPW][NB];
       Frag sf[CPW][NFK], uf[CPW][NFB], kt[NKT][NFB], qf[NB][NFK];
-      // ---- phase A: K S, Y = diag(a)(V - K S); U' = T Y (T of this chunk
-      //      is ready one phase early). The K, V, a and T fragments are
-      //      requested first, the Q fragments (for phase B) while the K S
-      //      products run
+      // ---- phase A: Y = V + K N; -U' = T' Y (T' of this chunk is ready one
+      //      phase early). The K, V and T' fragments are requested first, the
+      //      Q fragments (for phase B) while the K N products run
       if (act) {
         if constexpr (SAVE) {
           // lane (g, li) holds rows 16 rt + 4g .. + 3 of one column: 4
@@ -728,11 +732,11 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (w * CPW + cc) + li;
-              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(sacc[cc][rt]);
-              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
+              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(-sacc[cc][rt]);
+              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = -sacc[cc][rt];
               if (a.s_chunks_n) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
+                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = -sacc[cc][rt][e];
               }
             }
         }
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
         Frag kf[NB][NFK];
-        floatx4 al[NB], y[CPW][NB];
+        floatx4 y[CPW][NB];
         // the value columns stay in their storage type until Y: converting
         // them here would make the wave wait for every read before the first
         // product (a transition run ignores them: its value buffer holds keys)
@@ -752,7 +756,6 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           for (int f = 0; f < NFK; ++f) kf[ut][f] = MM::template ldp<NKT>(&B.K[16 * ut + li][0], f);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
-          al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc));
         }
@@ -762,24 +765,20 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
 #pragma unroll
-          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldp<ut + 1>(&B.T[16 * ut + li][0], f);
+          for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) tf[ut][f] = MM::template ldps<ut + 1>(&B.T[16 * ut + li][0], f);
         });
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
-          floatx4 p[CPW];
+          // Y = V - K S = V + K N, with the values as the accumulator's start
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) p[cc] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int cc = 0; cc < CPW; ++cc)
+            y[cc][ut] = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
 #pragma unroll
-            for (int cc = 0; cc < CPW; ++cc) p[cc] = MM::mma(p[cc], kf[ut][f], sf[cc][f]);
+            for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = MM::mma(y[cc][ut], kf[ut][f], sf[cc][f]);
             if constexpr (outs) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
-          }
-#pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) {
-            const floatx4 vv = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
-            y[cc][ut] = al[ut] * (vv - p[cc]);
           }
         }
         Frag yf[CPW][NFB];
@@ -850,7 +849,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
               constexpr int ut = decltype(ub)::value;
               if (ut == rt) {
 #pragma unroll
-                for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
+                for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldps<ut + 1>(&B.M[16 * ut + li][0], f);
               }
             });
           }
@@ -860,7 +859,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           constexpr int ut = decltype(ub)::value;
           if constexpr (ut >= NKT) {
 #pragma unroll
-            for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldp<ut + 1>(&B.M[16 * ut + li][0], f);
+            for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[ut][f] = MM::template ldps<ut + 1>(&B.M[16 * ut + li][0], f);
           }
         });
         static_for<NB>([&](auto ub) {
@@ -880,7 +879,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           if (16 * ut + li < nval) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc)
-              store4(orow + (size_t)16 * ut * D + 16 * (w * CPW + cc), oacc[cc][ut]);
+              store4(orow + (size_t)16 * ut * D + 16 * (w * CPW + cc), -oacc[cc][ut]);
           }
         }
       }
@@ -894,7 +893,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + cc) + li] = sacc[cc][rt][e];
+            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + cc) + li] = -sacc[cc][rt][e];
     }
   } else if (w < NSW + 2) {
     // ======================= solvers (prep waves 0, 1) =======================
@@ -1003,9 +1002,18 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
                 for (int r = j + 1; r < 16; ++r) t[r] -= acol[j][r >> 2][r & 3] * t[j];
               }
-              CT* Tb = &sm.Td[PW + 2 * g][0][0];
+              // lane li holds column li of the inverse: stored as row li of
+              // its transpose, in 16-byte pieces (two LDS stores for bf16
+              // instead of sixteen 2-byte ones)
+              CT* Tb = &sm.Td[PW + 2 * g][li][0];
+              constexpr int VE16 = 16 / (int)sizeof(CT);
 #pragma unroll
-              for (int r = 0; r < 16; ++r) Tb[Sm::TDS * r + li] = from_f32<CT>(t[r]);
+              for (int p = 0; p < 16 / VE16; ++p) {
+                Vec tv;
+#pragma unroll
+                for (int e = 0; e < VE16; ++e) tv[e] = from_f32<CT>(t[VE16 * p + e]);
+                *(Vec*)&Tb[VE16 * p] = tv;
+              }
             }
           }
         }
@@ -1013,9 +1021,10 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         // ---- phase B: the Gram tiles below the diagonal that this solver's
         //      column tiles of T need (stored as -K K^T, unscaled: a is
         //      applied in the solve), then those column tiles:
-        //        X_m = (I + A_mm)^{-1},
-        //        X_i = (I + A_ii)^{-1} diag(a_i) sum_{m<=j<i} (-K_i K_j^T) X_j, i > m;
-        //      X_i^T is formed too so T is written row-major.
+        //        X_m = -(I + A_mm)^{-1} diag(a_m),
+        //        X_i = (I + A_ii)^{-1} diag(a_i) sum_{m<=j<i} (-K_i K_j^T) X_j, i > m,
+        //      the column tile m of T' = -T diag(a); X_i^T is formed too so T'
+        //      is written row-major.
         constexpr int M0 = t_first<NB>(PW);
         if constexpr (M0 < NB) {
           if (act) {
@@ -1038,7 +1047,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
                   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                   for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, kf[j][f], kf[i][f]);
-                  MM::store_tp(&An[16 * i + li][0], j, -acc);
+                  MM::store_tps(&An[16 * i + li][0], j, -acc);
                 }
               });
             });
@@ -1067,16 +1076,32 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
                         }
                         floatx4 xin[2] = {x[MM::KT * f],
                                           MM::KT == 2 && 2 * f + 1 < i ? x[2 * f + 1] : x[MM::KT * f]};
-                        acc = MM::mma(acc, MM::template ldp<i>(&An[16 * i + li][0], f),
+                        acc = MM::mma(acc, MM::template ldps<i>(&An[16 * i + li][0], f),
                                       MM::template acc<(MM::KT == 2 ? 2 : 1)>(xin, 0));
                       }
                       yv = *(const floatx4*)&B.alpha[16 * i + 4 * g] * acc;
                     }
-                    const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
+                    // row li of (I + A_ii)^{-1}, columns 4g..4g+3, from the
+                    // transposed store: one transposed read
+                    Frag td{};
+                    {
+                      const auto t4 = ldtr4(&sm.Td[i][0][0], Sm::TDS, 4 * g, 0);
+#pragma unroll
+                      for (int e = 0; e < 4; ++e) td[e] = t4[e];
+                    }
                     const Frag yf = MM::template acc<1>(&yv, 0);
                     x[i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
-                    const floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
-                    MM::store_tp(&B.T[16 * i + li][0], m, xt);
+                    floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
+                    if constexpr (i == m) {
+                      // T' = -T diag(a): the columns of tile m are scaled by
+                      // -a in fp32 here; the tiles below inherit it through
+                      // the solve, which is linear in X_m
+                      const float ac = -B.alpha[16 * m + li];
+                      const floatx4 ar = -*(const floatx4*)&B.alpha[16 * m + 4 * g];
+                      x[i] = x[i] * ac;
+                      xt = xt * ar;
+                    }
+                    MM::store_tps(&B.T[16 * i + li][0], m, xt);
                   } else {
                     x[i] = floatx4{0.f, 0.f, 0.f, 0.f};
                   }
@@ -1206,7 +1231,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
             }
-            MM::store_tp(&Bm.M[16 * I + li][0], J, v);
+            MM::store_tps(&Bm.M[16 * I + li][0], J, v);
           });
         }
       };
