@@ -609,8 +609,15 @@ __host__ __device__ constexpr int t_first(int pw) {
 }
 
 
+// Loader waves of a pass mode: the segment summaries (mode 1) stage no queries
+// and form no M, so two loaders serve them.
+template <int PM>
+constexpr int pipe_loaders() {
+  return PM == 1 ? 2 : 4;
+}
+
 template <typename CT, int D, int C, int BV, int NSW, int PM>
-__global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
+__global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
   using Vec = typename Vec16<CT>::type;
@@ -618,7 +625,17 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   constexpr int NB = C / 16;
   constexpr int NKT = D / 16;
   constexpr int NVT = BV / 16;
-  constexpr int SW = NSW < NVT ? NSW : NVT;  // state waves holding columns
+  // Pass mode PM: 0 outputs (one pass, or one segment of a time-segmented
+  // pass); 1 segment summaries, no outputs: the first half of the state waves
+  // runs the slice's columns from S = I with zero values (the segment's
+  // transition), the second half from S = 0 with the values (its offset),
+  // both on one prep of the keys; 2 chunk-start states for the backward, no
+  // outputs. All compile-time.
+  constexpr bool SUMMARY = PM == 1;
+  constexpr bool SAVE = PM == 2;
+  constexpr bool outs = PM == 0;
+  constexpr int NSP = SUMMARY ? NSW / 2 : NSW;  // state waves per column set
+  constexpr int SW = NSP < NVT ? NSP : NVT;  // state waves holding columns
   constexpr int CPW = NVT / SW;              // 16-column tiles per state wave
   constexpr int VE = 16 / sizeof(CT);
   constexpr int NFK = NFrag<CT, NKT>::value;
@@ -627,6 +644,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   constexpr int LDV = Sm::VS;
   constexpr int NST = 64 * NSW;  // state-group threads
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
+  static_assert(!SUMMARY || NSW % 2 == 0, "summary state waves come in pairs");
   static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
                     (Sm::VS * sizeof(CT)) % 64 == 32 && (Sm::TDS * sizeof(CT)) % 64 == 32,
                 "row strides");
@@ -636,7 +654,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform (scalar), so role dispatch compiles to scalar branches
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..NSW-1 state, then 2 solvers, 4 loaders
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..NSW-1 state, then 2 solvers, the loaders
   const int li = lane & 15;
   const int g = lane >> 4;
 
@@ -647,24 +665,17 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
   const int vh = L / a.nvt;  // virtual head
   const int v0 = (L % a.nvt) * BV;
   int hd = vh, t_begin = 0, T = a.T;
-  // Pass mode PM: 0 outputs (one pass, or one segment of a time-segmented
-  // pass); 1 segment summaries: no outputs, odd virtual heads start from
-  // S = I with zero values; 2 chunk-start states for the backward, no
-  // outputs. All compile-time.
-  constexpr bool SUMMARY = PM == 1;
-  constexpr bool SAVE = PM == 2;
-  constexpr bool outs = PM == 0;
-  bool ident = false;
+  // the transition half of the summary state waves (wave-uniform)
+  const bool ident = SUMMARY && w < NSP;
   const float* s0p = a.s0 ? a.s0 + (size_t)hd * D * D : nullptr;
   float* sfp = a.s_final ? a.s_final + (size_t)hd * D * D : nullptr;
   if constexpr (SUMMARY) {
-    const int sg = (vh >> 1) % a.nseg;
-    hd = (vh >> 1) / a.nseg;
-    ident = vh & 1;
+    const int sg = vh % a.nseg;
+    hd = vh / a.nseg;
     t_begin = sg * a.seg_len;
     T = a.seg_len;
     s0p = nullptr;
-    sfp = a.seg_out + ((size_t)(hd * a.nseg + sg) * 2 + (vh & 1)) * D * D;
+    sfp = a.seg_out + ((size_t)(hd * a.nseg + sg) * 2 + (ident ? 1 : 0)) * D * D;
   } else if (a.mode == 2) {
     const int sg = vh % a.nseg;
     hd = vh / a.nseg;
@@ -673,13 +684,13 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     s0p = a.seg_s0 + (size_t)(hd * a.nseg + sg) * D * D;
     sfp = (sg == a.nseg - 1 && a.s_final) ? a.s_final + (size_t)hd * D * D : nullptr;
   }
-  ident = SUMMARY && __builtin_amdgcn_readfirstlane(ident);
   const size_t tok0 = (size_t)hd * a.T + t_begin;  // first token of this sequence piece
   const int nchunks = (T + C - 1) / C;
 
   if (w < NSW) {
     // ======================= state waves =======================
-    const bool owner = w < SW;
+    const int wl = SUMMARY ? w % NSP : w;  // wave within its column set
+    const bool owner = wl < SW;
     floatx4 sacc[CPW][NKT];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -692,7 +703,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + c) + li];
+            sacc[c][rt][e] = -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li];
     }
     if (SUMMARY && owner && ident) {
 #pragma unroll
@@ -701,7 +712,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (w * CPW + c) + li) ? -1.f : 0.f;
+            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (wl * CPW + c) + li) ? -1.f : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
-              const int col = v0 + 16 * (w * CPW + cc) + li;
+              const int col = v0 + 16 * (wl * CPW + cc) + li;
               if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(-sacc[cc][rt]);
               else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = -sacc[cc][rt];
               if (a.s_chunks_n) {
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (w * CPW + cc));
+          for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (wl * CPW + cc));
         }
         // T of this chunk is ready since phase B of the previous one: its
         // fragments are requested now so T Y finds them in registers
@@ -879,7 +890,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
           if (16 * ut + li < nval) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc)
-              store4(orow + (size_t)16 * ut * D + 16 * (w * CPW + cc), -oacc[cc][ut]);
+              store4(orow + (size_t)16 * ut * D + 16 * (wl * CPW + cc), -oacc[cc][ut]);
           }
         }
       }
@@ -893,7 +904,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (w * CPW + cc) + li] = -sacc[cc][rt][e];
+            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + cc) + li] = -sacc[cc][rt][e];
     }
   } else if (w < NSW + 2) {
     // ======================= solvers (prep waves 0, 1) =======================
@@ -1117,14 +1128,12 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     else solver(std::integral_constant<int, 1>{});
   } else {
     // ======================= loaders (prep waves 2, 3) =======================
-    const int lt = tid - NST - 128;  // loader thread 0..255
+    const int lt = tid - NST - 128;  // loader thread
     const CT* kg = (const CT*)a.k + tok0 * D;
-    // without outputs the queries are not needed, and a transition run has no
-    // values: those loads read the key rows instead (same lines, no extra HBM
-    // traffic) and their tiles are not formed
-    const CT* qg = outs ? (const CT*)a.q + tok0 * D : kg;
-    const CT* vg = (SUMMARY && ident) ? kg : (const CT*)a.v + tok0 * D;
-    constexpr int NLT = 256;
+    // without outputs the queries are neither loaded nor staged
+    const CT* qg = (const CT*)a.q + tok0 * D;
+    const CT* vg = (const CT*)a.v + tok0 * D;
+    constexpr int NLT = 64 * pipe_loaders<PM>();
     constexpr int VPR = D / VE;
     constexpr int VPRV = BV / VE;
     constexpr int NLK = (C * VPR + NLT - 1) / NLT;
@@ -1154,7 +1163,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     // Row-sum layout of the key slots: slot j, lane (q, p) = (lane / VPR,
     // lane % VPR) holds piece p of row (64 w' + NLT j) / VPR + q of this wave
     // w'. Lane (q, p < NLK) computes a for slot p's row q and loads its beta.
-    const int lw = lt >> 6;        // loader wave 0..3
+    const int lw = lt >> 6;        // loader wave
     const int lq = lane / VPR, lp = lane % VPR;
     const int arow = (64 * lw + NLT * lp) / VPR + lq;  // row of this lane's a (when lp < NLK)
     // coalesced 16-byte loads of one chunk
@@ -1183,9 +1192,11 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
     auto load_qv = [&](int chunk) {
       const auto rq = chunk_rsrc(qg, chunk, 0);
       const auto rv = chunk_rsrc(vg, chunk, v0);
+      if constexpr (outs) {
 #pragma unroll
-      for (int j = 0; j < NLK; ++j)
-        if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
+        for (int j = 0; j < NLK; ++j)
+          if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
+      }
 #pragma unroll
       for (int j = 0; j < NLV; ++j)
         if (lt + NLT * j < C * VPRV) buf_load(rv, voff[j], vreg[j]);
@@ -1254,7 +1265,7 @@ __global__ __launch_bounds__(64 * (NSW + 6), 1) void efla_chunked_pipe_kernel(Ch
             if (idx < C * VPR) {
               const int r = idx / VPR, cv = idx % VPR;
               st_perm(&B.K[r][0], cv * VE, kreg[j]);
-              st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+              if constexpr (outs) st_perm(&B.Q[r][0], cv * VE, qreg[j]);
             }
           }
 #pragma unroll
@@ -1434,8 +1445,10 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
       m1.seg_len = sp.seg_len;
       m1.nseg = sp.nseg - 1;
       m1.seg_out = seg_out;
-      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 1>),
-                         dim3((unsigned)(NH * (sp.nseg - 1) * 2 * a.nvt)), dim3(64 * (NSW + 6)), 0,
+      // one workgroup per (head, segment, column slice) forms both the
+      // transition and the offset of the segment: four state waves
+      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, 4, 1>),
+                         dim3((unsigned)(NH * (sp.nseg - 1) * a.nvt)), dim3(64 * (4 + 2 + pipe_loaders<1>())), 0,
                          stream, m1);
       hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0,
                          stream, a.s0, (const float*)seg_out, seg_s0, sp.nseg);
