@@ -521,11 +521,14 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 //   U' = T diag(a) Y               (= U - W S with W = T diag(a) K, U = T diag(a) V)
 //   O^T = S^T Q^T + U'^T M^T       (read out after each update)
 //   S <- S + K^T U'
-// The state waves hold N = -S and the solvers store T' = -T diag(a) (a applied
-// in fp32), so Y = V + K N comes out of the MFMAs with the values as the
-// accumulator's start, -U' = T' Y, N <- N + K^T (-U') and
-// -O^T = N^T Q^T + (-U')^T M^T: no per-element gate or subtraction in the
-// serial pass. Outputs and states are negated back when stored.
+// In the output and summary passes the state waves hold N = -S and the
+// solvers store T' = -T diag(a) (a applied in fp32), so Y = V + K N comes out
+// of the MFMAs with the values as the accumulator's start, -U' = T' Y,
+// N <- N + K^T (-U') and -O^T = N^T Q^T + (-U')^T M^T: no per-element gate or
+// subtraction in the serial pass; outputs and the final state are negated
+// back when stored. The state-saving pass (for the backward), which stores
+// the state at every chunk, keeps S and forms Y = diag(a) (V - K S) in the
+// state waves with T unscaled.
 // Two workgroup barriers per chunk split it into phases A and B. While the
 // state waves run chunk c:
 //   state waves    A: K S, Y, U' = T Y           B: S^T Q^T, K^T U', U'^T M^T;
@@ -634,6 +637,10 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
   constexpr bool SUMMARY = PM == 1;
   constexpr bool SAVE = PM == 2;
   constexpr bool outs = PM == 0;
+  // negated form (state N = -S, T' = -T diag(a) from the solvers) where the
+  // state is not stored every chunk; the state-saving pass keeps S and
+  // applies a in the state waves, so its stores need no sign flips
+  constexpr bool NEG = PM != 2;
   constexpr int NSP = SUMMARY ? NSW / 2 : NSW;  // state waves per column set
   constexpr int SW = NSP < NVT ? NSP : NVT;  // state waves holding columns
   constexpr int CPW = NVT / SW;              // 16-column tiles per state wave
@@ -703,7 +710,8 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li];
+            sacc[c][rt][e] = NEG ? -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li]
+                                 : s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li];
     }
     if (SUMMARY && owner && ident) {
 #pragma unroll
@@ -743,11 +751,11 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (wl * CPW + cc) + li;
-              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(-sacc[cc][rt]);
-              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = -sacc[cc][rt];
+              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(sacc[cc][rt]);
+              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
               if (a.s_chunks_n) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = -sacc[cc][rt][e];
+                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
               }
             }
         }
@@ -756,7 +764,7 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
         Frag kf[NB][NFK];
-        floatx4 y[CPW][NB];
+        floatx4 al[NB], y[CPW][NB];
         // the value columns stay in their storage type until Y: converting
         // them here would make the wave wait for every read before the first
         // product (a transition run ignores them: its value buffer holds keys)
@@ -767,6 +775,7 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
           for (int f = 0; f < NFK; ++f) kf[ut][f] = MM::template ldp<NKT>(&B.K[16 * ut + li][0], f);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
+          if constexpr (!NEG) al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (wl * CPW + cc));
         }
@@ -781,15 +790,20 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
-          // Y = V - K S = V + K N, with the values as the accumulator's start
+          // negated form: Y = V - K S = V + K N, with the values as the
+          // accumulator's start; else Y = diag(a) (V - K S)
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc)
-            y[cc][ut] = (SUMMARY && ident) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
+            y[cc][ut] = (!NEG || (SUMMARY && ident)) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = MM::mma(y[cc][ut], kf[ut][f], sf[cc][f]);
             if constexpr (outs) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
+          }
+          if constexpr (!NEG) {
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (to_f32x4(vraw[cc][ut]) - y[cc][ut]);
           }
         }
         Frag yf[CPW][NFB];
@@ -904,7 +918,7 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + cc) + li] = -sacc[cc][rt][e];
+            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + cc) + li] = NEG ? -sacc[cc][rt][e] : sacc[cc][rt][e];
     }
   } else if (w < NSW + 2) {
     // ======================= solvers (prep waves 0, 1) =======================
@@ -1103,10 +1117,11 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
                     const Frag yf = MM::template acc<1>(&yv, 0);
                     x[i] = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, td, yf);
                     floatx4 xt = MM::mma(floatx4{0.f, 0.f, 0.f, 0.f}, yf, td);
-                    if constexpr (i == m) {
-                      // T' = -T diag(a): the columns of tile m are scaled by
-                      // -a in fp32 here; the tiles below inherit it through
-                      // the solve, which is linear in X_m
+                    if constexpr (i == m && NEG) {
+                      // T' = -T diag(a) for the negated form of the state
+                      // pass: the columns of tile m are scaled by -a in fp32
+                      // here; the tiles below inherit it through the solve,
+                      // which is linear in X_m
                       const float ac = -B.alpha[16 * m + li];
                       const floatx4 ar = -*(const floatx4*)&B.alpha[16 * m + 4 * g];
                       x[i] = x[i] * ac;

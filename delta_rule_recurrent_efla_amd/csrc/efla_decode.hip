@@ -12,7 +12,8 @@
 // The step is HBM-bound (0.75 flop per state byte), so the kernel is a
 // single coalesced read and write of the state: each workgroup owns a
 // 32-column slice of one head, holds it in registers between the two passes
-// and reduces the column partial sums through LDS.
+// and reduces the column partial sums by lane exchanges inside each wave and
+// through LDS across the four waves.
 
 #include "efla_device.hpp"
 
@@ -31,14 +32,19 @@ struct DecodeArgs {
 
 template <typename CT, int D, int VB>
 __global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
+  // Thread layout: lane l of wave wv reads float4 column group cg = l % CG
+  // of rows rg + RG i, rg = l / CG + (64 / CG) wv. The column partial sums
+  // are reduced over the row groups of a wave by lane exchanges, then over
+  // the four waves through LDS.
   constexpr int CG = VB / 4;               // float4 column groups per row
   constexpr int RG = 256 / CG;             // row groups
   constexpr int RPT = (D + RG - 1) / RG;   // rows per thread
   __shared__ float sk[D], sq[D], sv[VB], su[VB];
-  __shared__ floatx4 sp[RG][CG], sr[RG][CG];
+  __shared__ floatx4 sp[4][CG], sr[4][CG];
   __shared__ float slam, skq;
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int head = blockIdx.x / a.nvt;
   const int v0 = (blockIdx.x % a.nvt) * VB;
   const int cg = tid % CG, rg = tid / CG;
@@ -61,9 +67,9 @@ __global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
   if (tid < VB) sv[tid] = to_f32(vg[v0 + tid]);
   __syncthreads();
 
-  if (tid < 64) {
+  if (wv == 0) {
     float l = 0.f, kq = 0.f;
-    for (int j = tid; j < D; j += 64) {
+    for (int j = lane; j < D; j += 64) {
       l += sk[j] * sk[j];
       kq += sk[j] * sq[j];
     }
@@ -72,7 +78,7 @@ __global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
       l += __shfl_xor(l, off);
       kq += __shfl_xor(kq, off);
     }
-    if (tid == 0) {
+    if (lane == 0) {
       slam = l;
       skq = kq;
     }
@@ -86,14 +92,27 @@ __global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
       rr += sq[r] * s[i];
     }
   }
-  sp[rg][cg] = p;
-  sr[rg][cg] = rr;
+  // sum over the row groups of this wave: lanes that differ in the bits
+  // above the column-group bits
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] += __shfl_xor(p[e], off);
+      rr[e] += __shfl_xor(rr[e], off);
+    }
+  }
+  if (lane < CG) {
+    sp[wv][lane] = p;
+    sr[wv][lane] = rr;
+  }
   __syncthreads();
 
   if (tid < VB) {
     const int j = tid;
     float pj = 0.f, rj = 0.f;
-    for (int x = 0; x < RG; ++x) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
       pj += sp[x][j >> 2][j & 3];
       rj += sr[x][j >> 2][j & 3];
     }
