@@ -1145,8 +1145,10 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
     // ======================= loaders (prep waves 2, 3) =======================
     const int lt = tid - NST - 128;  // loader thread
     const CT* kg = (const CT*)a.k + tok0 * D;
-    // without outputs the queries are neither loaded nor staged
-    const CT* qg = (const CT*)a.q + tok0 * D;
+    // without outputs the queries are not needed: those loads read the key
+    // rows instead (same lines, no extra HBM traffic; measured, skipping
+    // them altogether made the state-saving pass slower) and are not used
+    const CT* qg = outs ? (const CT*)a.q + tok0 * D : kg;
     const CT* vg = (const CT*)a.v + tok0 * D;
     constexpr int NLT = 64 * pipe_loaders<PM>();
     constexpr int VPR = D / VE;
@@ -1207,11 +1209,9 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
     auto load_qv = [&](int chunk) {
       const auto rq = chunk_rsrc(qg, chunk, 0);
       const auto rv = chunk_rsrc(vg, chunk, v0);
-      if constexpr (outs) {
 #pragma unroll
-        for (int j = 0; j < NLK; ++j)
-          if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
-      }
+      for (int j = 0; j < NLK; ++j)
+        if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
 #pragma unroll
       for (int j = 0; j < NLV; ++j)
         if (lt + NLT * j < C * VPRV) buf_load(rv, voff[j], vreg[j]);
@@ -1280,7 +1280,7 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
             if (idx < C * VPR) {
               const int r = idx / VPR, cv = idx % VPR;
               st_perm(&B.K[r][0], cv * VE, kreg[j]);
-              if constexpr (outs) st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+              st_perm(&B.Q[r][0], cv * VE, qreg[j]);
             }
           }
 #pragma unroll
