@@ -48,18 +48,19 @@ struct ChunkedArgs {
   float* s_final;
   int T;
   int nvt;  // state column slices per head
-  // Time-segmented passes (pipelined kernel only). mode 0: one pass over the
-  // whole sequence per head. mode 1: per head and segment g < nseg of seg_len
-  // tokens, the segment's affine map S_end = P_g S_start + R_g: virtual head
-  // 2 (h nseg + g) + kind runs the segment from S = 0 with the values
-  // (kind 0, gives R_g) or from S = I with zero values (kind 1, gives P_g),
-  // writes no outputs and stores S_end to seg_out[(h nseg + g) 2 + kind].
-  // mode 2: virtual head h nseg + g runs segment g from seg_s0[h nseg + g]
-  // and writes its outputs; the last segment writes s_final.
+  // Time-segmented passes (pipelined kernel only), over nseg segments of
+  // seg_len tokens. mode 0: one pass over the whole sequence per head.
+  // mode 1 (pass mode 1): the affine maps S_end = P_g S_start + R_g of
+  // segments g = 1 .. nseg - 2; virtual head h nrun + j (nrun = nseg - 2)
+  // handles segment j + 1 and stores R_g to seg_out[(h nrun + j) 2] and P_g
+  // to seg_out[(h nrun + j) 2 + 1]. mode 2: virtual head h nrun + j runs
+  // segment g = seg_first + j from its start state (S0 for g = 0, else
+  // seg_s0[h nseg + g]) and writes its outputs; segment 0 stores its end
+  // state to seg_s0[h nseg + 1], the last segment writes s_final.
   int mode;
   int seg_len;
   int nseg;
-  const float* seg_s0;
+  float* seg_s0;  // segment start states (workspace; segment 0 writes slot 1)
   float* seg_out;
   int coef;  // step coefficient rule (gate_coef)
   // pass mode 2 of the pipelined kernel (states for the backward): the state
@@ -68,6 +69,8 @@ struct ChunkedArgs {
   // s_chunks_n is not null, [head][chunk][d_k][d_v] fp32 (natural)
   float* s_chunks;
   float* s_chunks_n;
+  int seg_first;  // mode 2: first segment of this launch
+  int nrun;       // modes 1 and 2: segments per head in this launch
 };
 
 template <typename CT>
@@ -619,8 +622,10 @@ constexpr int pipe_loaders() {
   return PM == 1 ? 2 : 4;
 }
 
+// The pipelined chunk pass of one workgroup: L is its index among the
+// workgroups of the pass (head-major, column slices adjacent).
 template <typename CT, int D, int C, int BV, int NSW, int PM>
-__global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
+__device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, C, BV>& sm, const int L) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
   using Vec = typename Vec16<CT>::type;
@@ -656,8 +661,6 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
                     (Sm::VS * sizeof(CT)) % 64 == 32 && (Sm::TDS * sizeof(CT)) % 64 == 32,
                 "row strides");
 
-  __shared__ Sm sm;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave-uniform (scalar), so role dispatch compiles to scalar branches
@@ -665,10 +668,6 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
   const int li = lane & 15;
   const int g = lane >> 4;
 
-  int L = blockIdx.x;
-  const int total = gridDim.x;
-  if (total % 8 == 0 && ((total / 8) % a.nvt) == 0)
-    L = (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
   const int vh = L / a.nvt;  // virtual head
   const int v0 = (L % a.nvt) * BV;
   int hd = vh, t_begin = 0, T = a.T;
@@ -677,19 +676,25 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
   const float* s0p = a.s0 ? a.s0 + (size_t)hd * D * D : nullptr;
   float* sfp = a.s_final ? a.s_final + (size_t)hd * D * D : nullptr;
   if constexpr (SUMMARY) {
-    const int sg = vh % a.nseg;
-    hd = vh / a.nseg;
-    t_begin = sg * a.seg_len;
+    // segments 1 .. nseg - 2 (whole segments), summary j = segment j + 1
+    const int j = vh % a.nrun;
+    hd = vh / a.nrun;
+    t_begin = (j + 1) * a.seg_len;
     T = a.seg_len;
     s0p = nullptr;
-    sfp = a.seg_out + ((size_t)(hd * a.nseg + sg) * 2 + (ident ? 1 : 0)) * D * D;
+    sfp = a.seg_out + ((size_t)(hd * a.nrun + j) * 2 + (ident ? 1 : 0)) * D * D;
   } else if (a.mode == 2) {
-    const int sg = vh % a.nseg;
-    hd = vh / a.nseg;
+    // segments seg_first .. seg_first + nrun - 1; segment 0 starts from S0
+    // and leaves its end state as the start of segment 1, the last segment
+    // writes S_T
+    const int sg = a.seg_first + vh % a.nrun;
+    hd = vh / a.nrun;
     t_begin = sg * a.seg_len;
     T = min(a.seg_len, a.T - t_begin);
-    s0p = a.seg_s0 + (size_t)(hd * a.nseg + sg) * D * D;
-    sfp = (sg == a.nseg - 1 && a.s_final) ? a.s_final + (size_t)hd * D * D : nullptr;
+    s0p = sg == 0 ? (a.s0 ? a.s0 + (size_t)hd * D * D : nullptr)
+                  : a.seg_s0 + (size_t)(hd * a.nseg + sg) * D * D;
+    sfp = sg == a.nseg - 1 ? (a.s_final ? a.s_final + (size_t)hd * D * D : nullptr)
+                           : (sg == 0 ? a.seg_s0 + (size_t)(hd * a.nseg + 1) * D * D : nullptr);
   }
   const size_t tok0 = (size_t)hd * a.T + t_begin;  // first token of this sequence piece
   const int nchunks = (T + C - 1) / C;
@@ -1318,15 +1323,42 @@ __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_c
   }
 }
 
+// Workgroup -> pass index with the column slices of a head on one XCD (the
+// hardware deals workgroups to the 8 XCDs round robin): the slices read the
+// same keys and queries, which then come from that XCD's L2.
+__device__ __forceinline__ int xcd_slot(int nvt) {
+  const int total = gridDim.x;
+  if (total % 8 == 0 && ((total / 8) % nvt) == 0) return (blockIdx.x % 8) * (total / 8) + blockIdx.x / 8;
+  return blockIdx.x;
+}
+
+template <typename CT, int D, int C, int BV, int NSW, int PM>
+__global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
+  __shared__ PipeSmem<CT, D, C, BV> sm;
+  pipe_body<CT, D, C, BV, NSW, PM>(a, sm, xcd_slot(a.nvt));
+}
+
+// First launch of the time-segmented forward: the summaries of segments
+// 1 .. nseg - 2 (pass mode 1, first nsum workgroups) and the outputs of
+// segment 0, which starts from S0 and needs no carry (pass mode 0, the rest).
+// Both run 8 waves of 64 lanes on one shared-memory layout.
+template <typename CT, int D, int C, int BV>
+__global__ __launch_bounds__(512, 1) void efla_seg_first_kernel(ChunkedArgs summ, ChunkedArgs first, int nsum) {
+  __shared__ PipeSmem<CT, D, C, BV> sm;
+  const int L = xcd_slot(summ.nvt);
+  if (L < nsum) pipe_body<CT, D, C, BV, 4, 1>(summ, sm, L);
+  else pipe_body<CT, D, C, BV, 2, 0>(first, sm, L - nsum);
+}
+
 // ---------------------------------------------------------------------------
 // Carry of the time-segmented forward: per head, the start state of every
-// segment, S_start(0) = S0 (zeros without one) and
-// S_start(g + 1) = P_g S_start(g) + R_g, in fp32. One workgroup per (head,
-// 16-column slice of S): the columns of S evolve independently, so the
-// slices need no exchange. P_g is staged in LDS each step.
+// segment from the second on, S_start(1) = the end state of segment 0 (left
+// in seg_s0 by the first launch) and S_start(g + 1) = P_g S_start(g) + R_g
+// for g = 1 .. nseg - 2, in fp32. One workgroup per (head, 16-column slice
+// of S): the columns of S evolve independently, so the slices need no
+// exchange. P_g is staged in LDS each step.
 template <int D>
-__global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, const float* seg_out,
-                                                             float* seg_s0, int nseg) {
+__global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* seg_out, float* seg_s0, int nseg) {
   // fp32 MFMA (16x16x4): lane (g, i) of a 16x16 tile product takes
   // A[i][k] and B[k][i] for the four k values 16q + 4g + s of k-block q
   // (s = 0..3: one MFMA each) from one 16-byte read of a row of P and of a
@@ -1341,15 +1373,16 @@ __global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, co
   const int j0 = (blockIdx.x % (D / 16)) * 16;
   for (int i = tid; i < D * 16; i += 256) {
     const int r = i / 16, c = i % 16;
-    St[c][r] = s0 ? s0[((size_t)h * D + r) * D + j0 + c] : 0.f;
+    St[c][r] = seg_s0[((size_t)(h * nseg + 1) * D + r) * D + j0 + c];
   }
   __syncthreads();
   // P_g and this lane's R_g values are fetched into registers one step ahead
   constexpr int NPL = (D * D / 4 + 255) / 256;  // 16-byte pieces of P per thread
   constexpr int NT = (D / 16 + 3) / 4;  // 16-row tiles per wave
   floatx4 pr[NPL], rr[NT];
-  auto fetch = [&](int gs) {
-    const float* R = seg_out + ((size_t)(h * (nseg - 1) + gs) * 2) * D * D;
+  // maps of segments 1 .. nseg - 2, map j = segment j + 1
+  auto fetch = [&](int m) {
+    const float* R = seg_out + ((size_t)(h * (nseg - 2) + m) * 2) * D * D;
     const float* Pg = R + (size_t)D * D;
 #pragma unroll
     for (int j = 0; j < NPL; ++j)
@@ -1363,12 +1396,14 @@ __global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, co
       }
     }
   };
-  if (nseg > 1) fetch(0);
-  for (int gs = 0; gs < nseg; ++gs) {
-    float* dst = seg_s0 + ((size_t)h * nseg + gs) * D * D;
-    for (int i = tid; i < D * 16; i += 256) {
-      const int r = i / 16, c = i % 16;
-      dst[(size_t)r * D + j0 + c] = St[c][r];
+  fetch(0);
+  for (int gs = 1; gs < nseg; ++gs) {
+    if (gs > 1) {
+      float* dst = seg_s0 + ((size_t)h * nseg + gs) * D * D;
+      for (int i = tid; i < D * 16; i += 256) {
+        const int r = i / 16, c = i % 16;
+        dst[(size_t)r * D + j0 + c] = St[c][r];
+      }
     }
     if (gs == nseg - 1) break;
 #pragma unroll
@@ -1380,7 +1415,7 @@ __global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, co
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] = rr[tt];
     __syncthreads();
-    if (gs + 1 < nseg - 1) fetch(gs + 1);
+    if (gs + 1 < nseg - 1) fetch(gs);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const int t = w + 4 * tt;
@@ -1408,9 +1443,11 @@ __global__ __launch_bounds__(256) void efla_seg_carry_kernel(const float* s0, co
 
 // When a plain pass would leave most of the GPU idle (few heads, long
 // sequences), the forward runs as three launches over nseg time segments:
-// the segments' affine maps (mode 1, all segments at once), the carry, then
-// every segment's outputs from its true start state (mode 2). About three
-// times the arithmetic of one pass, spread over ~nseg times more workgroups.
+// the affine maps of segments 1 .. nseg - 2 together with the outputs of
+// segment 0 (which starts from S0), the carry, then the outputs of segments
+// 1 .. nseg - 1 from their true start states. About three times the state
+// arithmetic of one pass, spread over ~nseg times more workgroups; with W
+// workgroups per pass both big launches have W (nseg - 1) workgroups.
 struct SegPlan {
   int nseg = 1;
   int seg_len = 0;
@@ -1422,7 +1459,7 @@ static SegPlan seg_plan(int NH, int T, int d, int C, bool pipelined) {
   const long long W = (long long)NH * (d / (d < 64 ? d : 64));  // workgroups of one pass
   const int nchunks = (T + C - 1) / C;
   if (W >= 128 || nchunks < 64) return p;
-  const long long G = std::min<long long>(256 / W, nchunks / 32);  // segments of >= 32 chunks
+  const long long G = std::min<long long>(256 / W + 1, nchunks / 32);  // segments of >= 32 chunks
   if (G < 2) return p;
   const int cps = (int)((nchunks + G - 1) / G);  // chunks per segment
   p.seg_len = cps * C;
@@ -1431,9 +1468,11 @@ static SegPlan seg_plan(int NH, int T, int d, int C, bool pipelined) {
   return p;
 }
 
+// Workspace: the maps (R_g, P_g) of segments 1 .. nseg - 2, then the start
+// states of all segments (slot 0 unused).
 static size_t seg_workspace_bytes(const SegPlan& p, int NH, int d) {
   if (p.nseg < 2) return 0;
-  return (size_t)NH * (3 * (size_t)p.nseg - 2) * d * d * sizeof(float);
+  return (size_t)NH * (3 * (size_t)p.nseg - 4) * d * d * sizeof(float);
 }
 
 // ---------------------------------------------------------------------------
@@ -1453,27 +1492,38 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
     constexpr int NSW = EFLA_PIPE_STATE_WAVES;
     const SegPlan sp = seg_plan(NH, a.T, D, C, true);
     if (sp.nseg >= 2) {
+      static_assert(NSW == 2, "the first segmented launch runs the two-state-wave output pass");
+      const int ns = sp.nseg;
       float* seg_out = (float*)ws;
-      float* seg_s0 = seg_out + (size_t)NH * (sp.nseg - 1) * 2 * D * D;
-      ChunkedArgs m1 = a;
+      float* seg_s0 = seg_out + (size_t)NH * (ns - 2) * 2 * D * D;
+      ChunkedArgs m1 = a;  // maps of segments 1 .. ns - 2
       m1.mode = 1;
       m1.seg_len = sp.seg_len;
-      m1.nseg = sp.nseg - 1;
+      m1.nseg = ns;
+      m1.nrun = ns - 2;
       m1.seg_out = seg_out;
-      // one workgroup per (head, segment, column slice) forms both the
-      // transition and the offset of the segment: four state waves
-      hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, 4, 1>),
-                         dim3((unsigned)(NH * (sp.nseg - 1) * a.nvt)), dim3(64 * (4 + 2 + pipe_loaders<1>())), 0,
-                         stream, m1);
-      hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0,
-                         stream, a.s0, (const float*)seg_out, seg_s0, sp.nseg);
-      ChunkedArgs m2 = a;
+      ChunkedArgs m0 = a;  // outputs of segment 0
+      m0.mode = 2;
+      m0.seg_len = sp.seg_len;
+      m0.nseg = ns;
+      m0.seg_first = 0;
+      m0.nrun = 1;
+      m0.seg_s0 = seg_s0;
+      const int nsum = NH * (ns - 2) * a.nvt;
+      hipLaunchKernelGGL((efla_seg_first_kernel<CT, D, C, BV>), dim3((unsigned)(nsum + NH * a.nvt)), dim3(512), 0,
+                         stream, m1, m0, nsum);
+      if (ns >= 3)
+        hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0, stream,
+                           (const float*)seg_out, seg_s0, ns);
+      ChunkedArgs m2 = a;  // outputs of segments 1 .. ns - 1
       m2.mode = 2;
       m2.seg_len = sp.seg_len;
-      m2.nseg = sp.nseg;
+      m2.nseg = ns;
+      m2.seg_first = 1;
+      m2.nrun = ns - 1;
       m2.seg_s0 = seg_s0;
       hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 0>),
-                         dim3((unsigned)(NH * sp.nseg * a.nvt)), dim3(64 * (NSW + 6)), 0, stream, m2);
+                         dim3((unsigned)(NH * (ns - 1) * a.nvt)), dim3(64 * (NSW + 6)), 0, stream, m2);
       return hipGetLastError();
     }
     hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 0>), grid, dim3(64 * (NSW + 6)), 0,
