@@ -102,11 +102,15 @@ def test_workspace_query():
     assert lib.efla_fwd_chunked_workspace_bytes(8, 16, 4096, 128, 128, 64, 1) == 0    # 256 workgroups
     assert lib.efla_fwd_chunked_workspace_bytes(16, 8, 2048, 128, 128, 64, 1) == 0
     # few heads, long sequence: time segments. 16 heads x 2 column slices = 32
-    # workgroups -> 8 segments of 128 chunks; per head and segment the map
-    # (P, R) for all but the last segment plus every start state
-    nseg = 8
+    # workgroups -> 9 segments of 114 chunks (both big launches hold
+    # 32 x 8 = 256 workgroups); per head the maps (P, R) of segments
+    # 1 .. nseg - 2 plus a start state slot per segment
+    nseg = 9
     assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 64, 1) == \
-        16 * (3 * nseg - 2) * 128 * 128 * 4
+        16 * (2 * (nseg - 2) + nseg) * 128 * 128 * 4
+    # two segments: no maps, only the start states
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4133, 128, 128, 64, 1) == \
+        2 * 2 * 128 * 128 * 4
     # unsupported or invalid sizes report 0
     assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 48, 1) == 0
     assert lib.efla_fwd_chunked_workspace_bytes(0, 16, 65536, 128, 128, 64, 1) == 0
