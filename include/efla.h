@@ -81,11 +81,13 @@ typedef enum {
  * Bytes of device workspace efla_fwd_chunked needs for these sizes. It is 0
  * when one pass over the sequence fills the GPU. For few heads and long
  * sequences (fewer than 128 workgroups of 64 state columns, and at least 64
- * chunks; segments of at least 32 chunks) the forward runs over time segments: the affine map S -> P S + R of
- * every segment, then their composition, then each segment from its true start
- * state (the chunk recurrence is affine in S, section 整体框架 of the
- * papernotes note); the workspace then holds, per head and segment, the map
- * (P, R) and the start state: B H (3 nseg - 2) d_k d_v fp32 values.
+ * chunks; segments of at least 32 chunks) the forward runs over nseg time
+ * segments: the first segment from S0 beside the affine maps S -> P S + R of
+ * segments 1 .. nseg - 2, then their composition, then every later segment
+ * from its true start state (the chunk recurrence is affine in S, section
+ * 整体框架 of the papernotes note); the workspace then holds, per head, those
+ * maps (P, R) and a start state per segment: B H (3 nseg - 4) d_k d_v fp32
+ * values.
  * Returns 0 for unsupported sizes as well; efla_fwd_chunked reports those.
  */
 size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, int chunk,
