@@ -95,6 +95,21 @@ def test_chunked_edge_lengths(efla, dt, d, T):
     assert normwise(o, o_ref) <= tol and normwise(sT, s_ref) <= tol
 
 
+# fp32 with C = 64 at d <= 64 runs the 4-wave kernel: with 16-column state
+# slices when 64-column slices would leave CUs idle, with the wide slices when
+# there are enough heads; both layouts against the oracle
+@pytest.mark.parametrize("d,B,H", [(64, 2, 3), (64, 16, 16), (32, 16, 16)])
+def test_fp32_fallback_slices(efla, d, B, H):
+    T = 70
+    note(f"[fp32 4-wave kernel] d={d} chunk=64 B={B} H={H} T={T}")
+    x = efla_inputs.random_case(2024 + d + B, B=B, H=H, T=T, d=d, dtype="f32", s0_std=0.4)
+    o, sT = run_chunked(efla, x, 64, x["s0"])
+    o_ref, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"], nthreads=8)
+    eo, es = normwise(o, o_ref), normwise(sT, s_ref)
+    note(f"   err o={eo:.3e} S_T={es:.3e} (tol {TOL[DT['f32']]})")
+    assert eo <= TOL[DT["f32"]] and es <= TOL[DT["f32"]]
+
+
 # ------------------------------------------------------------ time segments
 # Few heads and long sequences run as segment maps + carry + per-segment
 # passes. These shapes trigger it (the workspace query says so) at sizes the
