@@ -615,8 +615,8 @@ __host__ __device__ constexpr int t_first(int pw) {
 }
 
 
-// Loader waves of a pass mode: the segment summaries (mode 1) stage no queries
-// and form no M, so two loaders serve them.
+// Loader waves of a pass mode: the segment summaries (mode 1) form no M, so
+// two loaders serve them and the other waves hold state columns.
 template <int PM>
 constexpr int pipe_loaders() {
   return PM == 1 ? 2 : 4;
