@@ -1010,29 +1010,88 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   auto mma = [](bf16x8 x, bf16x8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0); };
 
-  // ---- K, Q, dO and G rows (zero past T), c
-  for (int i = tid; i < C * D / 8; i += 64 * NWV) {
-    const int r = i / (D / 8), c8 = 8 * (i % (D / 8));
-    bf16x8 kx = {}, qx = {}, ox = {}, gx = {};
-    if (r < nval) {
-      kx = *(const bf16x8*)(kg + (size_t)r * D + c8);
-      qx = *(const bf16x8*)(qg + (size_t)r * D + c8);
-      ox = *(const bf16x8*)(dog + (size_t)r * D + c8);
-      gx = pk8(cv4(ld4(G + (size_t)r * D + c8)), cv4(ld4(G + (size_t)r * D + c8 + 4)));
+  static_assert(NKT <= NWV, "one v tile per wave in the Yh^T and dQ/dK phases");
+  // ---- K, Q, dO and G rows (zero past T), c: every load is issued before
+  //      the first LDS write
+  constexpr int NIT = (C * D / 8 + 64 * NWV - 1) / (64 * NWV);
+  bf16x8 kx[NIT], qx[NIT], ox[NIT];
+  floatx4 gx0[NIT], gx1[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+    kx[it] = qx[it] = ox[it] = bf16x8{};
+    gx0[it] = gx1[it] = z;
+    if (i < C * D / 8 && r < nval) {
+      kx[it] = *(const bf16x8*)(kg + (size_t)r * D + c8);
+      qx[it] = *(const bf16x8*)(qg + (size_t)r * D + c8);
+      ox[it] = *(const bf16x8*)(dog + (size_t)r * D + c8);
+      gx0[it] = ld4(G + (size_t)r * D + c8);
+      gx1[it] = ld4(G + (size_t)r * D + c8 + 4);
     }
-    st_perm(&sm.Kb[r][0], c8, kx);
-    st_perm(&sm.Qb[r][0], c8, qx);
-    st_perm(&sm.dOb[r][0], c8, ox);
-    st_perm(&sm.Gb[r][0], c8, gx);
+  }
+  // ---- the global operands of every later phase, requested now so that
+  //      their latency overlaps the staging instead of following a barrier:
+  //      Yh^T phase (v tile w): rows of -S^T, and V, G at (token, v);
+  //      U^T phase (token tile w % NB): rows of T; dM/E phase: Gram tiles;
+  //      dQ/dK phase (key tile w): rows of S and of dS'
+  const bool vt = w < NKT;
+  const int I1 = w, I2 = w % NB;
+  bf16x8 stf[KD], snf[KD], dsf[KD];
+  float vpre[NB][4], gpre[NB][4];
+  if (vt) {
+    bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * I1 + li) * D + k0]); });
+#pragma unroll
+    for (int J = 0; J < NB; ++J)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * J + 4 * g + e, v = 16 * I1 + li;
+        const bool ok = r < nval;
+        vpre[J][e] = ok ? (float)vg[(size_t)r * D + v] : 0.f;
+        gpre[J][e] = ok ? G[(size_t)r * D + v] : 0.f;
+      }
+    const int cj = 16 * I1 + li;
+    bf_frags<D>(snf, [&](int k0) {
+      floatx4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = ld1(&St[(size_t)(k0 + e) * D + cj]);
+      return x;
+    });
+    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+  }
+  floatx4 tpre[2 * KC];
+  {
+    const float* Tn = a.tn + mb;
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb) {
+      tpre[2 * kb] = ld4(&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 4 * g]);
+      tpre[2 * kb + 1] = ld4(&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 16 + 4 * g]);
+    }
+  }
+  constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
+  floatx4 grp[NJ3];
+#pragma unroll
+  for (int m = 0; m < NJ3; ++m) {
+    const int J = w / NB + JS * m;
+    grp[m] = (J < NB && J <= I2) ? ld4(a.gram + mb + (size_t)(16 * I2 + li) * C + 16 * J + 4 * g) : z;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+    if (i < C * D / 8) {
+      st_perm(&sm.Kb[r][0], c8, kx[it]);
+      st_perm(&sm.Qb[r][0], c8, qx[it]);
+      st_perm(&sm.dOb[r][0], c8, ox[it]);
+      st_perm(&sm.Gb[r][0], c8, pk8(cv4(gx0[it]), cv4(gx1[it])));
+    }
   }
   if (tid < C) sm.al[tid] = a.al[rb + tid];
   __syncthreads();
 
   // ---- Yh^T tiles (v tile I, token tile J): acc[e] = -(K S)[16 J + 4g + e][16 I + li];
   //      then + V, rowsum(G * Yh) over the tile's 16 v, stored as rows of Yh^T
-  for (int I = w; I < NKT; I += NWV) {
-    bf16x8 stf[KD];
-    bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * I + li) * D + k0]); });
+  if (vt) {
+    const int I = I1;
+#pragma unroll
     for (int J = 0; J < NB; ++J) {
       floatx4 acc = z;
 #pragma unroll
@@ -1040,10 +1099,8 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       floatx4 gy;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * J + 4 * g + e, v = 16 * I + li;
-        const bool ok = r < nval;
-        acc[e] += ok ? (float)vg[(size_t)r * D + v] : 0.f;
-        gy[e] = group_sum<16>(ok ? G[(size_t)r * D + v] * acc[e] : 0.f);
+        acc[e] += vpre[J][e];
+        gy[e] = group_sum<16>(gpre[J][e] * acc[e]);
       }
       if (li < 4) sm.dcp[16 * J + 4 * g + li][I] = gy[li];
       MM::store_tp(&sm.YTb[16 * I + li][0], J, acc);
@@ -1054,12 +1111,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   // ---- U^T tiles (token tile I, v tile J): acc[e] = U[16 I + li][16 J + 4g + e];
   //      B(j, i) = T[i][j] c_j, row i of T D, formed once per wave
   {
-    const int I = w % NB;
-    const float* Tn = a.tn + mb;
+    const int I = I2;
     bf16x8 tdf[KC];
-    bf_frags<C>(tdf, [&](int k0) {
-      return ld4(&Tn[(size_t)(16 * I + li) * C + k0]) * *(const floatx4*)&sm.al[k0];
-    });
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb)
+      tdf[kb] = pk8(cv4(tpre[2 * kb] * *(const floatx4*)&sm.al[32 * kb + 4 * g]),
+                    cv4(tpre[2 * kb + 1] * *(const floatx4*)&sm.al[32 * kb + 16 + 4 * g]));
     for (int J = w / NB; J < NKT; J += NWV / NB) {
       floatx4 acc = z;
 #pragma unroll
@@ -1073,7 +1130,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   //      (dO U^T)[16 I + li][16 J + 4g + e], and the same with -G; X = D E;
   //      rowsum(E * K K^T) over the tile's 16 columns
   {
-    const int I = w % NB;
+    const int I = I2;
     const float ci = sm.al[16 * I + li];
     bf16x8 dof[KD], gf[KD];
 #pragma unroll
@@ -1081,7 +1138,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       dof[kb] = MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb);
       gf[kb] = MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb);
     }
-    for (int J = w / NB; J < NB; J += NWV / NB) {
+#pragma unroll
+    for (int jm = 0; jm < NJ3; ++jm) {
+      const int J = w / NB + JS * jm;
+      if (J >= NB) break;
       floatx4 m = z, e4 = z;
       float s = 0.f;
       if (J <= I) {
@@ -1091,7 +1151,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
           m = mma(u, dof[kb], m);
           e4 = mma(u, gf[kb], e4);
         }
-        const floatx4 gr = ld4(a.gram + mb + (size_t)(16 * I + li) * C + 16 * J + 4 * g);
+        const floatx4 gr = grp[jm];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * I + li, j = 16 * J + 4 * g + e;
@@ -1127,16 +1187,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   //      row J of S, dS' (over v) and of columns J of K, Q (over tokens) once
   bf16* dqg = (bf16*)a.dq + ((size_t)h * a.T + t0) * D;
   bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
-  for (int J = w; J < NKT; J += NWV) {
+  if (vt) {
+    const int J = I1;
     const int cj = 16 * J + li;
-    bf16x8 snf[KD], dsf[KD], ktf[KC], qtf[KC];
-    bf_frags<D>(snf, [&](int k0) {
-      floatx4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = ld1(&St[(size_t)(k0 + e) * D + cj]);
-      return x;
-    });
-    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+    bf16x8 ktf[KC], qtf[KC];
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
       ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
