@@ -169,44 +169,69 @@ struct BwdArgs {
 // 2. Per (head, chunk): scalars, K K^T, T = (I + A)^{-1}, T^T, M^T.
 template <typename CT, int D, int C>
 __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
-  constexpr int LD = D + 4, LC = C + 4;
-  constexpr int LQ = LD > LC ? LD : LC;
-  // K rows, then (after the Gram tiles) T, C x LC
-  __shared__ __attribute__((aligned(16))) float Kf[C][LQ];
-  // Q rows, then (after the Q K^T tiles) strictly-lower D K K^T, C x LC
-  __shared__ __attribute__((aligned(16))) float Qf[C][LQ];
-  auto Am = [&](int i, int j) -> float& { return Qf[0][i * LC + j]; };
-  auto Ts = [&](int i, int j) -> float& { return Kf[0][i * LC + j]; };
+  // M^T and T^T are stored as bf16 where their only reader rounds them to bf16
+  // (the bf16 form of the state pass), else as fp32
+  constexpr bool MBF = sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0;
+  // K and Q rows are staged in the input type where the products take them as
+  // bf16 MFMA operands (the smaller footprint lets more workgroups share a
+  // CU), else in fp32; A and T (fp32, row stride LC) reuse their space
+  using LT = std::conditional_t<MBF, bf16, float>;
+  constexpr int LC = C + 4;
+  constexpr int LK = MBF ? D + 16 : D + 4;  // bf16 rows: 32 bytes mod 64
+  constexpr int LQ = LK * (int)sizeof(LT) >= LC * 4 ? LK : (LC * 4 + (int)sizeof(LT) - 1) / (int)sizeof(LT);
+  // K rows, then (after the Gram tiles) T
+  __shared__ __attribute__((aligned(16))) LT Kf[C][LQ];
+  // Q rows, then (after the Q K^T tiles) strictly-lower D K K^T
+  __shared__ __attribute__((aligned(16))) LT Qf[C][LQ];
+  auto Am = [&](int i, int j) -> float& { return ((float*)&Qf[0][0])[i * LC + j]; };
+  auto Ts = [&](int i, int j) -> float& { return ((float*)&Kf[0][0])[i * LC + j]; };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
   const int t0 = ch * C, nval = min(C, a.T - t0);
   const CT* kg = (const CT*)a.k + ((size_t)h * a.T + t0) * D;
   const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
-  // M^T and T^T are stored as bf16 where their only reader rounds them to bf16
-  // (the bf16 form of the state pass), else as fp32
-  constexpr bool MBF = sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0;
-  for (int i = tid; i < C * D / 4; i += 256) {
-    const int r = i / (D / 4), c4 = 4 * (i % (D / 4));
-    const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-    *(floatx4*)&Kf[r][c4] = r < nval ? ld4(kg + (size_t)r * D + c4) : z4;
-    *(floatx4*)&Qf[r][c4] = r < nval ? ld4(qg + (size_t)r * D + c4) : z4;
+  constexpr int VE = 16 / (int)sizeof(LT);  // elements per 16-byte piece
+  using Piece = std::conditional_t<MBF, bf16x8, floatx4>;
+  for (int i = tid; i < C * D / VE; i += 256) {
+    const int r = i / (D / VE), c = VE * (i % (D / VE));
+    if constexpr (MBF) {
+      const bf16x8 z8 = {};
+      *(bf16x8*)&Kf[r][c] = r < nval ? *(const bf16x8*)(kg + (size_t)r * D + c) : z8;
+      *(bf16x8*)&Qf[r][c] = r < nval ? *(const bf16x8*)(qg + (size_t)r * D + c) : z8;
+    } else {
+      const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+      *(floatx4*)&Kf[r][c] = r < nval ? ld4(kg + (size_t)r * D + c) : z4;
+      *(floatx4*)&Qf[r][c] = r < nval ? ld4(qg + (size_t)r * D + c) : z4;
+    }
   }
   __syncthreads();
   const size_t rb = (size_t)h * a.nc * C + t0;  // row base of this chunk
   __shared__ float cs[C];
-  if (tid < C) {
+  {
+    // lambda of row tid / 4: four lanes sum every fourth 16-byte piece
+    const int r = tid >> 2, part = tid & 3;
     float lam = 0.f;
-    for (int col = 0; col < D; ++col) lam = fmaf(Kf[tid][col], Kf[tid][col], lam);
-    float c = 0.f, db = 0.f, dl = 0.f;
-    if (tid < nval) {
-      const float b = ld1((const CT*)a.beta + (size_t)h * a.T + t0 + tid);
-      c = gate_coef(a.coef, b, lam);
-      gate_coef_grad(a.coef, b, lam, db, dl);
+    if (r < C) {
+      for (int pc = part; pc < D / VE; pc += 4) {
+        const Piece x = *(const Piece*)&Kf[r][VE * pc];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) lam = fmaf((float)x[e], (float)x[e], lam);
+      }
     }
-    cs[tid] = c;
-    a.al[rb + tid] = c;
-    a.fb[rb + tid] = db;
-    a.fl[rb + tid] = dl;
+    lam += __shfl_xor(lam, 1);
+    lam += __shfl_xor(lam, 2);
+    if (r < C && part == 0) {
+      float c = 0.f, db = 0.f, dl = 0.f;
+      if (r < nval) {
+        const float b = ld1((const CT*)a.beta + (size_t)h * a.T + t0 + r);
+        c = gate_coef(a.coef, b, lam);
+        gate_coef_grad(a.coef, b, lam, db, dl);
+      }
+      cs[r] = c;
+      a.al[rb + r] = c;
+      a.fb[rb + r] = db;
+      a.fl[rb + r] = dl;
+    }
   }
   __syncthreads();
   const size_t mb = ((size_t)h * a.nc + ch) * C * C;
@@ -219,8 +244,8 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
     const int I = tl / NT, J = tl % NT;
     // bf16 inputs: products of bf16 values are exact in fp32, so the bf16 MFMA
     // gives the same K K^T and Q K^T as the fp32 one
-    const floatx4 kq = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; },
-                                               [&](int k0) { return *(const floatx4*)&Qf[16 * I + li][k0]; });
+    const floatx4 kq = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * J + li][k0]); },
+                                               [&](int k0) { return ld4(&Qf[16 * I + li][k0]); });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = 16 * J + 4 * g + e, i = 16 * I + li;
@@ -233,8 +258,8 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   __syncthreads();  // Q is dead: its space takes A
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
-    const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return *(const floatx4*)&Kf[16 * I + li][k0]; },
-                                               [&](int k0) { return *(const floatx4*)&Kf[16 * J + li][k0]; });
+    const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * I + li][k0]); },
+                                               [&](int k0) { return ld4(&Kf[16 * J + li][k0]); });
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * I + 4 * g + e, j = 16 * J + li;
@@ -981,7 +1006,7 @@ struct GradSmemBf {
       bf16 Xb[C][LC];   // D E
     } m;
   };
-  float al[C], dc[C];
+  float al[C], dc[C], fl[C];
   float dcp[C][D / 16 + 1];   // rowsum(G * Yh) over one 16-column tile of v
   float dcp2[C][C / 16 + 1];  // rowsum(E * K K^T) over one 16-column tile
 };
@@ -1084,7 +1109,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       st_perm(&sm.Gb[r][0], c8, pk8(cv4(gx0[it]), cv4(gx1[it])));
     }
   }
-  if (tid < C) sm.al[tid] = a.al[rb + tid];
+  float fbt = 0.f;
+  if (tid < C) {
+    sm.al[tid] = a.al[rb + tid];
+    sm.fl[tid] = a.fl[rb + tid];
+    fbt = a.fb[rb + tid];
+  }
   __syncthreads();
 
   // ---- Yh^T tiles (v tile I, token tile J): acc[e] = -(K S)[16 J + 4g + e][16 I + li];
@@ -1178,7 +1208,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
 #pragma unroll
     for (int J = 0; J < NB; ++J) s += sm.dcp2[tid][J];
     sm.dc[tid] = s;
-    if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * a.fb[rb + tid]);
+    if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * fbt);
   }
   __syncthreads();
 
@@ -1217,7 +1247,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
         if (r < nval) {
           const float kv = (float)sm.Kb[r][MM::pcol(cj)];
           dqg[(size_t)r * D + cj] = (bf16)dq[e];
-          dkg[(size_t)r * D + cj] = (bf16)(dk[e] - sm.al[r] * dg[e] + 2.f * sm.dc[r] * a.fl[rb + r] * kv);
+          dkg[(size_t)r * D + cj] = (bf16)(dk[e] - sm.al[r] * dg[e] + 2.f * sm.dc[r] * sm.fl[r] * kv);
         }
       }
     }
