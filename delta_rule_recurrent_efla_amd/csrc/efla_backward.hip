@@ -1219,36 +1219,39 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
   if (vt) {
     const int J = I1;
-    const int cj = 16 * J + li;
     bf16x8 ktf[KC], qtf[KC];
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
       ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
       qtf[kb] = tr_frag<NB, true>(&sm.Qb[0][0], Sm::LD, kb, 16 * J);
     }
+    // the products are formed transposed (operands swapped): lane (g, li)
+    // holds token 16 I + li, keys 16 J + 4g .. + 3, stored as 8 bytes
     for (int I = 0; I < NB; ++I) {
       floatx4 dq = z, dk = z, dg = z;
 #pragma unroll
       for (int kb = 0; kb < KD; ++kb) {
-        dq = mma(MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb), snf[kb], dq);
-        dk = mma(MM::template ldp<NKT>(&sm.Ub[16 * I + li][0], kb), dsf[kb], dk);
-        dg = mma(MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb), snf[kb], dg);
+        dq = mma(snf[kb], MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb), dq);
+        dk = mma(dsf[kb], MM::template ldp<NKT>(&sm.Ub[16 * I + li][0], kb), dk);
+        dg = mma(snf[kb], MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb), dg);
       }
 #pragma unroll
       for (int kb = 0; kb < KC; ++kb) {
-        dq = mma(MM::template ldp<NB>(&sm.m.dMb[16 * I + li][0], kb), ktf[kb], dq);
-        dk = mma(tr_frag<NB, true>(&sm.m.dMb[0][0], Sm::LC, kb, 16 * I), qtf[kb], dk);
-        dk = mma(MM::template ldp<NB>(&sm.m.Xb[16 * I + li][0], kb), ktf[kb], dk);
-        dk = mma(tr_frag<NB, true>(&sm.m.Xb[0][0], Sm::LC, kb, 16 * I), ktf[kb], dk);
+        dq = mma(ktf[kb], MM::template ldp<NB>(&sm.m.dMb[16 * I + li][0], kb), dq);
+        dk = mma(qtf[kb], tr_frag<NB, true>(&sm.m.dMb[0][0], Sm::LC, kb, 16 * I), dk);
+        dk = mma(ktf[kb], MM::template ldp<NB>(&sm.m.Xb[16 * I + li][0], kb), dk);
+        dk = mma(ktf[kb], tr_frag<NB, true>(&sm.m.Xb[0][0], Sm::LC, kb, 16 * I), dk);
       }
+      const int r = 16 * I + li, k4 = 16 * J + 4 * g;
+      if (r < nval) {
+        // pcol keeps 4-aligned runs of 4 columns together
+        const floatx4 kv = __builtin_convertvector(*(const bf16x4*)&sm.Kb[r][MM::pcol(k4)], floatx4);
+        const float ar = sm.al[r], fr = 2.f * sm.dc[r] * sm.fl[r];
+        floatx4 dkr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * I + 4 * g + e;
-        if (r < nval) {
-          const float kv = (float)sm.Kb[r][MM::pcol(cj)];
-          dqg[(size_t)r * D + cj] = (bf16)dq[e];
-          dkg[(size_t)r * D + cj] = (bf16)(dk[e] - sm.al[r] * dg[e] + 2.f * sm.dc[r] * sm.fl[r] * kv);
-        }
+        for (int e = 0; e < 4; ++e) dkr[e] = dk[e] - ar * dg[e] + fr * kv[e];
+        *(bf16x4*)&dqg[(size_t)r * D + k4] = cv4(dq);
+        *(bf16x4*)&dkg[(size_t)r * D + k4] = cv4(dkr);
       }
     }
   }
