@@ -325,6 +325,15 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   }
 }
 
+// Workgroups are dealt to the 8 XCDs round robin. This index keeps the column
+// slices of one head on one XCD: they read the same K, Q, M^T and T^T rows,
+// so the second read hits that XCD's L2.
+__device__ __forceinline__ int bwd_xcd_slot(int nvt) {
+  const int n = gridDim.x;
+  if (n % 8 == 0 && (n / 8) % nvt == 0) return (blockIdx.x % 8) * (n / 8) + blockIdx.x / 8;
+  return blockIdx.x;
+}
+
 // ---------------------------------------------------------------------------
 // 3. Per (head, BV-column slice), chunks last to first: the dS recurrence.
 // Wave w < BV/16 owns columns 16 w .. 16 w + 15 of the slice; its d_k x 16
@@ -349,7 +358,8 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nvt = D / BV;
-  const int h = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * BV;
+  const int L = bwd_xcd_slot(nvt);
+  const int h = L / nvt, v0 = (L % nvt) * BV;
   const int col = v0 + 16 * w + li;  // this lane's state column (when w < NW)
   const bool owner = w < NW;
   floatx4 ds[NKT];
@@ -537,7 +547,8 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nvt = D / BV;
-  const int h = blockIdx.x / nvt, v0 = (blockIdx.x % nvt) * BV;
+  const int L = bwd_xcd_slot(nvt);
+  const int h = L / nvt, v0 = (L % nvt) * BV;
   const int col = v0 + 16 * w + li;
   const bool owner = w < NW;
   floatx4 ds[NKT];
