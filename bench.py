@@ -208,15 +208,29 @@ def bench_backward(efla, torch, efla_inputs, w, steps=10, warmup=3):
     def bwd():
         efla.efla_bwd_chunked(g["q"], g["k"], g["v"], g["beta"], dout, g["s0"], dsT, chunk=w.chunk)
 
-    _, per = time_launches(bwd, steps, warmup, torch.cuda.current_stream())
-    per.sort()
-    med = per[len(per) // 2]
+    # a whole training step, forward + backward, two ways: the plain forward
+    # and the recomputing backward; the training forward (outputs and the
+    # chunk-start states in one pass) and the backward that reuses the states
+    def step_plain():
+        efla.efla_fwd_chunked(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=w.chunk)
+        bwd()
+
+    def step_saved():
+        _, _, saved = efla.efla_fwd_chunked_train(g["q"], g["k"], g["v"], g["beta"], g["s0"], chunk=w.chunk)
+        efla.efla_bwd_chunked(g["q"], g["k"], g["v"], g["beta"], dout, None, dsT, chunk=w.chunk,
+                              saved_workspace=saved)
+
+    stream = torch.cuda.current_stream()
+    med, med_plain, med_saved = (sorted(per)[len(per) // 2] for per in
+                                 (time_launches(f, steps, warmup, stream)[1] for f in (bwd, step_plain, step_saved)))
     nbytes = alg_bytes_bwd(w)
     ws = efla.efla_bwd_chunked_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.chunk, w.torch_dtype)
     return {"workload": w.name, "ms_per_call_median": med,
             "head_tokens_per_s": w.head_tokens / (med * 1e-3),
             "alg_bytes": nbytes, "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "workspace_bytes": ws,
+            "train_step_ms_median": {"fwd_chunked + bwd_chunked": med_plain,
+                                     "fwd_chunked_train + bwd_chunked_saved": med_saved},
             "note": "includes the recomputed forward; bf16 MFMA operands, fp32 accumulation"}
 
 

@@ -78,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.efla_bwd_chunked_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         lib.efla_bwd_chunked.restype = i
         lib.efla_bwd_chunked.argtypes = [vp] * 13 + [sz] + [i] * 8 + [vp]
+        lib.efla_bwd_chunked_saved.restype = i
+        lib.efla_bwd_chunked_saved.argtypes = [vp] * 12 + [sz] + [i] * 8 + [vp]
+        lib.efla_fwd_chunked_train.restype = i
+        lib.efla_fwd_chunked_train.argtypes = [vp] * 8 + [sz] + [i] * 8 + [vp]
         lib.efla_status_string.restype = ctypes.c_char_p
         lib.efla_status_string.argtypes = [i]
         _lib = lib
@@ -211,14 +215,58 @@ def efla_bwd_chunked_workspace_bytes(B: int, H: int, T: int, d_k: int, d_v: int,
                                                                _DTYPES[dtype]))
 
 
+def efla_fwd_chunked_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                           s0: Optional[torch.Tensor] = None, chunk: int = 64, coef="exact",
+                           o: Optional[torch.Tensor] = None, s_final: Optional[torch.Tensor] = None,
+                           stream=None):
+    """Forward of a training step: the outputs of efla_fwd_chunked plus the
+    chunk-start states, kept for the backward. Returns (o, s_final, saved),
+    where ``saved`` is the backward workspace to pass to
+    ``efla_bwd_chunked(..., saved_workspace=saved)``."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape != q.shape or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, dev)
+        if s0.shape != (B, H, d, d):
+            raise ValueError("s0 must be [B, H, d_k, d_v]")
+    if o is None:
+        o = torch.empty_like(q)
+    else:
+        _require(o, "o", dt, dev)
+    if s_final is None:
+        s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        _require(s_final, "s_final", torch.float32, dev)
+    ws_bytes = int(lib.efla_bwd_chunked_workspace_bytes(B, H, T, d, d, chunk, _DTYPES[dt]))
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    st = lib.efla_fwd_chunked_train(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
+                                    _ptr(s_final), _ptr(ws), ws_bytes, B, H, T, d, d, int(chunk),
+                                    _coef(coef), _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
+    return o, s_final, ws
+
+
 def efla_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
                      dout: torch.Tensor, s0: Optional[torch.Tensor] = None,
                      ds_final: Optional[torch.Tensor] = None, chunk: int = 64, coef="exact",
-                     want_ds0: bool = True, stream=None):
+                     want_ds0: bool = True, stream=None,
+                     saved_workspace: Optional[torch.Tensor] = None):
     """Backward of efla_fwd_chunked for a loss L(o, S_T): given dout = dL/do
     [B,H,T,d] (input dtype) and ds_final = dL/dS_T [B,H,d,d] fp32 or None,
     returns (dq, dk, dv, dbeta, ds0) with dq, dk, dv, dbeta in the input dtype
-    and ds0 fp32 (None unless want_ds0)."""
+    and ds0 fp32 (None unless want_ds0). With ``saved_workspace`` (the third
+    result of efla_fwd_chunked_train for the same inputs) the forward is not
+    recomputed."""
     lib = load_library()
     dev = q.device
     if q.dim() != 4:
@@ -240,6 +288,16 @@ def efla_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
     db = torch.empty_like(beta)
     ds0 = torch.empty((B, H, d, d), dtype=torch.float32, device=dev) if want_ds0 else None
     ws_bytes = int(lib.efla_bwd_chunked_workspace_bytes(B, H, T, d, d, chunk, _DTYPES[dt]))
+    if saved_workspace is not None:
+        _require(saved_workspace, "saved_workspace", torch.uint8, dev)
+        if saved_workspace.numel() < ws_bytes:
+            raise ValueError("saved_workspace is smaller than the backward workspace for these sizes")
+        st = lib.efla_bwd_chunked_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(dout),
+                                        _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db),
+                                        _ptr(ds0), _ptr(saved_workspace), ws_bytes, B, H, T, d, d,
+                                        int(chunk), _coef(coef), _DTYPES[dt], _stream(dev, stream))
+        _raise(st)
+        return dq, dk, dv, db, ds0
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     st = lib.efla_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(dout),
                               _ptr(ds_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(ds0),

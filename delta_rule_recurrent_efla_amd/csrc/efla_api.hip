@@ -20,7 +20,10 @@ size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is
 hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v, const void* beta,
                                     const float* s0, const void* dout, const float* dsT, void* dq, void* dk,
                                     void* dv, void* dbeta, float* ds0, void* workspace, int NH, int T, int d,
-                                    int chunk, int coef, int is_bf16, hipStream_t stream);
+                                    int chunk, int coef, int is_bf16, int states_saved, hipStream_t stream);
+hipError_t efla_internal_launch_fwd_save(const void* q, const void* k, const void* v, const void* beta,
+                                         const float* s0, void* o, float* s_final, void* workspace, int NH, int T,
+                                         int d, int chunk, int coef, int is_bf16, hipStream_t stream);
 
 namespace {
 
@@ -107,11 +110,11 @@ extern "C" size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k,
   return efla_internal_bwd_workspace_bytes(B * H, T, d_k, chunk, dt == EFLA_DTYPE_BF16);
 }
 
-extern "C" efla_status efla_bwd_chunked(const void* q, const void* k, const void* v, const void* beta,
-                                        const float* s0, const void* dout, const float* ds_final, void* dq,
-                                        void* dk, void* dv, void* dbeta, float* ds0, void* workspace,
-                                        size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
-                                        int chunk, efla_coef coef, efla_dtype dt, void* stream) {
+namespace {
+efla_status bwd_common(const void* q, const void* k, const void* v, const void* beta, const float* s0,
+                       const void* dout, const float* ds_final, void* dq, void* dk, void* dv, void* dbeta,
+                       float* ds0, void* workspace, size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                       int chunk, efla_coef coef, efla_dtype dt, int states_saved, void* stream) {
   if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta) return EFLA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || T < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
   if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
@@ -125,7 +128,47 @@ extern "C" efla_status efla_bwd_chunked(const void* q, const void* k, const void
   if (need == 0 || workspace == nullptr || workspace_bytes < need) return EFLA_ERR_WORKSPACE;
   const hipError_t e = efla_internal_launch_bwd(q, k, v, beta, s0, dout, ds_final, dq, dk, dv, dbeta, ds0,
                                                 workspace, B * H, T, d_k, chunk, (int)coef,
-                                                dt == EFLA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+                                                dt == EFLA_DTYPE_BF16, states_saved,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
+}
+}  // namespace
+
+extern "C" efla_status efla_bwd_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                        const float* s0, const void* dout, const float* ds_final, void* dq,
+                                        void* dk, void* dv, void* dbeta, float* ds0, void* workspace,
+                                        size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                                        int chunk, efla_coef coef, efla_dtype dt, void* stream) {
+  return bwd_common(q, k, v, beta, s0, dout, ds_final, dq, dk, dv, dbeta, ds0, workspace, workspace_bytes, B, H,
+                    T, d_k, d_v, chunk, coef, dt, 0, stream);
+}
+
+extern "C" efla_status efla_bwd_chunked_saved(const void* q, const void* k, const void* v, const void* beta,
+                                              const void* dout, const float* ds_final, void* dq, void* dk,
+                                              void* dv, void* dbeta, float* ds0, void* workspace,
+                                              size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                                              int chunk, efla_coef coef, efla_dtype dt, void* stream) {
+  return bwd_common(q, k, v, beta, nullptr, dout, ds_final, dq, dk, dv, dbeta, ds0, workspace, workspace_bytes,
+                    B, H, T, d_k, d_v, chunk, coef, dt, 1, stream);
+}
+
+extern "C" efla_status efla_fwd_chunked_train(const void* q, const void* k, const void* v, const void* beta,
+                                              const float* s0, void* o, float* s_final, void* bwd_workspace,
+                                              size_t bwd_workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                                              int chunk, efla_coef coef, efla_dtype dt, void* stream) {
+  if (!q || !k || !v || !beta || !o) return EFLA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || T < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
+  if (!chunked_supported(d_k, chunk, dt) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s0) ||
+      !aligned16(s_final) || !aligned16(bwd_workspace) || !elem_aligned(beta, dt))
+    return EFLA_ERR_MISALIGNED;
+  const size_t need = efla_bwd_chunked_workspace_bytes(B, H, T, d_k, d_v, chunk, dt);
+  if (need == 0 || bwd_workspace == nullptr || bwd_workspace_bytes < need) return EFLA_ERR_WORKSPACE;
+  const hipError_t e = efla_internal_launch_fwd_save(q, k, v, beta, s0, o, s_final, bwd_workspace, B * H, T, d_k,
+                                                     chunk, (int)coef, dt == EFLA_DTYPE_BF16,
+                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }
 

@@ -1312,8 +1312,12 @@ static hipError_t bwd_d(const BwdArgs& a, int NH, int d, int chunk, hipStream_t 
 }  // namespace efla
 
 hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
-                                       const float* s0, float* s_chunks, float* s_chunks_n, int NH, int T,
-                                       int d, int chunk, int coef, int is_bf16, hipStream_t stream);
+                                       const float* s0, void* o, float* s_final, float* s_chunks,
+                                       float* s_chunks_n, int NH, int T, int d, int chunk, int coef, int is_bf16,
+                                       hipStream_t stream);
+hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                        const float* s0, void* o, float* s_final, void* workspace, int NH, int T,
+                                        int d, int chunk, int coef, int is_bf16, hipStream_t stream);
 bool efla_internal_states_supported(int d, int chunk, int is_bf16);
 
 // Chunk size the backward runs with for a requested forward chunk.
@@ -1332,10 +1336,37 @@ size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is
   return (size_t)NH * per_head * sizeof(float);
 }
 
+// The backward's workspace starts with the chunk-start states: [head][chunk]
+// [d_v][d_k] (bf16 in the bf16 form of the gradient kernel, else fp32), then,
+// where the fp32 form needs them, the same states as [head][chunk][d_k][d_v].
+static bool bwd_needs_kv_states(int d, int c, int is_bf16) { return !(is_bf16 && c % 32 == 0 && d % 32 == 0); }
+
+// Forward of a training step: o and s_final as the plain forward, plus the
+// chunk-start states in the backward's workspace. Where the pipelined kernel
+// serves the requested chunk one pass writes all of it; otherwise the states
+// pass (at the backward's chunk) runs first and the forward after it, so that
+// s_final may alias s0 in both cases.
+hipError_t efla_internal_launch_fwd_save(const void* q, const void* k, const void* v, const void* beta,
+                                         const float* s0, void* o, float* s_final, void* workspace, int NH, int T,
+                                         int d, int chunk, int coef, int is_bf16, hipStream_t stream) {
+  const int c = bwd_chunk_for(d, chunk, is_bf16);
+  if (c == 0) return hipErrorInvalidValue;
+  const size_t nc = (size_t)((T + c - 1) / c);
+  float* sc = (float*)workspace;
+  float* scn = bwd_needs_kv_states(d, c, is_bf16) ? sc + (size_t)NH * nc * d * d : nullptr;
+  if (c == chunk)
+    return efla_internal_launch_states(q, k, v, beta, s0, o, s_final, sc, scn, NH, T, d, c, coef, is_bf16, stream);
+  const hipError_t e =
+      efla_internal_launch_states(q, k, v, beta, s0, nullptr, nullptr, sc, scn, NH, T, d, c, coef, is_bf16, stream);
+  if (e != hipSuccess) return e;
+  return efla_internal_launch_chunked(q, k, v, beta, s0, o, s_final, nullptr, NH, T, d, chunk, coef, is_bf16,
+                                      stream);
+}
+
 hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v, const void* beta,
                                     const float* s0, const void* dout, const float* dsT, void* dq, void* dk,
                                     void* dv, void* dbeta, float* ds0, void* workspace, int NH, int T, int d,
-                                    int chunk, int coef, int is_bf16, hipStream_t stream) {
+                                    int chunk, int coef, int is_bf16, int states_saved, hipStream_t stream) {
   const int c = bwd_chunk_for(d, chunk, is_bf16);
   if (c == 0) return hipErrorInvalidValue;
   const size_t nc = (size_t)((T + c - 1) / c), Tp = nc * c;
@@ -1381,9 +1412,11 @@ hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v,
   a.mt = p;
   // the bf16 form of the gradient kernel (C and d multiples of 32) reads the
   // transposed states only
-  const bool need_n = !(is_bf16 && c % 32 == 0 && d % 32 == 0);
-  hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, sc, need_n ? scn : nullptr, NH, T, d, c, coef,
-                                             is_bf16, stream);
-  if (e != hipSuccess) return e;
+  if (!states_saved) {
+    const hipError_t e = efla_internal_launch_states(q, k, v, beta, s0, nullptr, nullptr, sc,
+                                                     bwd_needs_kv_states(d, c, is_bf16) ? scn : nullptr, NH, T, d,
+                                                     c, coef, is_bf16, stream);
+    if (e != hipSuccess) return e;
+  }
   return is_bf16 ? efla::bwd_d<efla::bf16>(a, NH, d, c, stream) : efla::bwd_d<float>(a, NH, d, c, stream);
 }

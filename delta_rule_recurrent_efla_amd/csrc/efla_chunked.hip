@@ -638,14 +638,19 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // runs the slice's columns from S = I with zero values (the segment's
   // transition), the second half from S = 0 with the values (its offset),
   // both on one prep of the keys; 2 chunk-start states for the backward, no
-  // outputs. All compile-time.
+  // outputs; 3 outputs and the chunk-start states (the forward of a training
+  // step, whose backward then skips its own state pass). All compile-time.
   constexpr bool SUMMARY = PM == 1;
-  constexpr bool SAVE = PM == 2;
-  constexpr bool outs = PM == 0;
+  constexpr bool SAVE = PM == 2 || PM == 3;
+  constexpr bool outs = PM == 0 || PM == 3;
   // negated form (state N = -S, T' = -T diag(a) from the solvers) where the
-  // state is not stored every chunk; the state-saving pass keeps S and
-  // applies a in the state waves, so its stores need no sign flips
-  constexpr bool NEG = PM != 2;
+  // state is not stored every chunk; the state-saving passes keep S and
+  // apply a in the state waves, so their stores need no sign flips
+  constexpr bool NEG = !SAVE;
+  // the query fragments of the output products are requested in phase A,
+  // except with outputs and state saving together (pass mode 3), whose plain
+  // state form holds more registers there: then in phase B, before their use
+  constexpr bool QA = outs && NEG;
   constexpr int NSP = SUMMARY ? NSW / 2 : NSW;  // state waves per column set
   constexpr int SW = NSP < NVT ? NSP : NVT;  // state waves holding columns
   constexpr int CPW = NVT / SW;              // 16-column tiles per state wave
@@ -804,7 +809,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           for (int f = 0; f < NFK; ++f) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = MM::mma(y[cc][ut], kf[ut][f], sf[cc][f]);
-            if constexpr (outs) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
+            if constexpr (QA) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
           }
           if constexpr (!NEG) {
 #pragma unroll
@@ -849,6 +854,10 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         static_for<NB>([&](auto ub) {
           constexpr int ut = decltype(ub)::value;
           if constexpr (outs) {
+            if constexpr (!QA) {
+#pragma unroll
+              for (int f = 0; f < NFK; ++f) qf[ut][f] = MM::template ldp<NKT>(&B.Q[16 * ut + li][0], f);
+            }
             // register-only products would otherwise be hoisted above the
             // barrier; tying their inputs to this point keeps them in phase B
 #pragma unroll
@@ -909,7 +918,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           if (16 * ut + li < nval) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc)
-              store4(orow + (size_t)16 * ut * D + 16 * (wl * CPW + cc), -oacc[cc][ut]);
+              store4(orow + (size_t)16 * ut * D + 16 * (wl * CPW + cc), NEG ? -oacc[cc][ut] : oacc[cc][ut]);
           }
         }
       }
@@ -1613,14 +1622,14 @@ hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void
 // the start of every chunk (for the backward). Only where the pipelined kernel
 // serves the shape.
 namespace efla {
-template <typename CT, int D, int C>
-static hipError_t launch_states(const ChunkedArgs& in, int NH, hipStream_t stream) {
+template <typename CT, int D, int C, int PM>
+static hipError_t launch_states_pm(const ChunkedArgs& in, int NH, hipStream_t stream) {
   if constexpr (pipelined<CT, D, C>()) {
     constexpr int BV = D < 64 ? D : 64;
     constexpr int NSW = EFLA_PIPE_STATE_WAVES;
     ChunkedArgs a = in;
     a.nvt = D / BV;
-    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 2>), dim3((unsigned)(NH * a.nvt)),
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, PM>), dim3((unsigned)(NH * a.nvt)),
                        dim3(64 * (NSW + 6)), 0, stream, a);
     return hipGetLastError();
   } else {
@@ -1628,14 +1637,16 @@ static hipError_t launch_states(const ChunkedArgs& in, int NH, hipStream_t strea
   }
 }
 
+// pass mode 2 (states only) or 3 (outputs and states)
 template <typename CT, int D>
 static hipError_t states_chunk(const ChunkedArgs& a, int NH, int chunk, hipStream_t s) {
+  const bool o = a.o != nullptr;
   switch (chunk) {
-    case 16: return launch_states<CT, D, 16>(a, NH, s);
-    case 32: return launch_states<CT, D, 32>(a, NH, s);
+    case 16: return o ? launch_states_pm<CT, D, 16, 3>(a, NH, s) : launch_states_pm<CT, D, 16, 2>(a, NH, s);
+    case 32: return o ? launch_states_pm<CT, D, 32, 3>(a, NH, s) : launch_states_pm<CT, D, 32, 2>(a, NH, s);
     case 64:
       if constexpr (sizeof(CT) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_states<CT, D, 64>(a, NH, s);
+      else return o ? launch_states_pm<CT, D, 64, 3>(a, NH, s) : launch_states_pm<CT, D, 64, 2>(a, NH, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1658,11 +1669,14 @@ bool efla_internal_states_supported(int d, int chunk, int is_bf16) {
   return is_bf16 ? efla::pipelined_d<efla::bf16>(d, chunk) : efla::pipelined_d<float>(d, chunk);
 }
 
+// The chunk-start states for the backward; with o (and optionally s_final)
+// the same pass also writes the outputs (pass mode 3).
 hipError_t efla_internal_launch_states(const void* q, const void* k, const void* v, const void* beta,
-                                       const float* s0, float* s_chunks, float* s_chunks_n, int NH, int T,
-                                       int d, int chunk, int coef, int is_bf16, hipStream_t stream) {
-  efla::ChunkedArgs a{q, k, v, beta, s0, nullptr, nullptr, T, 1, 0, 0, 1, nullptr, nullptr, coef, s_chunks,
-                      s_chunks_n};
+                                       const float* s0, void* o, float* s_final, float* s_chunks,
+                                       float* s_chunks_n, int NH, int T, int d, int chunk, int coef, int is_bf16,
+                                       hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, o ? s_final : nullptr, T, 1, 0, 0, 1, nullptr, nullptr, coef,
+                      s_chunks, s_chunks_n};
   if (is_bf16) return efla::states_d<efla::bf16>(a, NH, d, chunk, stream);
   return efla::states_d<float>(a, NH, d, chunk, stream);
 }

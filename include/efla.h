@@ -173,6 +173,42 @@ efla_status efla_bwd_chunked(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, int B, int H, int T, int d_k, int d_v, int chunk,
                              efla_coef coef, efla_dtype dt, void* stream);
 
+/*
+ * Forward of a training step: exactly the outputs of efla_fwd_chunked (o and,
+ * if not NULL, s_final; equal up to rounding order), and in the same call the
+ * state at the start of every chunk, written into the backward's workspace,
+ * so that efla_bwd_chunked_saved can skip the forward that efla_bwd_chunked
+ * recomputes. The chunk form and the state update are those of
+ * efla_fwd_chunked (section 整体框架 of the papernotes note).
+ *   q, k, v, beta, s0, o, s_final, chunk, coef, dt   as for efla_fwd_chunked
+ *             (s_final may alias s0).
+ *   bwd_workspace, bwd_workspace_bytes   caller-owned device memory of at
+ *             least efla_bwd_chunked_workspace_bytes() bytes for the same
+ *             sizes, 16-byte aligned (required). On return it holds the
+ *             chunk-start states; pass it unchanged to efla_bwd_chunked_saved.
+ * Where the pipelined kernel serves the chunk size this is one pass; otherwise
+ * the states pass runs first and the plain forward after it. Errors as for
+ * efla_fwd_chunked; a missing or short workspace is EFLA_ERR_WORKSPACE.
+ */
+efla_status efla_fwd_chunked_train(const void* q, const void* k, const void* v, const void* beta,
+                                   const float* s0, void* o, float* s_final, void* bwd_workspace,
+                                   size_t bwd_workspace_bytes, int B, int H, int T, int d_k, int d_v,
+                                   int chunk, efla_coef coef, efla_dtype dt, void* stream);
+
+/*
+ * efla_bwd_chunked without the recomputed forward: the chunk-start states are
+ * taken from `workspace`, which efla_fwd_chunked_train filled for the same
+ * q, k, v, beta, s0, sizes, chunk, coef and dt (s0 itself is not read again).
+ * All other arguments, outputs and errors are those of efla_bwd_chunked; the
+ * gradients are the same. The workspace must not have been used by another
+ * call in between.
+ */
+efla_status efla_bwd_chunked_saved(const void* q, const void* k, const void* v, const void* beta,
+                                   const void* dout, const float* ds_final, void* dq, void* dk, void* dv,
+                                   void* dbeta, float* ds0, void* workspace, size_t workspace_bytes, int B,
+                                   int H, int T, int d_k, int d_v, int chunk, efla_coef coef, efla_dtype dt,
+                                   void* stream);
+
 /* Static, human-readable name of a status code. Never NULL. */
 const char* efla_status_string(efla_status s);
 

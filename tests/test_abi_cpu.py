@@ -168,3 +168,43 @@ def test_backward_workspace_query():
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 64, 64, 64, 0) == per * 4
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 128, 128, 64, 0) == 0
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 48, 48, 64, 1) == 0
+
+
+def train(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, s0=None, o=FAKE, sf=None, ws=FAKE, wsb=1 << 40,
+          B=1, H=1, T=8, dk=64, dv=64, chunk=64, coef=0, dt=1):
+    return lib.efla_fwd_chunked_train(q, k, v, beta, s0, o, sf, ws, wsb, B, H, T, dk, dv, chunk, coef, dt,
+                                      None)
+
+
+def saved(lib, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dout=FAKE, dsT=None, dq=FAKE, dk=FAKE, dv=FAKE,
+          db=FAKE, ds0=None, ws=FAKE, wsb=1 << 40, B=1, H=1, T=8, dk_=64, dv_=64, chunk=64, coef=0, dt=1):
+    return lib.efla_bwd_chunked_saved(q, k, v, beta, dout, dsT, dq, dk, dv, db, ds0, ws, wsb, B, H, T, dk_,
+                                      dv_, chunk, coef, dt, None)
+
+
+def test_train_forward_rejects_bad_arguments_before_launch():
+    lib = efla.load_library()
+    assert train(lib, q=None) == 1
+    assert train(lib, o=None) == 1
+    assert train(lib, B=0) == 2
+    assert train(lib, dv=32) == 2
+    assert train(lib, chunk=8) == 3
+    assert train(lib, dk=128, dv=128, chunk=64, dt=0) == 3
+    assert train(lib, coef=7) == 3
+    assert train(lib, q=FAKE + 8) == 4
+    assert train(lib, ws=FAKE + 8) == 4
+    assert train(lib, ws=None) == 5          # the backward's workspace is required
+    need = lib.efla_bwd_chunked_workspace_bytes(1, 1, 8, 64, 64, 64, 1)
+    assert need > 0
+    assert train(lib, wsb=need - 1) == 5
+
+
+def test_saved_backward_rejects_bad_arguments_before_launch():
+    lib = efla.load_library()
+    assert saved(lib, dout=None) == 1
+    assert saved(lib, dq=None) == 1
+    assert saved(lib, B=0) == 2
+    assert saved(lib, chunk=48) == 3
+    assert saved(lib, db=FAKE + 1) == 4
+    assert saved(lib, ws=None) == 5
+    assert saved(lib, wsb=16) == 5
