@@ -237,35 +237,36 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   const size_t mb = ((size_t)h * a.nc + ch) * C * C;
   constexpr int NT = C / 16;
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-  // K Q^T tiles (J, I), i.e. M^T: A = rows of K, B(k, i) = Q[16I + i][k], a
-  // row of Q; lane (g, li) holds M^T[16J + 4g + e][16I + li], so a row of M^T
-  // is written by 16 consecutive lanes
+  // M^T tiles (J, I) as Q K^T products: A = rows of Q, B = rows of K; lane
+  // (g, li) holds M[16I + 4g + e][16J + li] = M^T[16J + li][16I + 4g + e],
+  // 4 consecutive entries of one row of M^T, stored together
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
     // bf16 inputs: products of bf16 values are exact in fp32, so the bf16 MFMA
     // gives the same K K^T and Q K^T as the fp32 one
-    const floatx4 kq = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * J + li][k0]); },
-                                               [&](int k0) { return ld4(&Qf[16 * I + li][k0]); });
+    const floatx4 qk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Qf[16 * I + li][k0]); },
+                                               [&](int k0) { return ld4(&Kf[16 * J + li][k0]); });
+    const int j = 16 * J + li, i0 = 16 * I + 4 * g;
+    floatx4 m;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 16 * J + 4 * g + e, i = 16 * I + li;
-      // M[i][j] = q_i . k_j for j <= i
-      const float m = j <= i ? kq[e] : 0.f;
-      if constexpr (MBF) ((bf16*)a.mt)[mb + (size_t)j * C + i] = (bf16)m;
-      else a.mt[mb + (size_t)j * C + i] = m;
-    }
+    for (int e = 0; e < 4; ++e) m[e] = j <= i0 + e ? qk[e] : 0.f;  // M[i][j] = q_i . k_j for j <= i
+    if constexpr (MBF) *(bf16x4*)&((bf16*)a.mt)[mb + (size_t)j * C + i0] = __builtin_convertvector(m, bf16x4);
+    else *(floatx4*)&a.mt[mb + (size_t)j * C + i0] = m;
   }
   __syncthreads();  // Q is dead: its space takes A
+  // K K^T tiles (I, J): lane (g, li) holds row 16I + li, columns
+  // 16J + 4g .. + 3 (operands swapped), stored 16 bytes at a time
   for (int tl = w; tl < NT * NT; tl += 4) {
     const int I = tl / NT, J = tl % NT;
-    const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * I + li][k0]); },
-                                               [&](int k0) { return ld4(&Kf[16 * J + li][k0]); });
+    const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * J + li][k0]); },
+                                               [&](int k0) { return ld4(&Kf[16 * I + li][k0]); });
+    const int i = 16 * I + li, j0 = 16 * J + 4 * g;
+    *(floatx4*)&a.gram[mb + (size_t)i * C + j0] = gk;
+    const float ci = cs[i];
+    floatx4 am;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * I + 4 * g + e, j = 16 * J + li;
-      a.gram[mb + (size_t)i * C + j] = gk[e];
-      Am(i, j) = j < i ? cs[i] * gk[e] : 0.f;
-    }
+    for (int e = 0; e < 4; ++e) am[e] = j0 + e < i ? ci * gk[e] : 0.f;
+    *(floatx4*)&Am(i, j0) = am;
   }
   __syncthreads();  // K is dead: its space takes T
   // T = (I + A)^{-1} by blocks. Diagonal blocks: lane (b, c) solves column c
