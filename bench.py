@@ -89,6 +89,102 @@ def copy_calibration(torch, reps: int = 5):
     del src, dst
 
 
+FLUSH_BYTES = 512 << 20  # larger than the 256 MB Infinity Cache
+
+
+def make_flush(torch):
+    """A 512 MB device buffer and a function that overwrites it (a fill
+    kernel): run between timed launches, it evicts the previous launch's data
+    from the Infinity Cache and the L2s, so the next launch reads from HBM."""
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.fill_(1.0)
+
+    return flush
+
+
+def time_flushed(fn, steps, warmup, stream, flush):
+    """Per-launch times with the caches flushed before every launch; the
+    flush itself is outside the events."""
+    import torch
+
+    for _ in range(warmup):
+        flush()
+        fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(steps):
+        flush()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        per.append((s, e))
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in per]
+
+
+def measured_peaks(torch):
+    """Achievable rates on this GPU, from the measurement-only kernels in
+    libefla_bench.so: a loop of v_mfma_f32_32x32x16_bf16 (and of
+    v_mfma_f32_16x16x4_f32) over 8 workgroups of 4 waves per CU, and a
+    streaming copy of 1 GiB (2 GiB moved). Median of 5 timed launches each."""
+    import ctypes
+
+    from delta_rule_recurrent_efla_amd import build as _b
+
+    lib = ctypes.CDLL(_b.BENCH_LIB)
+    lib.efla_bench_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.efla_bench_mfma_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.efla_bench_mfma_bf16_flops.restype = ctypes.c_double
+    lib.efla_bench_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.efla_bench_mfma_f32_flops.restype = ctypes.c_double
+    lib.efla_bench_mfma_f32_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.efla_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                    ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    blocks = 8 * cus
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def med(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        _, per = time_launches(fn, n, 2, stream)
+        return sorted(per)[len(per) // 2]
+
+    it_bf, it_f = 4000, 4000
+    t_bf = med(lambda: lib.efla_bench_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, it_bf, sp))
+    t_f = med(lambda: lib.efla_bench_mfma_f32(ctypes.c_void_p(out.data_ptr()), blocks, it_f, sp))
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_c = med(lambda: lib.efla_bench_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                          n // 16, 4 * cus * 8, sp))
+    assert torch.equal(dst[:1024], src[:1024])
+    del src, dst, out
+    return {"bf16_mfma_TFLOPs": lib.efla_bench_mfma_bf16_flops(blocks, it_bf) / (t_bf * 1e-3) / 1e12,
+            "fp32_mfma_TFLOPs": lib.efla_bench_mfma_f32_flops(blocks, it_f) / (t_f * 1e-3) / 1e12,
+            "copy_GBs": 2 * n / (t_c * 1e-3) / 1e9,
+            "note": "MFMA loops: 8 workgroups x 4 waves per CU, 4 independent chains per wave; "
+                    "copy: 1 GiB read + 1 GiB written, 16-byte accesses"}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def alg_bytes_fwd(w, with_s0: bool) -> int:
     """Bytes the method must move: read q, k, v, beta and write o
     ((4d+1) elements per head-token), plus S0 read (if given) and S_T write
@@ -150,6 +246,39 @@ def cpu_baseline(w, x, min_seconds: float, max_threads: int = 16):
             "kind": "oracle",
             "sample": f"{passes} pass(es) over the whole workload ({nh} heads x T={w.T}), "
                       f"fp64 sequential recurrence, {use} threads, {dt:.1f} s wall"}
+
+
+def cpu_single_thread(efla_inputs, seconds: float = 2.0):
+    """The oracle on one thread, head-tokens/s: the fp32 d=64 workload (whole
+    heads, as many as fit in ``seconds``) and the 340M layer's decode (all 256
+    decode tokens of as many heads, continuing from zero states)."""
+    import oracle
+
+    out = {}
+    w = efla_inputs.WORKLOADS["fp32_d64"]
+    x = efla_inputs.make_inputs(w)
+    nh = w.B * w.H
+    flat = lambda t: t.reshape((nh,) + tuple(t.shape[2:]))
+    done, t0 = 0, time.perf_counter()
+    while done < nh and time.perf_counter() - t0 < seconds:
+        sl = slice(done, done + 1)
+        oracle.fwd(flat(x["q"])[sl], flat(x["k"])[sl], flat(x["v"])[sl], flat(x["beta"])[sl], nthreads=1)
+        done += 1
+    dt = time.perf_counter() - t0
+    out["fp32_d64"] = {"head_tokens_per_s": done * w.T / dt, "sample": f"{done} head(s) x T={w.T}"}
+    w = efla_inputs.WORKLOADS["layer340m_d128"]
+    x = efla_inputs.make_inputs(w)
+    nh = w.B * w.H
+    done, t0 = 0, time.perf_counter()
+    while done < nh and time.perf_counter() - t0 < seconds:
+        sl = slice(done, done + 1)
+        oracle.fwd(flat(x["dec_q"])[sl], flat(x["dec_k"])[sl], flat(x["dec_v"])[sl], flat(x["dec_beta"])[sl],
+                   nthreads=1)
+        done += 1
+    dt = time.perf_counter() - t0
+    out["layer340m_d128_decode"] = {"head_tokens_per_s": done * w.decode_steps / dt,
+                                    "sample": f"{done} head(s) x {w.decode_steps} decode tokens"}
+    return out
 
 
 def bench_other_workloads(efla, torch, efla_inputs, skip: str, steps=10, warmup=3):
@@ -234,7 +363,10 @@ def bench_backward(efla, torch, efla_inputs, w, steps=10, warmup=3):
             "note": "includes the recomputed forward; bf16 MFMA operands, fp32 accumulation"}
 
 
-def bench_decode(efla, torch, efla_inputs, steps=256):
+def bench_decode(efla, torch, efla_inputs, flush, steps=256):
+    """256 decode steps on the 340M layer shape (128 heads), continuing from
+    the chunked forward's final state: back to back (the 16.9 MB state stays
+    in the Infinity Cache) and with the caches flushed before every step."""
     w = efla_inputs.WORKLOADS["layer340m_d128"]
     x = efla_inputs.make_inputs(w)
     g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
@@ -253,13 +385,21 @@ def bench_decode(efla, torch, efla_inputs, steps=256):
     total, per = time_launches(one, nsteps, 8, stream)
     per.sort()
     med_us = per[len(per) // 2] * 1e3
+    fl = sorted(time_flushed(one, 32, 2, stream, flush))
+    fl_us = fl[len(fl) // 2] * 1e3
     state_bytes = w.B * w.H * w.d * w.d * 4 * 2
     io_bytes = w.B * w.H * (4 * w.d + 1) * 2
+    nb = state_bytes + io_bytes
     return {"workload": f"{w.name} decode", "heads": w.B * w.H, "steps": nsteps,
-            "us_per_step_median": med_us, "us_per_step_mean": total * 1e3 / nsteps,
-            "alg_bytes_per_step": state_bytes + io_bytes,
-            "achieved_GBs_median": (state_bytes + io_bytes) / (med_us * 1e-6) / 1e9,
-            "note": "back-to-back steps; the 16.8 MB state stays cache-warm"}
+            "alg_bytes_per_step": nb,
+            "warm": {"us_per_step_median": med_us, "us_per_step_mean": total * 1e3 / nsteps,
+                     "achieved_GBs": nb / (med_us * 1e-6) / 1e9,
+                     "hbm_frac": nb / (med_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "note": "back-to-back steps; the state stays cache-resident, so this may exceed HBM"},
+            "flushed": {"us_per_step_median": fl_us, "steps": len(fl),
+                        "achieved_GBs": nb / (fl_us * 1e-6) / 1e9,
+                        "hbm_frac": nb / (fl_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "note": "512 MB written before every step (outside the events)"}}
 
 
 def main():
@@ -280,6 +420,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (HBM-counter calibration)")
+    ap.add_argument("--no-flushed", action="store_true",
+                    help="skip the cache-flushed per-launch timing of the forward")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA and copy peaks")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -338,8 +482,23 @@ def main():
                      "kernel": "efla_chunked_pipe_kernel",
                      "mfma_bf16_frac": flops / (avg_launch_ms * 1e-3) / BF16_PEAK_FLOPS},
     }
+    flush = make_flush(torch)
+    if not args.no_flushed:
+        # the same launch with a 512 MB write before each one (outside the
+        # events): every input byte comes from HBM, none from the Infinity
+        # Cache left warm by the previous launch
+        fl = sorted(time_flushed(step, 20, 3, stream, flush))
+        fmed = fl[len(fl) // 2]
+        res["flushed"] = {"ms_per_launch_median": fmed, "launches": len(fl),
+                          "head_tokens_per_s": w.head_tokens / (fmed * 1e-3),
+                          "hbm_frac": nbytes / (fmed * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not args.no_peaks:
+        pk = measured_peaks(torch)
+        pk["hbm_frac_vs_copy"] = achieved / pk["copy_GBs"]
+        pk["bf16_mfma_frac_vs_loop"] = flops / (avg_launch_ms * 1e-3) / (pk["bf16_mfma_TFLOPs"] * 1e12)
+        res["measured_peaks"] = pk
     if not args.no_decode:
-        res["decode"] = bench_decode(efla, torch, efla_inputs)
+        res["decode"] = bench_decode(efla, torch, efla_inputs, flush)
     if not args.no_backward:
         res["backward"] = bench_backward(efla, torch, efla_inputs, w)
     if not args.no_others:
@@ -348,6 +507,8 @@ def main():
         copy_calibration(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        res["cpu_baseline"]["cpu_model"] = host_cpu_model()
+        res["cpu_baseline"]["single_thread"] = cpu_single_thread(efla_inputs)
     print(json.dumps(res), flush=True)
 
 

@@ -106,7 +106,22 @@ def _stream(device: torch.device, stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _require(t: torch.Tensor, name: str, dtype, device):
+def _keep(stream, *tensors):
+    """Tie the binding's own allocations (outputs, workspaces) to a launch
+    stream that is not torch's current one: the caching allocator then does
+    not hand their memory to later work on the current stream while the
+    kernels on ``stream`` may still use it."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, device, shape=None):
+    """Device, dtype, contiguity and (when given) the exact shape. The C ABI
+    receives bare pointers and cannot see sizes, so a buffer that is too
+    small is caught here or not at all."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device:
@@ -115,6 +130,8 @@ def _require(t: torch.Tensor, name: str, dtype, device):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _coef(coef) -> int:
@@ -158,20 +175,24 @@ def efla_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
         _require(s0, "s0", torch.float32, dev)
         if s0.shape != (B, H, d, dv):
             raise ValueError("s0 must be [B, H, d_k, d_v]")
+    own = []
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=dt, device=dev)
+        own.append(o)
     else:
-        _require(o, "o", dt, dev)
+        _require(o, "o", dt, dev, (B, H, T, dv))
     if s_final is None and return_state:
         s_final = torch.empty((B, H, d, dv), dtype=torch.float32, device=dev)
+        own.append(s_final)
     elif s_final is not None:
-        _require(s_final, "s_final", torch.float32, dev)
+        _require(s_final, "s_final", torch.float32, dev, (B, H, d, dv))
     ws_bytes = int(lib.efla_fwd_chunked_workspace_bytes(B, H, T, d, dv, chunk, _DTYPES[dt]))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
     st = lib.efla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
                               _ptr(s_final), _ptr(ws), ws_bytes, B, H, T, d, dv, int(chunk),
                               _coef(coef), _DTYPES[dt], _stream(dev, stream))
     _raise(st)
+    _keep(stream, ws, *own)
     return o, s_final
 
 
@@ -198,14 +219,16 @@ def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _require(state, "state", torch.float32, dev)
     if state.shape != (B, H, d, dv):
         raise ValueError("state must be [B, H, d_k, d_v]")
+    own = None
     if o is None:
-        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+        o = own = torch.empty((B, H, dv), dtype=dt, device=dev)
     else:
-        _require(o, "o", dt, dev)
+        _require(o, "o", dt, dev, (B, H, dv))
     st = lib.efla_fwd_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(state),
                                      _ptr(o), B, H, d, dv, _coef(coef), _DTYPES[dt],
                                      _stream(dev, stream))
     _raise(st)
+    _keep(stream, own)
     return o
 
 
@@ -239,20 +262,24 @@ def efla_fwd_chunked_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, be
         _require(s0, "s0", torch.float32, dev)
         if s0.shape != (B, H, d, d):
             raise ValueError("s0 must be [B, H, d_k, d_v]")
+    own = []
     if o is None:
         o = torch.empty_like(q)
+        own.append(o)
     else:
-        _require(o, "o", dt, dev)
+        _require(o, "o", dt, dev, (B, H, T, d))
     if s_final is None:
         s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+        own.append(s_final)
     else:
-        _require(s_final, "s_final", torch.float32, dev)
+        _require(s_final, "s_final", torch.float32, dev, (B, H, d, d))
     ws_bytes = int(lib.efla_bwd_chunked_workspace_bytes(B, H, T, d, d, chunk, _DTYPES[dt]))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     st = lib.efla_fwd_chunked_train(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
                                     _ptr(s_final), _ptr(ws), ws_bytes, B, H, T, d, d, int(chunk),
                                     _coef(coef), _DTYPES[dt], _stream(dev, stream))
     _raise(st)
+    _keep(stream, ws, *own)
     return o, s_final, ws
 
 
@@ -297,6 +324,7 @@ def efla_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
                                         _ptr(ds0), _ptr(saved_workspace), ws_bytes, B, H, T, d, d,
                                         int(chunk), _coef(coef), _DTYPES[dt], _stream(dev, stream))
         _raise(st)
+        _keep(stream, dq, dk, dv, db, ds0)
         return dq, dk, dv, db, ds0
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     st = lib.efla_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(dout),
@@ -304,4 +332,5 @@ def efla_bwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
                               _ptr(ws), ws_bytes, B, H, T, d, d, int(chunk), _coef(coef),
                               _DTYPES[dt], _stream(dev, stream))
     _raise(st)
+    _keep(stream, ws, dq, dk, dv, db, ds0)
     return dq, dk, dv, db, ds0

@@ -18,6 +18,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libefla.so")
 
 SOURCES = ["efla_api.hip", "efla_chunked.hip", "efla_decode.hip", "efla_backward.hip"]
+# measurement-only kernels (achievable MFMA rate and streaming bandwidth),
+# linked into a separate library that only the benchmark loads
+BENCH_SOURCES = ["bench_peaks.hip"]
+BENCH_LIB = os.path.join(PKG, "libefla_bench.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -59,19 +63,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc link failed")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build_library(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in BENCH_SOURCES], BENCH_LIB, verbose)
     return LIB
 
 

@@ -24,7 +24,12 @@
 //      chunks last to first: the dS recurrence (the only serial part), dV,
 //      G and the dS' of every chunk;
 //   4. efla_bwd_grad_kernel, one workgroup per (head, chunk): dq, dk, dbeta.
-// Arithmetic is fp32 throughout (v_mfma_f32_16x16x4_f32), for bf16 inputs too.
+// Numerics: fp32 inputs run every product as v_mfma_f32_16x16x4_f32 with fp32
+// storage. bf16 inputs with C and d multiples of 32 (the "bf16 form":
+// efla_bwd_state_kernel_bf, efla_bwd_grad_kernel_bf) take bf16 MFMA operands
+// (v_mfma_f32_16x16x32_bf16) and keep the chunk-start states, T^T, M^T and
+// dS' as bf16 in the workspace, accumulating in fp32; the other bf16 shapes
+// run the fp32 form. The gate and its derivatives are fp32 everywhere.
 
 #include <hip/hip_runtime.h>
 

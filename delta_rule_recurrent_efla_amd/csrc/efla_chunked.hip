@@ -1521,9 +1521,12 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
       const int nsum = NH * (ns - 2) * a.nvt;
       hipLaunchKernelGGL((efla_seg_first_kernel<CT, D, C, BV>), dim3((unsigned)(nsum + NH * a.nvt)), dim3(512), 0,
                          stream, m1, m0, nsum);
-      if (ns >= 3)
+      if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      if (ns >= 3) {
         hipLaunchKernelGGL((efla_seg_carry_kernel<D>), dim3((unsigned)(NH * (D / 16))), dim3(256), 0, stream,
                            (const float*)seg_out, seg_s0, ns);
+        if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+      }
       ChunkedArgs m2 = a;  // outputs of segments 1 .. ns - 1
       m2.mode = 2;
       m2.seg_len = sp.seg_len;

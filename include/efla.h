@@ -43,7 +43,19 @@
 extern "C" {
 #endif
 
-typedef enum { EFLA_DTYPE_F32 = 0, EFLA_DTYPE_BF16 = 1 } efla_dtype;
+/*
+ * The enumerations below have int as their underlying type in C++ as well
+ * (EFLA_ENUM), so any int a C or foreign-language caller passes is a valid
+ * value of the parameter's type and reaches the validation, which rejects it
+ * with EFLA_ERR_UNSUPPORTED; in C an enumeration already holds any int.
+ */
+#ifdef __cplusplus
+#define EFLA_ENUM(name) enum name : int
+#else
+#define EFLA_ENUM(name) enum name
+#endif
+
+typedef EFLA_ENUM(efla_dtype_e) { EFLA_DTYPE_F32 = 0, EFLA_DTYPE_BF16 = 1 } efla_dtype;
 
 /*
  * Scalar of the rank-1 step S_t = (I - c k k^T) S_{t-1} + c k v^T, with
@@ -60,14 +72,14 @@ typedef enum { EFLA_DTYPE_F32 = 0, EFLA_DTYPE_BF16 = 1 } efla_dtype;
  *           term, the second-order approximation that section names.
  * All four are evaluated in fp32. Only EXACT floors lambda.
  */
-typedef enum {
+typedef EFLA_ENUM(efla_coef_e) {
   EFLA_COEF_EXACT = 0,
   EFLA_COEF_EULER = 1,
   EFLA_COEF_RK4 = 2,
   EFLA_COEF_ORDER2 = 3
 } efla_coef;
 
-typedef enum {
+typedef EFLA_ENUM(efla_status_e) {
   EFLA_OK = 0,
   EFLA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   EFLA_ERR_BAD_SHAPE = 2,    /* B, H or T < 1, or d_k != d_v */
@@ -161,7 +173,12 @@ size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  *             efla_bwd_chunked_workspace_bytes() bytes (required); contents
  *             on entry do not matter; calls sharing one must not overlap.
  * The forward is recomputed inside (the chunk-start states go to the
- * workspace); arithmetic is fp32 for both input types. Supported sizes are
+ * workspace). Numerics: for fp32 inputs every product is fp32 MFMA with fp32
+ * storage. For bf16 inputs with chunk and d multiples of 32, the products
+ * take bf16 MFMA operands (the saved chunk-start states, T^T, M^T and the
+ * state gradients are stored as bf16, which is exactly the rounding their
+ * consumers apply) and accumulate in fp32; other bf16 shapes run the fp32
+ * form. The gate, its derivatives and every accumulator are fp32. Supported sizes are
  * the forward's; where the forward's pipelined kernel does not serve the
  * chunk size, the backward runs with chunk 32 (same result up to rounding).
  * Errors as for efla_fwd_chunked; a missing or short workspace is

@@ -208,3 +208,60 @@ def test_saved_backward_rejects_bad_arguments_before_launch():
     assert saved(lib, db=FAKE + 1) == 4
     assert saved(lib, ws=None) == 5
     assert saved(lib, wsb=16) == 5
+
+
+def test_binding_rejects_undersized_outputs_before_launch():
+    """The C ABI takes bare pointers and cannot see buffer sizes, so the
+    binding checks caller-provided outputs against the exact shapes the
+    kernels write (CPU tensors here: the check raises before any call into
+    the library)."""
+    import torch
+
+    B, H, T, d = 1, 2, 40, 64
+    q = torch.zeros(B, H, T, d, dtype=torch.bfloat16)
+    beta = torch.zeros(B, H, T, dtype=torch.bfloat16)
+    small_o = torch.zeros(B, H, T - 1, d, dtype=torch.bfloat16)
+    small_s = torch.zeros(B, H, d, d - 16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="o has shape"):
+        efla.efla_fwd_chunked(q, q, q, beta, None, o=small_o)
+    with pytest.raises(ValueError, match="s_final has shape"):
+        efla.efla_fwd_chunked(q, q, q, beta, None, s_final=small_s)
+    with pytest.raises(ValueError, match="o has shape"):
+        efla.efla_fwd_chunked_train(q, q, q, beta, None, o=small_o)
+    with pytest.raises(ValueError, match="s_final has shape"):
+        efla.efla_fwd_chunked_train(q, q, q, beta, None, s_final=small_s)
+    state = torch.zeros(B, H, d, d, dtype=torch.float32)
+    with pytest.raises(ValueError, match="o has shape"):
+        q1, b1 = q[:, :, 0].contiguous(), beta[:, :, 0].contiguous()
+        efla.efla_fwd_recurrent_step(q1, q1, q1, b1, state,
+                                     o=torch.zeros(B, H, d // 2, dtype=torch.bfloat16))
+
+
+_NO_GPU_CHILD = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import delta_rule_recurrent_efla_amd as efla
+lib = efla.load_library()
+F = 0x100000
+print(lib.efla_fwd_chunked(F, F, F, F, None, F, None, None, 0, 1, 1, 8, 64, 64, 64, 0, 1, None),
+      lib.efla_fwd_recurrent_step(F, F, F, F, F, F, 1, 1, 64, 64, 0, 1, None))
+"""
+
+
+def test_well_formed_call_without_a_gpu_returns_hip_error():
+    """On a host with no usable GPU a call that passes validation reaches the
+    launch, which fails: the library reports EFLA_ERR_HIP (6) and does not
+    crash. Runs in a child process with the GPUs hidden from HIP; skipped where
+    a GPU is visible, so no kernel is ever launched on the stand-in pointers."""
+    import subprocess
+    import sys
+
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", _NO_GPU_CHILD, ROOT], capture_output=True, text=True,
+                       timeout=300, env=env)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[-2:] == ["6", "6"], r.stdout

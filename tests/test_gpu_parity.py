@@ -147,35 +147,40 @@ def test_time_segmented_in_place_state(efla):
 
 
 # ------------------------------------------------------------ the five configs
-SAMPLE_HEADS = {"layer340m_d128": 6, "layer1p3b_d128": 6, "stiff_long_d128": 2}
+def record(key, **vals):
+    """Print one parity record as a JSON line (the measured errors per config
+    are kept in the run's log)."""
+    import json
+
+    note("PARITY " + json.dumps({"case": key, **vals}))
 
 
 @pytest.mark.parametrize("name", list(efla_inputs.WORKLOADS))
 def test_config_parity(efla, name):
+    """Every head of every synthetic configuration, at full size and in the
+    launch configuration the benchmark times, against the fp64 oracle."""
     w = efla_inputs.WORKLOADS[name]
     note(f"[config] {name}: B={w.B} H={w.H} T={w.T} d={w.d} chunk={w.chunk} {w.dtype}")
     x = efla_inputs.make_inputs(w)
     o, sT = run_chunked(efla, x, w.chunk, x["s0"])
     assert torch.isfinite(o).all() and torch.isfinite(sT).all()
-    nh = w.B * w.H
-    flat = lambda t: None if t is None else t.reshape((nh,) + tuple(t.shape[2:]))
-    heads = list(range(nh))
-    if name in SAMPLE_HEADS:
-        n = SAMPLE_HEADS[name]
-        heads = sorted(set(np.linspace(0, nh - 1, n).round().astype(int).tolist()))
-    sel = lambda t: None if t is None else flat(t)[heads]
-    o_ref, s_ref, norms = oracle.fwd(sel(x["q"]), sel(x["k"]), sel(x["v"]), sel(x["beta"]),
-                                     sel(x["s0"]), nthreads=16, want_norms=True)
+    o_ref, s_ref, norms = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], x["s0"], nthreads=16,
+                                     want_norms=True)
     tol = TOL[w.torch_dtype]
-    eo = normwise(flat(o)[heads], o_ref)
-    es = normwise(flat(sT)[heads], s_ref)
-    note(f"   heads={heads[:8]}{'...' if len(heads) > 8 else ''} err o={eo:.3e} S_T={es:.3e} "
-         f"(tol {tol}); oracle max ||S_t||_F={norms.max():.3g}")
-    assert eo <= tol and es <= tol
+    eo, es = normwise(o, o_ref), normwise(sT, s_ref)
+    # the final state's norm per head, GPU against the oracle's per-step norm
+    # output at the last token
+    sn_gpu = sT.double().flatten(-2).norm(dim=-1).flatten()
+    sn_ref = torch.from_numpy(norms[..., -1]).flatten()
+    en = float(((sn_gpu - sn_ref).abs() / sn_ref.clamp_min(1e-30)).max())
+    record(name, heads=w.B * w.H, o=eo, S_T=es, final_norm=en, tol=tol,
+           oracle_max_state_norm=float(norms.max()))
+    assert eo <= tol and es <= tol and en <= tol
 
 
 def test_layer340m_decode_continues_forward(efla):
-    """256 single-token steps from the chunked forward's final state."""
+    """256 single-token steps from the chunked forward's final state, every
+    one of the 128 heads against the oracle."""
     w = efla_inputs.WORKLOADS["layer340m_d128"]
     note(f"[decode] {w.name}: {w.decode_steps} steps from S_T")
     x = efla_inputs.make_inputs(w)
@@ -188,15 +193,12 @@ def test_layer340m_decode_continues_forward(efla):
             g["dec_v"][:, :, i].contiguous(), g["dec_beta"][:, :, i].contiguous(), st))
     od = torch.stack(outs, 2).float().cpu()
     torch.cuda.synchronize()
-    nh = w.B * w.H
-    heads = [0, 37, 90, nh - 1]
-    f = lambda t: t.reshape((nh,) + tuple(t.shape[2:]))[heads]
-    _, s_ref = oracle.fwd(f(x["q"]), f(x["k"]), f(x["v"]), f(x["beta"]), nthreads=8)
-    od_ref, sd_ref = oracle.fwd(f(x["dec_q"]), f(x["dec_k"]), f(x["dec_v"]), f(x["dec_beta"]),
-                                s_ref)
-    eo = normwise(f(od), od_ref)
-    es = normwise(f(st.cpu()), sd_ref)
-    note(f"   err decode o={eo:.3e} S={es:.3e}")
+    _, s_ref = oracle.fwd(x["q"], x["k"], x["v"], x["beta"], nthreads=16)
+    od_ref, sd_ref = oracle.fwd(x["dec_q"], x["dec_k"], x["dec_v"], x["dec_beta"], s_ref,
+                                nthreads=16)
+    eo = normwise(od, od_ref)
+    es = normwise(st.cpu(), sd_ref)
+    record("layer340m_d128 decode x256", heads=w.B * w.H, o=eo, S=es, tol=2e-2)
     assert eo <= 2e-2 and es <= 2e-2
 
 

@@ -387,3 +387,57 @@ def test_chunked_form_equals_sequential_oracle(T, C):
     scale = max(1.0, np.abs(o).max())
     np.testing.assert_allclose(oc, o[0], atol=1e-12 * scale)
     np.testing.assert_allclose(sc, sf[0], atol=1e-12 * scale)
+
+
+# ------------------------------------------------- per-step state norm output
+def test_state_norm_output_matches_ode_states():
+    """The per-step output ||S_t||_F (want_norms) against the Frobenius norm of
+    the state after each token, with every state taken from the augmented-ODE
+    solution (scipy expm, zero-order hold over [0, beta]; 关键设计 items 1-2),
+    never from the oracle. Three heads with S0 of very different scales, so a
+    norm taken over the wrong head is off by orders of magnitude; the keys are
+    stiff enough that the norm before a token's update differs from the norm
+    after it, so a norm taken before the update fails too."""
+    nh, T, d = 3, 24, 5
+    scales = [0.01, 1.0, 30.0]
+    q = RNG.standard_normal((nh, T, d))
+    v = RNG.standard_normal((nh, T, d))
+    k = np.stack([[rand_key(d, n) for n in np.exp(RNG.uniform(math.log(0.5), math.log(4), T))]
+                  for _ in range(nh)])
+    beta = RNG.uniform(0.3, 1.0, (nh, T))
+    S0 = np.stack([s * RNG.standard_normal((d, d)) for s in scales])
+    _, sf, sn = oracle.fwd(q, k, v, beta, S0, want_norms=True)
+    assert sn.shape == (nh, T)
+    for h in range(nh):
+        S = S0[h].copy()
+        before, after = [], []
+        for t in range(T):
+            before.append(np.linalg.norm(S))
+            S = augmented_exact_update(S, k[h, t], v[h, t], beta[h, t])
+            after.append(np.linalg.norm(S))
+        after, before = np.array(after), np.array(before)
+        np.testing.assert_allclose(sn[h], after, rtol=1e-10)
+        np.testing.assert_allclose(np.linalg.norm(sf[h]), after[-1], rtol=1e-10)
+        # the pin tells the two readings apart on these inputs
+        assert np.abs(before - after).max() > 1e-3 * after.max()
+
+
+def test_state_norm_output_special_cases():
+    """beta = 0 keeps ||S_t||_F = ||S0||_F at every step (no update); k = 0 too
+    (the floor makes alpha = beta, and the rank-1 terms vanish); from S0 = 0 the
+    first step gives ||alpha_1 k_1 v_1^T||_F = alpha_1 ||k_1|| ||v_1|| with
+    alpha_1 from mpmath (关键设计 item 2)."""
+    T, d = 9, 4
+    q = RNG.standard_normal((1, T, d))
+    k = RNG.standard_normal((1, T, d))
+    v = RNG.standard_normal((1, T, d))
+    S0 = RNG.standard_normal((1, d, d))
+    _, _, sn = oracle.fwd(q, k, v, np.zeros((1, T)), S0, want_norms=True)
+    np.testing.assert_allclose(sn[0], np.full(T, np.linalg.norm(S0)), rtol=1e-14)
+    _, _, sn = oracle.fwd(q, np.zeros_like(k), v, np.ones((1, T)), S0, want_norms=True)
+    np.testing.assert_allclose(sn[0], np.full(T, np.linalg.norm(S0)), rtol=1e-14)
+    beta = RNG.uniform(0.2, 0.9, (1, T))
+    _, _, sn = oracle.fwd(q, k, v, beta, None, want_norms=True)
+    lam = float(k[0, 0] @ k[0, 0])
+    a1 = float(mp_alpha(beta[0, 0], lam))
+    np.testing.assert_allclose(sn[0, 0], a1 * math.sqrt(lam) * np.linalg.norm(v[0, 0]), rtol=1e-13)
