@@ -65,6 +65,13 @@ def _load():
     lib.efla_oracle_fwd.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp,
                                     ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int]
+    lib.efla_oracle_step_gated.restype = None
+    lib.efla_oracle_step_gated.argtypes = [ctypes.c_int, dp, dp, dp, ctypes.c_double, ctypes.c_double,
+                                           dp, dp, ctypes.c_int, ctypes.c_int]
+    lib.efla_oracle_fwd_gated.restype = ctypes.c_int
+    lib.efla_oracle_fwd_gated.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp,
+                                          ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int]
     lib.efla_oracle_coef_grad.restype = None
     lib.efla_oracle_coef_grad.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, dp, dp]
     lib.efla_oracle_bwd.restype = ctypes.c_int
@@ -139,6 +146,43 @@ def fwd(q, k, v, beta, s0=None, mode: int = EXACT, nthreads: int = 1,
         raise ValueError("efla_oracle_fwd rejected the sizes")
     if want_norms:
         return o, sf, sn
+    return o, sf
+
+
+def step_gated(q, k, v, beta: float, log_g: float, S, mode: int = EXACT):
+    """One gated token on one head: S_new = exp(log_g) (I - c k k^T) S + c k v^T.
+    Returns (S_new, o); inputs untouched."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = _f64(S).copy()
+    dk, dv = S.shape
+    o = np.zeros(dv, dtype=np.float64)
+    _load().efla_oracle_step_gated(int(mode), _ptr(q), _ptr(k), _ptr(v), float(beta), float(log_g),
+                                   _ptr(S), _ptr(o), dk, dv)
+    return S, o
+
+
+def fwd_gated(q, k, v, beta, log_g, s0=None, mode: int = EXACT, nthreads: int = 1):
+    """Sequential fp64 forward of the gated variant: per token
+    S_t = g_t (I - c_t k_t k_t^T) S_{t-1} + c_t k_t v_t^T, g_t = exp(log_g_t),
+    o_t = S_t^T q_t. Shapes as fwd, log_g like beta. Returns (o, s_final)."""
+    q, k, v, beta, log_g = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(log_g)
+    lead = beta.shape[:-1]
+    T = beta.shape[-1]
+    dk = k.shape[-1]
+    dv = v.shape[-1]
+    nh = int(np.prod(lead)) if len(lead) else 1
+    assert q.shape == lead + (T, dk) and k.shape == lead + (T, dk)
+    assert v.shape == lead + (T, dv) and log_g.shape == beta.shape
+    s0a = None
+    if s0 is not None:
+        s0a = _f64(s0)
+        assert s0a.shape == lead + (dk, dv)
+    o = np.zeros(lead + (T, dv), dtype=np.float64)
+    sf = np.zeros(lead + (dk, dv), dtype=np.float64)
+    rc = _load().efla_oracle_fwd_gated(int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_g),
+                                       _ptr(s0a), _ptr(o), _ptr(sf), nh, T, dk, dv, int(nthreads))
+    if rc != 0:
+        raise ValueError("efla_oracle_fwd_gated rejected the sizes")
     return o, sf
 
 

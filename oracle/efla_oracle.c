@@ -36,9 +36,12 @@
  *     c = beta (1 - x/2).
  * No floor applies to lambda in these three: none of them divides by it.
  * Also exposed, for tests only: the Frobenius norm of the state after every
- * step.
+ * step; and a gated variant (efla_oracle_step_gated / efla_oracle_fwd_gated),
+ * the reading taken of the pages' "Gated EFLA": the same step applied to the
+ * state decayed by a per-token factor g_t = exp(log_g_t).
  *
- * Parity pins live in the test suite: the worked example printed in the note
+ * Parity pins live in the test suite (the gated variant's in
+ * test_oracle_gated_pins.py): the worked example printed in the note
  * (section 一个完整示例), scipy's matrix exponential of the augmented ODE
  * matrix, a fine-step RK4 integration of dS/dt = -k k^T S + k v^T, a truncated
  * Taylor series with scaling and squaring, mpmath alpha, limits, bounds,
@@ -98,10 +101,45 @@ void efla_oracle_step(int mode, const double* q, const double* k, const double* 
   }
 }
 
+/* Gated EFLA, one token on one head. The pages name a gated variant (the
+ * papernotes note's main-results table, "Gated EFLA", and its key findings:
+ * the exact flow upgrades Gated DeltaNet) but print no formula. The reading
+ * taken here: Gated DeltaNet's update with its step coefficient replaced by
+ * the exact-flow one,
+ *   S_t = g_t (I - c k k^T) S_{t-1} + c k v^T,   g_t = exp(log_g),
+ * i.e. the ungated step applied to the decayed state g_t S_{t-1}; with
+ * log_g = 0 it is the step above. Steps in that order: lambda and c, p = S^T k,
+ * S <- g (S - c k p^T) + c k v^T, o = S^T q. */
+void efla_oracle_step_gated(int mode, const double* q, const double* k, const double* v,
+                            double beta, double log_g, double* S, double* o, int dk, int dv) {
+  double lam = 0.0;
+  for (int i = 0; i < dk; ++i) lam += k[i] * k[i];
+  double a = efla_oracle_coef(mode, beta, lam);
+  double g = exp(log_g);
+
+  double* p = (double*)malloc(sizeof(double) * (size_t)dv);
+  for (int j = 0; j < dv; ++j) p[j] = 0.0;
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) p[j] += k[i] * S[(size_t)i * dv + j];
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j)
+      S[(size_t)i * dv + j] = g * (S[(size_t)i * dv + j] - a * k[i] * p[j]) + a * k[i] * v[j];
+  free(p);
+
+  if (o) {
+    for (int j = 0; j < dv; ++j) {
+      double acc = 0.0;
+      for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * q[i];
+      o[j] = acc;
+    }
+  }
+}
+
 typedef struct {
   int mode;
   const double *q, *k, *v, *beta, *s0;
   double *o, *s_final, *snorm;
+  const double* log_g; /* [nh, T] log-decays (gated variant), or NULL */
   long nh, T;
   int dk, dv;
   long h_begin, h_end;
@@ -121,7 +159,10 @@ static void run_head(const oracle_job* J, long h) {
     const double* v = J->v + ((size_t)h * T + t) * dv;
     double b = J->beta[(size_t)h * T + t];
     double* o = J->o ? J->o + ((size_t)h * T + t) * dv : NULL;
-    efla_oracle_step(J->mode, q, k, v, b, S, o, dk, dv);
+    if (J->log_g)
+      efla_oracle_step_gated(J->mode, q, k, v, b, J->log_g[(size_t)h * T + t], S, o, dk, dv);
+    else
+      efla_oracle_step(J->mode, q, k, v, b, S, o, dk, dv);
     if (J->snorm) {
       double n2 = 0.0;
       for (size_t e = 0; e < ss; ++e) n2 += S[e] * S[e];
@@ -147,15 +188,12 @@ static void* run_range(void* arg) {
  *   snorm [nh, T] or NULL              (out: ||S_t||_F after each token)
  * nthreads <= 1 runs on the calling thread. Returns 0, or -1 on bad sizes.
  */
-int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
-                    const double* beta, const double* s0, double* o, double* s_final,
-                    double* snorm, long nh, long T, int dk, int dv, int nthreads) {
-  if (nh < 0 || T < 0 || dk < 1 || dv < 1) return -1;
+static int run_heads(oracle_job base, int nthreads) {
+  const long nh = base.nh;
+  if (nh < 0 || base.T < 0 || base.dk < 1 || base.dv < 1) return -1;
   if (nh == 0) return 0;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > nh) nthreads = (int)nh;
-
-  oracle_job base = {mode, q, k, v, beta, s0, o, s_final, snorm, nh, T, dk, dv, 0, nh};
   if (nthreads == 1) {
     run_range(&base);
     return 0;
@@ -174,6 +212,23 @@ int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
   free(th);
   free(jobs);
   return 0;
+}
+
+int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
+                    const double* beta, const double* s0, double* o, double* s_final,
+                    double* snorm, long nh, long T, int dk, int dv, int nthreads) {
+  oracle_job base = {mode, q, k, v, beta, s0, o, s_final, snorm, NULL, nh, T, dk, dv, 0, nh};
+  return run_heads(base, nthreads);
+}
+
+/* The gated variant over nh heads: as efla_oracle_fwd, with log_g [nh, T]
+ * the per-token log-decays (efla_oracle_step_gated). */
+int efla_oracle_fwd_gated(int mode, const double* q, const double* k, const double* v,
+                          const double* beta, const double* log_g, const double* s0, double* o,
+                          double* s_final, long nh, long T, int dk, int dv, int nthreads) {
+  if (!log_g) return -1;
+  oracle_job base = {mode, q, k, v, beta, s0, o, s_final, NULL, log_g, nh, T, dk, dv, 0, nh};
+  return run_heads(base, nthreads);
 }
 
 /* ---------------------------------------------------------------------------

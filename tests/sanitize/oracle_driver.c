@@ -20,6 +20,11 @@ int efla_oracle_fwd(int mode, const double* q, const double* k, const double* v,
                     const double* beta, const double* s0, double* o, double* s_final,
                     double* snorm, long nh, long T, int dk, int dv, int nthreads);
 void efla_oracle_coef_grad(int mode, double beta, double lam, double* dbeta, double* dlam);
+void efla_oracle_step_gated(int mode, const double* q, const double* k, const double* v, double beta,
+                            double log_g, double* S, double* o, int dk, int dv);
+int efla_oracle_fwd_gated(int mode, const double* q, const double* k, const double* v,
+                          const double* beta, const double* log_g, const double* s0, double* o,
+                          double* s_final, long nh, long T, int dk, int dv, int nthreads);
 int efla_oracle_bwd(int mode, const double* q, const double* k, const double* v,
                     const double* beta, const double* s0, const double* dout, const double* dsT,
                     double* dq, double* dk, double* dv, double* dbeta, double* ds0, long nh,
@@ -78,10 +83,21 @@ int main(void) {
   double* z = (double*)calloc((size_t)nh * T, sizeof(double));
   efla_oracle_fwd(0, q, k, v, z, s0, o, sf, NULL, nh, T, dk, dv, 2);
   if (memcmp(sf, s0, sizeof(double) * (size_t)nh * dk * dv) != 0) ++fails;
+  /* gated variant: zero log-decays reproduce the ungated forward to rounding */
+  for (int th = 1; th <= 3; th += 2) {
+    double* sf2 = (double*)calloc((size_t)nh * dk * dv, sizeof(double));
+    efla_oracle_fwd(0, q, k, v, beta, s0, o, sf, NULL, nh, T, dk, dv, 1);
+    if (efla_oracle_fwd_gated(0, q, k, v, beta, z, s0, o, sf2, nh, T, dk, dv, th) != 0) ++fails;
+    for (long e = 0; e < nh * dk * dv; ++e)
+      if (fabs(sf2[e] - sf[e]) > 1e-9 * (1.0 + fabs(sf[e]))) ++fails;
+    free(sf2);
+  }
+  if (efla_oracle_fwd_gated(0, q, k, v, beta, NULL, s0, o, sf, nh, T, dk, dv, 1) != -1) ++fails;
   /* one step on one head, no output */
   double S[24];
   memcpy(S, s0, sizeof(S));
   efla_oracle_step(0, q, k, v, 0.5, S, NULL, dk, dv);
+  efla_oracle_step_gated(0, q, k, v, 0.5, -0.3, S, NULL, dk, dv);
   free(z), free(q), free(k), free(v), free(beta), free(s0), free(dout), free(dsT), free(o), free(sf), free(sn);
   printf("oracle sanitizer driver: %d failed checks\n", fails);
   return fails ? 1 : 0;
