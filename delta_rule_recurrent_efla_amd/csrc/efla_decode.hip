@@ -9,11 +9,12 @@
 //   u = a (v - p)                          (S_new = S + k u^T)
 //   o = S_new^T q = r + (k.q) u
 //   S <- S + k u^T                         (one write pass over S)
-// The step is HBM-bound (0.75 flop per state byte), so the kernel is a
-// single coalesced read and write of the state: each workgroup owns a
-// 32-column slice of one head, holds it in registers between the two passes
-// and reduces the column partial sums by lane exchanges inside each wave and
-// through LDS across the four waves.
+// The step is HBM-bound (0.75 flop per state byte) and, at serving batch
+// sizes, latency-bound: one read of the state, a reduction, one write. Each
+// workgroup is a single wave64 that owns a VB-column slice of one head and
+// keeps it in registers between the read and the write; every reduction is
+// a cross-lane exchange inside the wave, so the step has no LDS round trip
+// and no workgroup barrier.
 
 #include "efla_device.hpp"
 
@@ -30,105 +31,90 @@ struct DecodeArgs {
   int coef;  // step coefficient rule (gate_coef)
 };
 
-template <typename CT, int D, int VB>
-__global__ __launch_bounds__(256) void efla_decode_kernel(DecodeArgs a) {
-  // Thread layout: lane l of wave wv reads float4 column group cg = l % CG
-  // of rows rg + RG i, rg = l / CG + (64 / CG) wv. The column partial sums
-  // are reduced over the row groups of a wave by lane exchanges, then over
-  // the four waves through LDS.
-  constexpr int CG = VB / 4;               // float4 column groups per row
-  constexpr int RG = 256 / CG;             // row groups
-  constexpr int RPT = (D + RG - 1) / RG;   // rows per thread
-  __shared__ float sk[D], sq[D], sv[VB], su[VB];
-  __shared__ floatx4 sp[4][CG], sr[4][CG];
-  __shared__ float slam, skq;
+// RPT consecutive elements of a d-vector starting at element e0 (a multiple
+// of RPT), upcast to fp32: 16-byte loads when the run is a multiple of 16
+// bytes, else element loads.
+template <typename CT, int RPT>
+__device__ __forceinline__ void load_run(const CT* p, int e0, float (&x)[RPT]) {
+  constexpr int VE = 16 / (int)sizeof(CT);
+  if constexpr ((RPT * (int)sizeof(CT)) % 16 == 0) {
+    typedef typename std::conditional<sizeof(CT) == 2, bf16x8, floatx4>::type V;
+#pragma unroll
+    for (int j = 0; j < RPT / VE; ++j) {
+      const V w = *(const V*)(p + e0 + VE * j);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) x[VE * j + e] = to_f32(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x[i] = to_f32(p[e0 + i]);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+// Sum over the lanes that share lane % CG (the row groups of one column
+// group); every lane receives its column group's total.
+template <int CG>
+__device__ __forceinline__ float rowgroup_sum(float x) {
+#pragma unroll
+  for (int off = CG; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename CT, int D, int VB>
+__global__ __launch_bounds__(64) void efla_decode_kernel(DecodeArgs a) {
+  // lane = rg * CG + cg: column group cg holds columns v0 + 4 cg .. + 3,
+  // row group rg holds the RPT consecutive rows rg * RPT ..
+  constexpr int CG = VB / 4;
+  constexpr int RG = 64 / CG;
+  constexpr int RPT = D / RG;
+  static_assert(VB % 4 == 0 && 64 % CG == 0 && D % RG == 0 && RPT >= 1, "slice shape");
+  const int lane = threadIdx.x;
+  const int cg = lane % CG, rg = lane / CG;
   const int head = blockIdx.x / a.nvt;
   const int v0 = (blockIdx.x % a.nvt) * VB;
-  const int cg = tid % CG, rg = tid / CG;
+  const int r0 = rg * RPT;
 
-  const CT* qg = (const CT*)a.q + (size_t)head * D;
-  const CT* kg = (const CT*)a.k + (size_t)head * D;
-  const CT* vg = (const CT*)a.v + (size_t)head * D;
-  float* S = a.state + (size_t)head * D * D;
-
+  float* S = a.state + (size_t)head * D * D + (size_t)r0 * D + v0 + 4 * cg;
   floatx4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    if (r < D) s[i] = *(const floatx4*)(S + (size_t)r * D + v0 + 4 * cg);
-  }
-  if (tid < D) {
-    sk[tid] = to_f32(kg[tid]);
-    sq[tid] = to_f32(qg[tid]);
-  }
-  if (tid < VB) sv[tid] = to_f32(vg[v0 + tid]);
-  __syncthreads();
+  for (int i = 0; i < RPT; ++i) s[i] = *(const floatx4*)(S + (size_t)i * D);
+  float kr[RPT], qr[RPT];
+  load_run<CT, RPT>((const CT*)a.k + (size_t)head * D, r0, kr);
+  load_run<CT, RPT>((const CT*)a.q + (size_t)head * D, r0, qr);
+  float vv[4];
+  load_run<CT, 4>((const CT*)a.v + (size_t)head * D, v0 + 4 * cg, vv);
+  const float b = to_f32(((const CT*)a.beta)[head]);
 
-  if (wv == 0) {
-    float l = 0.f, kq = 0.f;
-    for (int j = lane; j < D; j += 64) {
-      l += sk[j] * sk[j];
-      kq += sk[j] * sq[j];
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      l += __shfl_xor(l, off);
-      kq += __shfl_xor(kq, off);
-    }
-    if (lane == 0) {
-      slam = l;
-      skq = kq;
-    }
-  }
-  floatx4 p = {0.f, 0.f, 0.f, 0.f}, rr = {0.f, 0.f, 0.f, 0.f};
+  // lambda = k.k and k.q: partial sums over this lane's rows, completed
+  // across the row groups
+  float lam = 0.f, kq = 0.f;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    if (r < D) {
-      p += sk[r] * s[i];
-      rr += sq[r] * s[i];
-    }
+    lam += kr[i] * kr[i];
+    kq += kr[i] * qr[i];
   }
-  // sum over the row groups of this wave: lanes that differ in the bits
-  // above the column-group bits
-#pragma unroll
-  for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[e] += __shfl_xor(p[e], off);
-      rr[e] += __shfl_xor(rr[e], off);
-    }
-  }
-  if (lane < CG) {
-    sp[wv][lane] = p;
-    sr[wv][lane] = rr;
-  }
-  __syncthreads();
-
-  if (tid < VB) {
-    const int j = tid;
-    float pj = 0.f, rj = 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      pj += sp[x][j >> 2][j & 3];
-      rj += sr[x][j >> 2][j & 3];
-    }
-    const float al = gate_coef(a.coef, to_f32(((const CT*)a.beta)[head]), slam);
-    const float u = al * (sv[j] - pj);
-    su[j] = u;
-    ((CT*)a.o)[(size_t)head * D + v0 + j] = from_f32<CT>(rj + skq * u);
-  }
-  __syncthreads();
-
-  const floatx4 u4 = *(const floatx4*)&su[4 * cg];
+  // p = S^T k and r = S^T q for this lane's four columns
+  floatx4 p = {0.f, 0.f, 0.f, 0.f}, r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int r = rg + RG * i;
-    if (r < D) *(floatx4*)(S + (size_t)r * D + v0 + 4 * cg) = s[i] + sk[r] * u4;
+    p += kr[i] * s[i];
+    r += qr[i] * s[i];
   }
+  lam = rowgroup_sum<CG>(lam);
+  kq = rowgroup_sum<CG>(kq);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p[e] = rowgroup_sum<CG>(p[e]);
+    r[e] = rowgroup_sum<CG>(r[e]);
+  }
+  // u = a (v - p): S_new = S + k u^T; o = S_new^T q = r + (k.q) u
+  const float al = gate_coef(a.coef, b, lam);
+  floatx4 u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = al * (vv[e] - p[e]);
+  if (rg == 0) store4((CT*)a.o + (size_t)head * D + v0 + 4 * cg, r + kq * u);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) *(floatx4*)(S + (size_t)i * D) = s[i] + kr[i] * u;
 }
 
 template <typename CT, int D>
@@ -136,8 +122,7 @@ static hipError_t launch_decode(const DecodeArgs& in, int NH, hipStream_t stream
   constexpr int VB = D < 32 ? D : 32;
   DecodeArgs a = in;
   a.nvt = D / VB;
-  dim3 grid((unsigned)(NH * a.nvt)), block(256);
-  hipLaunchKernelGGL((efla_decode_kernel<CT, D, VB>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((efla_decode_kernel<CT, D, VB>), dim3((unsigned)(NH * a.nvt)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
