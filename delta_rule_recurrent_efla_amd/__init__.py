@@ -35,6 +35,7 @@ STATUS_NAMES = {
     4: "EFLA_ERR_MISALIGNED",
     5: "EFLA_ERR_WORKSPACE",
     6: "EFLA_ERR_HIP",
+    7: "EFLA_ERR_SCRATCH_LIMIT",
 }
 
 # Step coefficient rules (efla_coef): the exact flow, explicit Euler (the
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.efla_bwd_chunked_saved.argtypes = [vp] * 12 + [sz] + [i] * 8 + [vp]
         lib.efla_fwd_chunked_train.restype = i
         lib.efla_fwd_chunked_train.argtypes = [vp] * 8 + [sz] + [i] * 8 + [vp]
+        lib.efla_fwd_chunked_noalloc.restype = i
+        lib.efla_fwd_chunked_noalloc.argtypes = [vp] * 7 + [i] * 8 + [vp]
         lib.efla_status_string.restype = ctypes.c_char_p
         lib.efla_status_string.argtypes = [i]
         _lib = lib
@@ -194,6 +197,36 @@ def efla_fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: to
     _raise(st)
     _keep(stream, ws, *own)
     return o, s_final
+
+
+def efla_fwd_chunked_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                             s0: Optional[torch.Tensor], o: torch.Tensor, s_final: Optional[torch.Tensor],
+                             chunk: int = 64, stream=None, coef="exact") -> None:
+    """efla_fwd_chunked through the C entry point that allocates nothing: the
+    caller passes o (and s_final, or None) and the library's fixed scratch
+    serves the time-segmented path. Same checks as efla_fwd_chunked; calls
+    that overlap in time on one GPU must not be made."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape != q.shape or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, dev, (B, H, d, d))
+    _require(o, "o", dt, dev, (B, H, T, d))
+    if s_final is not None:
+        _require(s_final, "s_final", torch.float32, dev, (B, H, d, d))
+    st = lib.efla_fwd_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(s0), _ptr(o),
+                                      _ptr(s_final), B, H, T, d, d, int(chunk), _coef(coef),
+                                      _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
 
 
 def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

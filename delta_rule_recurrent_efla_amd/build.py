@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libefla.so")
 
-SOURCES = ["efla_api.hip", "efla_chunked.hip", "efla_decode.hip", "efla_backward.hip"]
+SOURCES = ["efla_api.hip", "efla_chunked.hip", "efla_decode.hip", "efla_backward.hip", "efla_noalloc.hip"]
 # measurement-only kernels (achievable MFMA rate and streaming bandwidth),
 # linked into a separate library that only the benchmark loads
 BENCH_SOURCES = ["bench_peaks.hip"]

@@ -181,6 +181,8 @@ extern "C" const char* efla_status_string(efla_status s) {
     case EFLA_ERR_MISALIGNED: return "EFLA_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
     case EFLA_ERR_WORKSPACE: return "EFLA_ERR_WORKSPACE: workspace too small";
     case EFLA_ERR_HIP: return "EFLA_ERR_HIP: the HIP runtime reported a launch error";
+    case EFLA_ERR_SCRATCH_LIMIT:
+      return "EFLA_ERR_SCRATCH_LIMIT: the sizes need more workspace than the no-allocation entry's fixed scratch";
   }
   return "EFLA_ERR_UNKNOWN";
 }

@@ -86,7 +86,8 @@ typedef EFLA_ENUM(efla_status_e) {
   EFLA_ERR_UNSUPPORTED = 3,  /* head dim, chunk size, dtype or coefficient outside the supported set */
   EFLA_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned */
   EFLA_ERR_WORKSPACE = 5,    /* workspace smaller than efla_fwd_chunked_workspace_bytes() */
-  EFLA_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+  EFLA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch */
+  EFLA_ERR_SCRATCH_LIMIT = 7 /* efla_fwd_chunked_noalloc: the sizes need more than its fixed scratch */
 } efla_status;
 
 /*
@@ -128,6 +129,27 @@ efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const 
                              const float* s0, void* o, float* s_final, void* workspace,
                              size_t workspace_bytes, int B, int H, int T, int d_k, int d_v,
                              int chunk, efla_coef coef, efla_dtype dt, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * efla_fwd_chunked with no workspace argument. Arguments, layouts, results
+ * and errors are those of efla_fwd_chunked. Where efla_fwd_chunked needs a
+ * workspace (the time-segmented path), this call uses a fixed device array
+ * of EFLA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; every size the segmented path takes fits (at most
+ * 383 d^2 fp32 values), and a size that would not returns
+ * EFLA_ERR_SCRATCH_LIMIT before any launch. The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device that needs the array looks up its device address. All
+ * calls on one GPU share that array: calls that overlap in time on one GPU
+ * (other streams, other host threads) must not be made.
+ */
+#define EFLA_NOALLOC_SCRATCH_BYTES (24u << 20)
+efla_status efla_fwd_chunked_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                                     const float* s0, void* o, float* s_final, int B, int H, int T,
+                                     int d_k, int d_v, int chunk, efla_coef coef, efla_dtype dt,
+                                     void* stream);
 
 /*
  * One token per head, token-serial (the recurrent decode form; section 整体框架
