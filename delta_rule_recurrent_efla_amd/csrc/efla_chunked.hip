@@ -563,8 +563,8 @@ struct __attribute__((aligned(16))) PipeSmem {
   static constexpr int VS = BV + ((32 - (int)sizeof(CT) * BV % 64 + 64) % 64) / (int)sizeof(CT);
   static constexpr int TDS = 32 / (int)sizeof(CT) + (sizeof(CT) == 4 ? 16 : 0);  // 32 or 96 bytes
   struct Buf {
-    CT K[C][DP];       // keys, column-permuted rows
-    CT Q[C][DP];       // queries, column-permuted rows
+    CT K[C][DP];       // keys, row-major (column-permuted for bf16, d = 16)
+    CT Q[C][DP];       // queries, likewise
     CT V[C][VS];       // value slice, natural layout
     CT T[C][CP];       // (I + A)^{-1}, permuted; only the lower block triangle is read
     CT M[C][CP];       // lower-incl-diag(Q K^T), permuted; only J <= I blocks are read
@@ -660,6 +660,17 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   constexpr int LDK = Sm::DP;
   constexpr int LDV = Sm::VS;
   constexpr int NST = 64 * NSW;  // state-group threads
+  // Key order of the state rows. bf16 MFMA operands take 8 k values per lane
+  // in the order (4 rows of accumulator tile 2f, 4 rows of tile 2f + 1), so
+  // a state tile feeds the next product straight from its registers only if
+  // the keys it multiplies come in that same order. With d >= 32 the state
+  // row r holds key pcol(r) (a permutation inside each 32-key block): the K
+  // and Q tiles can then stay in natural column order in LDS, staged with
+  // whole 16-byte stores, and K^T is read transposed at pcol-mapped
+  // addresses. With d = 16 (one 16-row tile) pcol is no permutation of the
+  // keys; there the state rows are natural and K, Q are stored permuted.
+  constexpr bool SROWP = sizeof(CT) == 2 && D >= 32;
+  auto skey = [](int r) { return SROWP ? MM::pcol(r) : r; };
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
   static_assert(!SUMMARY || NSW % 2 == 0, "summary state waves come in pairs");
   static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
@@ -720,8 +731,8 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = NEG ? -s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li]
-                                 : s0p[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li];
+            sacc[c][rt][e] = NEG ? -s0p[(size_t)skey(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li]
+                                 : s0p[(size_t)skey(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + c) + li];
     }
     if (SUMMARY && owner && ident) {
 #pragma unroll
@@ -730,7 +741,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc[c][rt][e] = (16 * rt + 4 * g + e == v0 + 16 * (wl * CPW + c) + li) ? -1.f : 0.f;
+            sacc[c][rt][e] = (skey(16 * rt + 4 * g + e) == v0 + 16 * (wl * CPW + c) + li) ? -1.f : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
@@ -761,11 +772,13 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (wl * CPW + cc) + li;
-              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(sacc[cc][rt]);
-              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
+              // rows skey(16 rt + 4g) + e, e = 0..3: 4 consecutive keys
+              const int kr = skey(16 * rt + 4 * g);
+              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + kr] = Mma<bf16>::cvt4(sacc[cc][rt]);
+              else *(floatx4*)&dst[(size_t)col * D + kr] = sacc[cc][rt];
               if (a.s_chunks_n) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
+                for (int e = 0; e < 4; ++e) dsn[(size_t)(kr + e) * D + col] = sacc[cc][rt][e];
               }
             }
         }
@@ -932,7 +945,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         for (int rt = 0; rt < NKT; ++rt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sf[(size_t)(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + cc) + li] = NEG ? -sacc[cc][rt][e] : sacc[cc][rt][e];
+            sf[(size_t)skey(16 * rt + 4 * g + e) * D + v0 + 16 * (wl * CPW + cc) + li] = NEG ? -sacc[cc][rt][e] : sacc[cc][rt][e];
     }
   } else if (w < NSW + 2) {
     // ======================= solvers (prep waves 0, 1) =======================
@@ -1293,8 +1306,13 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
             const int idx = lt + NLT * j;
             if (idx < C * VPR) {
               const int r = idx / VPR, cv = idx % VPR;
-              st_perm(&B.K[r][0], cv * VE, kreg[j]);
-              st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+              if constexpr (SROWP) {
+                *(Vec*)&B.K[r][cv * VE] = kreg[j];  // 16-byte aligned rows
+                *(Vec*)&B.Q[r][cv * VE] = qreg[j];
+              } else {
+                st_perm(&B.K[r][0], cv * VE, kreg[j]);
+                st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+              }
             }
           }
 #pragma unroll
