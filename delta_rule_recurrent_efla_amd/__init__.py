@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.efla_fwd_chunked_train.argtypes = [vp] * 8 + [sz] + [i] * 8 + [vp]
         lib.efla_fwd_chunked_noalloc.restype = i
         lib.efla_fwd_chunked_noalloc.argtypes = [vp] * 7 + [i] * 8 + [vp]
+        lib.efla_fwd_chunked_gated.restype = i
+        lib.efla_fwd_chunked_gated.argtypes = [vp] * 8 + [i] * 8 + [vp]
+        lib.efla_fwd_recurrent_step_gated.restype = i
+        lib.efla_fwd_recurrent_step_gated.argtypes = [vp] * 7 + [i] * 6 + [vp]
         lib.efla_status_string.restype = ctypes.c_char_p
         lib.efla_status_string.argtypes = [i]
         _lib = lib
@@ -227,6 +231,81 @@ def efla_fwd_chunked_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
                                       _ptr(s_final), B, H, T, d, d, int(chunk), _coef(coef),
                                       _DTYPES[dt], _stream(dev, stream))
     _raise(st)
+
+
+def efla_fwd_chunked_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                           log_g: torch.Tensor, s0: Optional[torch.Tensor] = None, chunk: int = 64,
+                           o: Optional[torch.Tensor] = None, s_final: Optional[torch.Tensor] = None,
+                           return_state: bool = True, stream=None, coef="exact"
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Gated EFLA forward: S_t = g_t (I - c_t k_t k_t^T) S_{t-1} + c_t k_t v_t^T
+    with g_t = exp(log_g_t); log_g [B,H,T] fp32 (values <= 0). Everything else
+    as efla_fwd_chunked."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape != q.shape or beta.shape != (B, H, T):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    _require(log_g, "log_g", torch.float32, dev, (B, H, T))
+    if s0 is not None:
+        _require(s0, "s0", torch.float32, dev, (B, H, d, d))
+    own = []
+    if o is None:
+        o = torch.empty((B, H, T, d), dtype=dt, device=dev)
+        own.append(o)
+    else:
+        _require(o, "o", dt, dev, (B, H, T, d))
+    if s_final is None and return_state:
+        s_final = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+        own.append(s_final)
+    elif s_final is not None:
+        _require(s_final, "s_final", torch.float32, dev, (B, H, d, d))
+    st = lib.efla_fwd_chunked_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_g), _ptr(s0),
+                                    _ptr(o), _ptr(s_final), B, H, T, d, d, int(chunk), _coef(coef),
+                                    _DTYPES[dt], _stream(dev, stream))
+    _raise(st)
+    _keep(stream, *own)
+    return o, s_final
+
+
+def efla_fwd_recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  beta: torch.Tensor, log_g: torch.Tensor, state: torch.Tensor,
+                                  o: Optional[torch.Tensor] = None, stream=None,
+                                  coef="exact") -> torch.Tensor:
+    """One gated token per head: q, k, v [B,H,d]; beta [B,H]; log_g [B,H] fp32;
+    state [B,H,d,d] fp32 advanced in place. Returns o [B,H,d]."""
+    lib = load_library()
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d]")
+    B, H, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dt}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _require(t, name, dt, dev)
+    if k.shape != q.shape or v.shape != q.shape or beta.shape != (B, H):
+        raise ValueError("shape mismatch between q, k, v, beta")
+    _require(log_g, "log_g", torch.float32, dev, (B, H))
+    _require(state, "state", torch.float32, dev, (B, H, d, d))
+    own = None
+    if o is None:
+        o = own = torch.empty((B, H, d), dtype=dt, device=dev)
+    else:
+        _require(o, "o", dt, dev, (B, H, d))
+    st = lib.efla_fwd_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_g),
+                                           _ptr(state), _ptr(o), B, H, d, d, _coef(coef), _DTYPES[dt],
+                                           _stream(dev, stream))
+    _raise(st)
+    _keep(stream, own)
+    return o
 
 
 def efla_fwd_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -13,8 +13,12 @@ hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void
                                         int chunk, int coef, int is_bf16, hipStream_t stream);
 size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16);
 hipError_t efla_internal_launch_decode(const void* q, const void* k, const void* v,
-                                       const void* beta, float* state, void* o, int NH, int d,
-                                       int coef, int is_bf16, hipStream_t stream);
+                                       const void* beta, const float* log_g, float* state, void* o,
+                                       int NH, int d, int coef, int is_bf16, hipStream_t stream);
+hipError_t efla_internal_launch_chunked_gated(const void* q, const void* k, const void* v, const void* beta,
+                                              const float* log_g, const float* s0, void* o, float* s_final,
+                                              int NH, int T, int d, int chunk, int coef, int is_bf16,
+                                              hipStream_t stream);
 
 size_t efla_internal_bwd_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16);
 hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v, const void* beta,
@@ -41,11 +45,9 @@ bool coef_ok(efla_coef c) {
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-bool chunked_supported(int d, int chunk, efla_dtype dt) {
+bool chunked_supported(int d, int chunk, efla_dtype) {
   if (!head_dim_ok(d)) return false;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return false;
-  if (dt == EFLA_DTYPE_F32 && d == 128 && chunk == 64) return false;
-  return true;
+  return chunk == 16 || chunk == 32 || chunk == 64;
 }
 
 }  // namespace
@@ -95,9 +97,44 @@ extern "C" efla_status efla_fwd_recurrent_step(const void* q, const void* k, con
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) ||
       !elem_aligned(beta, dt))
     return EFLA_ERR_MISALIGNED;
-  const hipError_t e = efla_internal_launch_decode(q, k, v, beta, state, o, B * H, d_k,
+  const hipError_t e = efla_internal_launch_decode(q, k, v, beta, nullptr, state, o, B * H, d_k,
                                                    (int)coef, dt == EFLA_DTYPE_BF16,
                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
+}
+
+extern "C" efla_status efla_fwd_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                                     const void* beta, const float* log_g, float* state,
+                                                     void* o, int B, int H, int d_k, int d_v,
+                                                     efla_coef coef, efla_dtype dt, void* stream) {
+  if (!q || !k || !v || !beta || !log_g || !state || !o) return EFLA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
+  if (!head_dim_ok(d_k) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) ||
+      !elem_aligned(beta, dt) || !elem_aligned(log_g, EFLA_DTYPE_F32))
+    return EFLA_ERR_MISALIGNED;
+  const hipError_t e = efla_internal_launch_decode(q, k, v, beta, log_g, state, o, B * H, d_k, (int)coef,
+                                                   dt == EFLA_DTYPE_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
+}
+
+extern "C" efla_status efla_fwd_chunked_gated(const void* q, const void* k, const void* v, const void* beta,
+                                              const float* log_g, const float* s0, void* o, float* s_final,
+                                              int B, int H, int T, int d_k, int d_v, int chunk, efla_coef coef,
+                                              efla_dtype dt, void* stream) {
+  if (!q || !k || !v || !beta || !log_g || !o) return EFLA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || T < 1 || d_k != d_v) return EFLA_ERR_BAD_SHAPE;
+  if (dt != EFLA_DTYPE_F32 && dt != EFLA_DTYPE_BF16) return EFLA_ERR_UNSUPPORTED;
+  if (!chunked_supported(d_k, chunk, dt) || !coef_ok(coef)) return EFLA_ERR_UNSUPPORTED;
+  if ((long long)B * H > (1LL << 30) || (long long)T > (1LL << 30)) return EFLA_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(s0) ||
+      !aligned16(s_final) || !elem_aligned(beta, dt) || !elem_aligned(log_g, EFLA_DTYPE_F32))
+    return EFLA_ERR_MISALIGNED;
+  const hipError_t e = efla_internal_launch_chunked_gated(q, k, v, beta, log_g, s0, o, s_final, B * H, T, d_k,
+                                                          chunk, (int)coef, dt == EFLA_DTYPE_BF16,
+                                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? EFLA_OK : EFLA_ERR_HIP;
 }
 

@@ -71,6 +71,8 @@ struct ChunkedArgs {
   float* s_chunks_n;
   int seg_first;  // mode 2: first segment of this launch
   int nrun;       // modes 1 and 2: segments per head in this launch
+  // gated variant (4-wave kernel): per-token log-decay [head][T], fp32
+  const float* log_g;
 };
 
 template <typename CT>
@@ -95,6 +97,7 @@ struct __attribute__((aligned(16))) ChunkedSmem {
   float Adt[NB][16][20];  // fp32 diagonal blocks of A, transposed
   CT Td[NB][16][16 + P];  // (I + diagonal block of A)^{-1}
   float alpha[C];
+  float lg[C];            // gated variant: b_r, the log-decay summed over rows 0..r
 };
 
 template <typename CT, int D, int C, int BV>
@@ -136,7 +139,18 @@ struct SolvePlan {
   }
 };
 
-template <typename CT, int D, int C, int BV, int SWQ>
+// GATED: the gated variant S_t = g_t (I - c k k^T) S_{t-1} + c k v^T,
+// g_t = exp(log_g_t) (the reading taken of the papernotes note's "Gated
+// EFLA": Gated DeltaNet's update with the exact-flow coefficient). With
+// b_r = log_g summed over the chunk's rows 0..r and Gamma_r = exp(b_r), the
+// chunk's rows satisfy (I + A) U = diag(c) (V - diag(Gamma) K S) with
+// A = strictly-lower(diag(c) K K^T * exp(b_r - b_i)), so:
+//   W  = T diag(c Gamma) K,  U = T diag(c) V,  U' = U - W S
+//   O  = diag(Gamma) Q S + (lower-incl-diag(Q K^T) * exp(b_r - b_i)) U'
+//   S <- Gamma_C S + K^T diag(Gamma_C / Gamma) U'
+// Every exponent b_r - b_i (i <= r) and b_C - b_r is <= 0 for decays g <= 1;
+// a decay factor is only formed where the recurrence carries it.
+template <typename CT, int D, int C, int BV, int SWQ, bool GATED = false>
 __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
@@ -217,9 +231,12 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
   constexpr int NLV = (C * VPRV + 255) / 256;
   Vec kreg[NLK], qreg[NLK], vreg[NLV];
   CT breg[NLK];  // raw: converting here would make the prefetch wait for its loads
+  float lgreg = 0.f;  // gated: wave 0, lane r holds log_g of the chunk's row r
+  const float* lgg = GATED ? a.log_g + (size_t)head * T : nullptr;
   auto prefetch = [&](int chunk) {
     const int t0 = chunk * C;
     const int nval = min(C, T - t0);
+    if constexpr (GATED) lgreg = (tid < nval) ? lgg[t0 + tid] : 0.f;
 #pragma unroll
     for (int j = 0; j < NLK; ++j) {
       const int idx = tid + 256 * j;
@@ -282,6 +299,19 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
         }
       }
     }
+    if constexpr (GATED) {
+      // b_r: inclusive prefix sum of the chunk's log-decays (rows past T
+      // carry 0, so the last row holds b of the last valid token)
+      if (w == 0) {
+        float x = lgreg;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        if (lane < C) sm.lg[lane] = x;
+      }
+    }
     // issue the global loads of the next chunk; they land during this one
     if (ch + 1 < nchunks) prefetch(ch + 1);
     __syncthreads();
@@ -301,8 +331,16 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
         const int cb = 16 * J + 4 * g;
         const float al = sm.alpha[r];
         floatx4 ad;
+        if constexpr (GATED) {
+          // the decay factor is formed only below the diagonal, where its
+          // exponent b_r - b_i is what the recurrence carries
+          const float br = sm.lg[r];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] : 0.f;
+          for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] * __expf(br - sm.lg[cb + e]) : 0.f;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ad[e] = (cb + e < r) ? al * acc[e] : 0.f;
+        }
         MM::store_t(&sm.An[r][16 * J], -ad);
         return ad;
       };
@@ -357,8 +395,14 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
           const int r = 16 * I + li;
           const int cb = 16 * J + 4 * g;
           floatx4 m;
+          if constexpr (GATED) {
+            const float br = sm.lg[r];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) m[e] = (cb + e <= r) ? acc[e] : 0.f;
+            for (int e = 0; e < 4; ++e) m[e] = (cb + e <= r) ? acc[e] * __expf(br - sm.lg[cb + e]) : 0.f;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m[e] = (cb + e <= r) ? acc[e] : 0.f;
+          }
           MM::store_t(&sm.M[r][16 * J], m);
         }
       }
@@ -386,6 +430,12 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
       static_for<NB>([&](auto ib) {
         constexpr int i = decltype(ib)::value;
         const floatx4 al = *(const floatx4*)&sm.alpha[16 * i + 4 * g];
+        // gated: the key right-hand sides take diag(c Gamma), the values diag(c)
+        floatx4 alk = al;
+        if constexpr (GATED) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) alk[e] = al[e] * __expf(sm.lg[16 * i + 4 * g + e]);
+        }
         const Frag td = MM::template lds<1>(&sm.Td[i][li][0], 0, 0);
         Frag an[NFrag<CT, (i > 0 ? i : 1)>::value];
         if constexpr (i > 0) {
@@ -395,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          floatx4 y = al * MM::load4(rhs[t] + ((16 * i + 4 * g) ^ swz[t]));
+          floatx4 y = (plan.kind[w][t] == 1 ? alk : al) * MM::load4(rhs[t] + ((16 * i + 4 * g) ^ swz[t]));
           if constexpr (i > 0) {
 #pragma unroll
             for (int f = 0; f < NFrag<CT, i>::value; ++f) {
@@ -459,6 +509,15 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
           }
         }
       }
+      if constexpr (GATED) {
+        // O^T tile column li is token 16 ut + li: the Q S part takes Gamma
+#pragma unroll
+        for (int ut = 0; ut < NB; ++ut) {
+          const float gm = __expf(sm.lg[16 * ut + li]);
+#pragma unroll
+          for (int c = 0; c < CPW; ++c) oacc[c][ut] = oacc[c][ut] * gm;
+        }
+      }
       Frag uf[CPW][NFB];
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
@@ -473,6 +532,25 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
           for (int c = 0; c < CPW; ++c) oacc[c][ut] = MM::mma(oacc[c][ut], uf[c][f], mf);
         }
       });
+      if constexpr (GATED) {
+        // S <- Gamma_C S + K^T diag(Gamma_C / Gamma) U': rows 4g + e of U'
+        // tile ut are tokens 16 ut + 4g + e
+        const float bl = sm.lg[C - 1];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+#pragma unroll
+          for (int ut = 0; ut < NB; ++ut)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uacc[c][ut][e] *= __expf(bl - sm.lg[16 * ut + 4 * g + e]);
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) uf[c][f] = MM::template acc<NB>(uacc[c], f);
+        }
+        const float gc = __expf(bl);
+#pragma unroll
+        for (int c = 0; c < CPW; ++c)
+#pragma unroll
+          for (int rt = 0; rt < NKT; ++rt) sacc[c][rt] = sacc[c][rt] * gc;
+      }
 #pragma unroll
       for (int rt = 0; rt < NKT; ++rt) {
         const int row = 16 * rt + li;
@@ -1576,14 +1654,63 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
   return hipGetLastError();
 }
 
+// fp32 tiles of 64 tokens at d = 128 exceed the 160 KiB of LDS in every
+// kernel, so that size runs with 32-token chunks: the chunk length changes
+// the rounding order only (the chunked form is exact algebra for any length).
+static int effective_chunk(int d, int chunk, bool is_bf16) {
+  return (!is_bf16 && d == 128 && chunk == 64) ? 32 : chunk;
+}
+
 template <typename CT, int D>
 static hipError_t dispatch_chunk(const ChunkedArgs& a, int NH, int chunk, void* ws, hipStream_t s) {
   switch (chunk) {
     case 16: return launch_chunked<CT, D, 16>(a, NH, ws, s);
     case 32: return launch_chunked<CT, D, 32>(a, NH, ws, s);
     case 64:
-      if constexpr (sizeof(CT) == 4 && D == 128) return hipErrorInvalidValue;
+      if constexpr (sizeof(CT) == 4 && D == 128) return launch_chunked<CT, D, 32>(a, NH, ws, s);
       else return launch_chunked<CT, D, 64>(a, NH, ws, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Gated variant: the 4-wave kernel with the decay terms (GATED). Slices of
+// 16 state columns when 64-column slices would leave CUs idle.
+template <typename CT, int D, int C>
+static hipError_t launch_chunked_gated(const ChunkedArgs& in, int NH, hipStream_t stream) {
+  constexpr int BV = D < 64 ? D : 64;
+  static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");
+  ChunkedArgs a = in;
+  a.nvt = D / BV;
+  if (NH * a.nvt < 256 && BV > 16) {
+    a.nvt = D / 16;
+    hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, 16, EFLA_STATE_WAVES, true>), dim3((unsigned)(NH * a.nvt)),
+                       dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, BV, EFLA_STATE_WAVES, true>), dim3((unsigned)(NH * a.nvt)),
+                       dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename CT, int D>
+static hipError_t dispatch_chunk_gated(const ChunkedArgs& a, int NH, int chunk, hipStream_t s) {
+  switch (chunk) {
+    case 16: return launch_chunked_gated<CT, D, 16>(a, NH, s);
+    case 32: return launch_chunked_gated<CT, D, 32>(a, NH, s);
+    case 64:
+      if constexpr (sizeof(CT) == 4 && D == 128) return launch_chunked_gated<CT, D, 32>(a, NH, s);
+      else return launch_chunked_gated<CT, D, 64>(a, NH, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename CT>
+static hipError_t dispatch_d_gated(const ChunkedArgs& a, int NH, int d, int chunk, hipStream_t s) {
+  switch (d) {
+    case 16: return dispatch_chunk_gated<CT, 16>(a, NH, chunk, s);
+    case 32: return dispatch_chunk_gated<CT, 32>(a, NH, chunk, s);
+    case 64: return dispatch_chunk_gated<CT, 64>(a, NH, chunk, s);
+    case 128: return dispatch_chunk_gated<CT, 128>(a, NH, chunk, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1626,8 +1753,21 @@ static hipError_t dispatch_d(const ChunkedArgs& a, int NH, int d, int chunk, voi
 
 // Internal entries used by the C ABI layer (arguments already validated).
 size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16) {
-  const bool pipe = is_bf16 ? efla::pipelined_d<efla::bf16>(d, chunk) : efla::pipelined_d<float>(d, chunk);
-  return efla::seg_workspace_bytes(efla::seg_plan(NH, T, d, chunk, pipe), NH, d);
+  const int c = efla::effective_chunk(d, chunk, is_bf16 != 0);
+  const bool pipe = is_bf16 ? efla::pipelined_d<efla::bf16>(d, c) : efla::pipelined_d<float>(d, c);
+  return efla::seg_workspace_bytes(efla::seg_plan(NH, T, d, c, pipe), NH, d);
+}
+
+// Gated forward: one pass of the 4-wave kernel per (head, column slice); no
+// workspace.
+hipError_t efla_internal_launch_chunked_gated(const void* q, const void* k, const void* v, const void* beta,
+                                              const float* log_g, const float* s0, void* o, float* s_final,
+                                              int NH, int T, int d, int chunk, int coef, int is_bf16,
+                                              hipStream_t stream) {
+  efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef, nullptr, nullptr};
+  a.log_g = log_g;
+  if (is_bf16) return efla::dispatch_d_gated<efla::bf16>(a, NH, d, chunk, stream);
+  return efla::dispatch_d_gated<float>(a, NH, d, chunk, stream);
 }
 
 hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void* v,

@@ -28,7 +28,8 @@ struct DecodeArgs {
   float* state;
   void* o;
   int nvt;
-  int coef;  // step coefficient rule (gate_coef)
+  int coef;            // step coefficient rule (gate_coef)
+  const float* log_g;  // gated variant: [NH] per-head log-decay of this token
 };
 
 // RPT consecutive elements of a d-vector starting at element e0 (a multiple
@@ -60,7 +61,11 @@ __device__ __forceinline__ float rowgroup_sum(float x) {
   return x;
 }
 
-template <typename CT, int D, int VB>
+// GATED: the gated variant, S_new = g (I - c k k^T) S + c k v^T with
+// g = exp(log_g) per head (the plain reading of the papernotes note's
+// "Gated EFLA": Gated DeltaNet's update with the exact-flow coefficient).
+// Then u = c (v - g p), S_new = g S + k u^T and o = g r + (k.q) u.
+template <typename CT, int D, int VB, bool GATED>
 __global__ __launch_bounds__(64) void efla_decode_kernel(DecodeArgs a) {
   // lane = rg * CG + cg: column group cg holds columns v0 + 4 cg .. + 3,
   // row group rg holds the RPT consecutive rows rg * RPT ..
@@ -84,6 +89,7 @@ __global__ __launch_bounds__(64) void efla_decode_kernel(DecodeArgs a) {
   float vv[4];
   load_run<CT, 4>((const CT*)a.v + (size_t)head * D, v0 + 4 * cg, vv);
   const float b = to_f32(((const CT*)a.beta)[head]);
+  const float gd = GATED ? __expf(a.log_g[head]) : 1.f;
 
   // lambda = k.k and k.q: partial sums over this lane's rows, completed
   // across the row groups
@@ -110,11 +116,19 @@ __global__ __launch_bounds__(64) void efla_decode_kernel(DecodeArgs a) {
   // u = a (v - p): S_new = S + k u^T; o = S_new^T q = r + (k.q) u
   const float al = gate_coef(a.coef, b, lam);
   floatx4 u;
+  if constexpr (GATED) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) u[e] = al * (vv[e] - p[e]);
-  if (rg == 0) store4((CT*)a.o + (size_t)head * D + v0 + 4 * cg, r + kq * u);
+    for (int e = 0; e < 4; ++e) u[e] = al * (vv[e] - gd * p[e]);
+    if (rg == 0) store4((CT*)a.o + (size_t)head * D + v0 + 4 * cg, gd * r + kq * u);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) *(floatx4*)(S + (size_t)i * D) = s[i] + kr[i] * u;
+    for (int i = 0; i < RPT; ++i) *(floatx4*)(S + (size_t)i * D) = gd * s[i] + kr[i] * u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = al * (vv[e] - p[e]);
+    if (rg == 0) store4((CT*)a.o + (size_t)head * D + v0 + 4 * cg, r + kq * u);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) *(floatx4*)(S + (size_t)i * D) = s[i] + kr[i] * u;
+  }
 }
 
 template <typename CT, int D>
@@ -122,7 +136,10 @@ static hipError_t launch_decode(const DecodeArgs& in, int NH, hipStream_t stream
   constexpr int VB = D < 32 ? D : 32;
   DecodeArgs a = in;
   a.nvt = D / VB;
-  hipLaunchKernelGGL((efla_decode_kernel<CT, D, VB>), dim3((unsigned)(NH * a.nvt)), dim3(64), 0, stream, a);
+  if (a.log_g)
+    hipLaunchKernelGGL((efla_decode_kernel<CT, D, VB, true>), dim3((unsigned)(NH * a.nvt)), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((efla_decode_kernel<CT, D, VB, false>), dim3((unsigned)(NH * a.nvt)), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -140,9 +157,9 @@ static hipError_t dispatch_decode(const DecodeArgs& a, int NH, int d, hipStream_
 }  // namespace efla
 
 hipError_t efla_internal_launch_decode(const void* q, const void* k, const void* v,
-                                       const void* beta, float* state, void* o, int NH, int d,
-                                       int coef, int is_bf16, hipStream_t stream) {
-  efla::DecodeArgs a{q, k, v, beta, state, o, 1, coef};
+                                       const void* beta, const float* log_g, float* state, void* o,
+                                       int NH, int d, int coef, int is_bf16, hipStream_t stream) {
+  efla::DecodeArgs a{q, k, v, beta, state, o, 1, coef, log_g};
   if (is_bf16) return efla::dispatch_decode<efla::bf16>(a, NH, d, stream);
   return efla::dispatch_decode<float>(a, NH, d, stream);
 }

@@ -133,3 +133,13 @@ def random_case(seed: int, B: int, H: int, T: int, d: int, dtype: str = "f32",
     w = Workload("random", seed - 42, B, H, T, d, 16, dtype, "normal", k_rule, k_lo, k_hi,
                  beta_mu, s0_std)
     return make_inputs(w)
+
+
+def log_decay(seed: int, shape, mu: float = 2.0, scale: float = 1.0) -> torch.Tensor:
+    """Per-token log-decays for the gated variant, fp32: log(sigmoid(x)) with
+    x ~ N(mu, scale^2), so every decay g = exp(log_g) lies in (0, 1) (mu = 2
+    gives g around 0.88)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    x = mu + scale * torch.randn(tuple(shape), generator=gen, dtype=torch.float32)
+    return torch.nn.functional.logsigmoid(x).contiguous()

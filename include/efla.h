@@ -122,8 +122,10 @@ size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  *             overlap in time.
  *   chunk     tokens per chunk, one of 16, 32, 64. T need not be a multiple.
  *   coef      step coefficient (efla_coef; EFLA_COEF_EXACT for EFLA itself).
- * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64};
- * fp32 with d = 128 needs chunk <= 32. Anything else: EFLA_ERR_UNSUPPORTED.
+ * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ * fp32 with d = 128 and chunk 64 runs with 32-token chunks (64-token fp32
+ * tiles at d = 128 do not fit in LDS); the chunk length changes only the
+ * rounding order. Anything else: EFLA_ERR_UNSUPPORTED.
  */
 efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                              const float* s0, void* o, float* s_final, void* workspace,
@@ -166,6 +168,35 @@ efla_status efla_fwd_recurrent_step(const void* q, const void* k, const void* v,
                                     const void* beta, float* state, void* o, int B, int H,
                                     int d_k, int d_v, efla_coef coef, efla_dtype dt,
                                     void* stream);
+
+/*
+ * Gated EFLA. The papernotes note lists a gated variant ("Gated EFLA", main
+ * results table) and states that the exact flow upgrades Gated DeltaNet and
+ * any other delta-rule variant (key findings), without printing its update.
+ * The reading implemented: Gated DeltaNet's update with the exact-flow
+ * coefficient,
+ *   S_t = g_t (I - c_t k_t k_t^T) S_{t-1} + c_t k_t v_t^T,  o_t = S_t^T q_t,
+ * with the per-token decay g_t = exp(log_g_t) given as its natural log.
+ * log_g = 0 everywhere gives efla_fwd_chunked's recurrence.
+ *   log_g     [B, H, T] fp32 log-decays (4-byte aligned); values <= 0 keep
+ *             every decay factor the kernel forms at most 1.
+ * Every other argument, layout, supported size and error as in
+ * efla_fwd_chunked; no workspace is needed (one pass per head and column
+ * slice).
+ */
+efla_status efla_fwd_chunked_gated(const void* q, const void* k, const void* v, const void* beta,
+                                   const float* log_g, const float* s0, void* o, float* s_final,
+                                   int B, int H, int T, int d_k, int d_v, int chunk, efla_coef coef,
+                                   efla_dtype dt, void* stream);
+
+/*
+ * One gated token per head (the decode form of efla_fwd_chunked_gated):
+ * log_g is [B, H] fp32; every other argument as in efla_fwd_recurrent_step.
+ */
+efla_status efla_fwd_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                          const void* beta, const float* log_g, float* state,
+                                          void* o, int B, int H, int d_k, int d_v, efla_coef coef,
+                                          efla_dtype dt, void* stream);
 
 /*
  * Bytes of device workspace efla_bwd_chunked needs: per head, the state at

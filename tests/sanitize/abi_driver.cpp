@@ -20,8 +20,14 @@ hipError_t efla_internal_launch_chunked(const void*, const void*, const void*, c
   return hipSuccess;
 }
 size_t efla_internal_chunked_workspace_bytes(int, int, int, int, int) { return fwd_ws; }
-hipError_t efla_internal_launch_decode(const void*, const void*, const void*, const void*, float*, void*,
-                                       int, int, int, int, hipStream_t) {
+hipError_t efla_internal_launch_decode(const void*, const void*, const void*, const void*, const float*, float*,
+                                       void*, int, int, int, int, hipStream_t) {
+  ++launches;
+  return hipSuccess;
+}
+hipError_t efla_internal_launch_chunked_gated(const void*, const void*, const void*, const void*, const float*,
+                                              const float*, void*, float*, int, int, int, int, int, int,
+                                              hipStream_t) {
   ++launches;
   return hipSuccess;
 }
@@ -94,6 +100,19 @@ int main() {
   expect("step misaligned", efla_fwd_recurrent_step(P, P, P, P, (float*)M, P, 2, 3, 128, 128, X, BF, nullptr),
          EFLA_ERR_MISALIGNED, 0);
 
+  const float* G = (const float*)mem;
+  expect("gated ok", efla_fwd_chunked_gated(P, P, P, P, G, S, P, S, 2, 3, 100, 128, 128, 64, X, F32, nullptr),
+         EFLA_OK, 1);
+  expect("gated null gate", efla_fwd_chunked_gated(P, P, P, P, nullptr, S, P, S, 2, 3, 100, 64, 64, 64, X, BF,
+                                                   nullptr), EFLA_ERR_NULL_POINTER, 0);
+  expect("gated gate misaligned", efla_fwd_chunked_gated(P, P, P, P, (const float*)M, S, P, S, 2, 3, 100, 64, 64,
+                                                         64, X, BF, nullptr), EFLA_ERR_MISALIGNED, 0);
+  expect("gated chunk", efla_fwd_chunked_gated(P, P, P, P, G, S, P, S, 2, 3, 100, 64, 64, 8, X, BF, nullptr),
+         EFLA_ERR_UNSUPPORTED, 0);
+  expect("gated step ok", efla_fwd_recurrent_step_gated(P, P, P, P, G, S, P, 2, 3, 64, 64, X, BF, nullptr), EFLA_OK,
+         1);
+  expect("gated step null", efla_fwd_recurrent_step_gated(P, P, P, P, nullptr, S, P, 2, 3, 64, 64, X, BF,
+                                                          nullptr), EFLA_ERR_NULL_POINTER, 0);
   expect("bwd ok", efla_bwd_chunked(P, P, P, P, S, P, S, P, P, P, P, S, P, 64, 1, 2, 70, 32, 32, 32, X, BF,
                                     nullptr), EFLA_OK, 1);
   expect("bwd workspace", efla_bwd_chunked(P, P, P, P, S, P, S, P, P, P, P, S, P, 63, 1, 2, 70, 32, 32, 32, X,

@@ -69,7 +69,6 @@ def test_chunked_rejects_bad_arguments_before_launch():
     assert chunked(lib, chunk=8) == 3
     assert chunked(lib, chunk=128) == 3
     assert chunked(lib, dt=2) == 3
-    assert chunked(lib, dk=128, dv=128, chunk=64, dt=0) == 3  # fp32, d=128 needs chunk <= 32
     assert chunked(lib, coef=4) == 3
     assert chunked(lib, coef=-1) == 3
     assert chunked(lib, q=FAKE + 8) == 4
@@ -111,6 +110,11 @@ def test_workspace_query():
     # two segments: no maps, only the start states
     assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4133, 128, 128, 64, 1) == \
         2 * 2 * 128 * 128 * 4
+    # fp32 with d = 128 and chunk 64 runs (and plans its segments) with chunk 32
+    for T in (1000, 8229, 65536):
+        assert lib.efla_fwd_chunked_workspace_bytes(1, 2, T, 128, 128, 64, 0) == \
+            lib.efla_fwd_chunked_workspace_bytes(1, 2, T, 128, 128, 32, 0)
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 8229, 128, 128, 32, 0) > 0
     # unsupported or invalid sizes report 0
     assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 48, 1) == 0
     assert lib.efla_fwd_chunked_workspace_bytes(0, 16, 65536, 128, 128, 64, 1) == 0
@@ -166,7 +170,9 @@ def test_backward_workspace_query():
     nc, Tp = 4, 128
     per = 3 * nc * 64 * 64 + Tp * 64 + 3 * Tp + 4 * nc * 32 * 32
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 64, 64, 64, 0) == per * 4
-    assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 128, 128, 64, 0) == 0
+    # fp32, d = 128, C = 64 runs with chunk 32 as well
+    per = 3 * nc * 128 * 128 + Tp * 128 + 3 * Tp + 4 * nc * 32 * 32
+    assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 128, 128, 64, 0) == per * 4
     assert lib.efla_bwd_chunked_workspace_bytes(1, 1, 100, 48, 48, 64, 1) == 0
 
 
@@ -189,7 +195,6 @@ def test_train_forward_rejects_bad_arguments_before_launch():
     assert train(lib, B=0) == 2
     assert train(lib, dv=32) == 2
     assert train(lib, chunk=8) == 3
-    assert train(lib, dk=128, dv=128, chunk=64, dt=0) == 3
     assert train(lib, coef=7) == 3
     assert train(lib, q=FAKE + 8) == 4
     assert train(lib, ws=FAKE + 8) == 4
