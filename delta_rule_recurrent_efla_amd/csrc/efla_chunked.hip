@@ -746,9 +746,20 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // and Q tiles can then stay in natural column order in LDS, staged with
   // whole 16-byte stores, and K^T is read transposed at pcol-mapped
   // addresses. With d = 16 (one 16-row tile) pcol is no permutation of the
-  // keys; there the state rows are natural and K, Q are stored permuted.
-  constexpr bool SROWP = sizeof(CT) == 2 && D >= 32;
-  auto skey = [](int r) { return SROWP ? MM::pcol(r) : r; };
+  // keys; there the state rows are natural and K, Q are stored permuted. The
+  // state-saving passes (modes 2, 3) keep natural rows as well: they store
+  // the state every chunk, and the permuted store addresses cost them the
+  // register that keeps the pass without spills.
+  constexpr bool SROWP = sizeof(CT) == 2 && D >= 32 && !SAVE;
+#define skey(r) (SROWP ? MM::pcol(r) : (r))
+  // Where the chunk has four 16-row blocks and four loaders (bf16, C = 64,
+  // every pass mode but the summaries), loader L fetches the key rows of
+  // block L straight into MFMA operand layout. It then forms, one chunk
+  // ahead, the gate of those rows and the diagonal Gram block
+  // a_r (K_L K_L^T)_{rc}, c < r, and leaves it in LDS: the solvers' phase A
+  // starts at the forward substitution, with no key fetch, no Gram product
+  // and no LDS round trip of their own.
+  constexpr bool LGRAM = sizeof(CT) == 2 && NB == 4 && PM != 1 && D >= 32;
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
   static_assert(!SUMMARY || NSW % 2 == 0, "summary state waves come in pairs");
   static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
@@ -850,13 +861,14 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
 #pragma unroll
             for (int rt = 0; rt < NKT; ++rt) {
               const int col = v0 + 16 * (wl * CPW + cc) + li;
-              // rows skey(16 rt + 4g) + e, e = 0..3: 4 consecutive keys
-              const int kr = skey(16 * rt + 4 * g);
-              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + kr] = Mma<bf16>::cvt4(sacc[cc][rt]);
-              else *(floatx4*)&dst[(size_t)col * D + kr] = sacc[cc][rt];
+              // rows 16 rt + 4g + e, e = 0..3: 4 consecutive keys (the saving
+              // passes keep the state rows in natural key order)
+              static_assert(!SROWP, "saving passes keep natural state rows");
+              if constexpr (SBF) *(bf16x4*)&dsb[(size_t)col * D + 16 * rt + 4 * g] = Mma<bf16>::cvt4(sacc[cc][rt]);
+              else *(floatx4*)&dst[(size_t)col * D + 16 * rt + 4 * g] = sacc[cc][rt];
               if (a.s_chunks_n) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dsn[(size_t)(kr + e) * D + col] = sacc[cc][rt][e];
+                for (int e = 0; e < 4; ++e) dsn[(size_t)(16 * rt + 4 * g + e) * D + col] = sacc[cc][rt][e];
               }
             }
         }
@@ -1053,7 +1065,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           }
         }
       };
-      if constexpr (NDB > 0) load_rows(0);
+      if constexpr (NDB > 0 && !LGRAM) load_rows(0);
       // blocks of this solver's An copy left of its first column tile are
       // never computed; they are read only against zero blocks of X, so they
       // must hold zeros, not stale bits
@@ -1075,6 +1087,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         //      rows past T, which clears their rows of A)
         if constexpr (NDB > 0) {
           if (act) {
+           if constexpr (!LGRAM) {
             float al[NDB];
 #pragma unroll
             for (int i = 0; i < NDB; ++i) al[i] = B.alpha[16 * (PW + 2 * i) + li];
@@ -1102,6 +1115,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+           }
             if (g < NDB) {
               // column-parallel right-looking forward substitution in fp32:
               // lane group g = block PW + 2g, lane li = column li; once t_j is
@@ -1366,9 +1380,54 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           });
         }
       };
-      load_k(0);
-      load_qv(0);
-      gate_rows(0, sm.buf[0].alpha);
+      // LGRAM: this loader's block PW of key rows in MFMA operand layout:
+      // lane (g, li) holds row 16 PW + li, 16-byte pieces at columns
+      // 32 f + 8 g (the pieces' k order only has to agree between the two
+      // Gram operands, which are these same registers), and that row's beta
+      const int li0 = lane & 15, g0 = lane >> 4;
+      constexpr int NKB = LGRAM ? NFK : 1;
+      Vec kb[NKB];
+      CT kbeta;
+      unsigned kboff[NKB];
+      if constexpr (LGRAM) {
+#pragma unroll
+        for (int f = 0; f < NFK; ++f) kboff[f] = (unsigned)(((16 * PW + li0) * D + 32 * f + 8 * g0) * (int)sizeof(CT));
+      }
+      auto load_kb = [&](int chunk) {
+        const auto rk = chunk_rsrc(kg, chunk, 0);
+#pragma unroll
+        for (int f = 0; f < NKB; ++f) buf_load(rk, kboff[f], kb[f]);
+        const long long tok = (long long)chunk * C;
+        buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
+                 (unsigned)((16 * PW + li0) * (int)sizeof(CT)), kbeta);
+      };
+      // a of rows 16 PW + li of `chunk` (zero past T) and the strictly lower
+      // a_r G_rc of the block's Gram matrix, stored transposed for the
+      // solvers' column-parallel forward substitution
+      auto gate_gram = [&](int chunk, float* alpha) {
+        float lam = 0.f;
+#pragma unroll
+        for (int f = 0; f < NKB; ++f) lam += sumsq(kb[f]);
+        lam += __shfl_xor(lam, 16);
+        lam += __shfl_xor(lam, 32);
+        const int row = 16 * PW + li0;
+        const float al = row < min(C, T - chunk * C) ? gate_coef(a.coef, to_f32(kbeta), lam) : 0.f;
+        if (g0 == 0) alpha[row] = al;
+        floatx4 dg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, kb[f], kb[f]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
+      };
+      if constexpr (LGRAM) {
+        load_kb(0);
+        load_qv(0);
+        gate_gram(0, sm.buf[0].alpha);
+      } else {
+        load_k(0);
+        load_qv(0);
+        gate_rows(0, sm.buf[0].alpha);
+      }
       __syncthreads();
       for (int c = -1; c < nchunks; ++c) {
         const int n = c + 1;  // chunk being prepared
@@ -1379,6 +1438,24 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         // ---- phase A: stage chunk n (keys, queries, value slice)
         if (act) {
           // rows past T arrived as zeros
+          if constexpr (LGRAM) {
+            // kb[f] holds columns 32 f + 8 g .. + 7 of row 16 PW + li, stored
+            // in the key layout of this pass (natural, or column-permuted)
+#pragma unroll
+            for (int f = 0; f < NKB; ++f) {
+              if constexpr (SROWP) *(Vec*)&B.K[16 * PW + li][32 * f + 8 * g] = kb[f];
+              else st_perm(&B.K[16 * PW + li][0], 32 * f + 8 * g, kb[f]);
+            }
+#pragma unroll
+            for (int j = 0; j < NLK; ++j) {
+              const int idx = lt + NLT * j;
+              if (idx < C * VPR) {
+                const int r = idx / VPR, cv = idx % VPR;
+                if constexpr (SROWP) *(Vec*)&B.Q[r][cv * VE] = qreg[j];
+                else st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+              }
+            }
+          } else
 #pragma unroll
           for (int j = 0; j < NLK; ++j) {
             const int idx = lt + NLT * j;
@@ -1406,7 +1483,8 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         if constexpr (NA > 0) {
           if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
         }
-        load_k(min(n + 1, nchunks - 1));
+        if constexpr (LGRAM) load_kb(min(n + 1, nchunks - 1));
+        else load_k(min(n + 1, nchunks - 1));
         __syncthreads();
         // ---- phase B: load the queries and values of chunk n + 1; the rest
         //      of this wave's lower-incl-diag Q K^T tiles of chunk n (-> M)
@@ -1414,8 +1492,12 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         if constexpr (NJ > NA) {
           if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
         }
-        // a of chunk n + 1 (its keys arrived during this phase)
-        if (n + 1 < nchunks) gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
+        // a of chunk n + 1 (its keys arrived during this phase), and with
+        // LGRAM the diagonal Gram blocks the solvers invert in the next phase
+        if (n + 1 < nchunks) {
+          if constexpr (LGRAM) gate_gram(n + 1, sm.buf[(n + 1) & 1].alpha);
+          else gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
+        }
         __syncthreads();
       }
     };
@@ -1427,6 +1509,8 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
     }
   }
 }
+
+#undef skey
 
 // Workgroup -> pass index with the column slices of a head on one XCD (the
 // hardware deals workgroups to the 8 XCDs round robin): the slices read the
