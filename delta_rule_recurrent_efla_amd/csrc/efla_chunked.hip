@@ -1738,11 +1738,19 @@ static hipError_t launch_chunked(const ChunkedArgs& in, int NH, void* ws, hipStr
   return hipGetLastError();
 }
 
-// fp32 tiles of 64 tokens at d = 128 exceed the 160 KiB of LDS in every
-// kernel, so that size runs with 32-token chunks: the chunk length changes
-// the rounding order only (the chunked form is exact algebra for any length).
-static int effective_chunk(int d, int chunk, bool is_bf16) {
-  return (!is_bf16 && d == 128 && chunk == 64) ? 32 : chunk;
+// Chunk length the forward runs with. fp32 tiles of 64 tokens do not fit the
+// pipelined kernel's double-buffered LDS (and at d = 128 no kernel's), so
+// fp32 with chunk 64 runs the pipelined kernel with 32-token chunks when one
+// pass fills the GPU (>= 128 workgroups) and with 16-token chunks otherwise,
+// where the time-segmented schedule then has twice the chunks to split into
+// segments. Measured on MI355X (fp32, T = 2048): 32 heads at d = 64 340 ->
+// 166 us, 256 heads at d = 64 474 -> 294 us, 32 heads at d = 128 476 ->
+// 284 us. The chunk length changes the rounding order only: the chunked
+// form is exact algebra for any length.
+static int effective_chunk(int NH, int d, int chunk, bool is_bf16) {
+  if (is_bf16 || chunk != 64) return chunk;
+  const long long W = (long long)NH * (d / (d < 64 ? d : 64));
+  return W >= 128 ? 32 : 16;
 }
 
 template <typename CT, int D>
@@ -1837,7 +1845,7 @@ static hipError_t dispatch_d(const ChunkedArgs& a, int NH, int d, int chunk, voi
 
 // Internal entries used by the C ABI layer (arguments already validated).
 size_t efla_internal_chunked_workspace_bytes(int NH, int T, int d, int chunk, int is_bf16) {
-  const int c = efla::effective_chunk(d, chunk, is_bf16 != 0);
+  const int c = efla::effective_chunk(NH, d, chunk, is_bf16 != 0);
   const bool pipe = is_bf16 ? efla::pipelined_d<efla::bf16>(d, c) : efla::pipelined_d<float>(d, c);
   return efla::seg_workspace_bytes(efla::seg_plan(NH, T, d, c, pipe), NH, d);
 }
@@ -1859,8 +1867,9 @@ hipError_t efla_internal_launch_chunked(const void* q, const void* k, const void
                                         float* s_final, void* workspace, int NH, int T, int d,
                                         int chunk, int coef, int is_bf16, hipStream_t stream) {
   efla::ChunkedArgs a{q, k, v, beta, s0, o, s_final, T, 1, 0, 0, 1, nullptr, nullptr, coef, nullptr, nullptr};
-  if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, chunk, workspace, stream);
-  return efla::dispatch_d<float>(a, NH, d, chunk, workspace, stream);
+  const int c = efla::effective_chunk(NH, d, chunk, is_bf16 != 0);
+  if (is_bf16) return efla::dispatch_d<efla::bf16>(a, NH, d, c, workspace, stream);
+  return efla::dispatch_d<float>(a, NH, d, c, workspace, stream);
 }
 
 // Pass mode 2 of the pipelined kernel: one plain pass that stores the state at

@@ -123,9 +123,10 @@ size_t efla_fwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  *   chunk     tokens per chunk, one of 16, 32, 64. T need not be a multiple.
  *   coef      step coefficient (efla_coef; EFLA_COEF_EXACT for EFLA itself).
  * Supported (d, chunk, dtype): d in {16, 32, 64, 128}; chunk in {16, 32, 64}.
- * fp32 with d = 128 and chunk 64 runs with 32-token chunks (64-token fp32
- * tiles at d = 128 do not fit in LDS); the chunk length changes only the
- * rounding order. Anything else: EFLA_ERR_UNSUPPORTED.
+ * fp32 with chunk 64 runs with 32-token chunks when B H d / min(d, 64) >=
+ * 128 and with 16-token chunks otherwise (64-token fp32 tiles do not fit the
+ * pipelined kernel's LDS); the chunk length changes only the rounding order.
+ * Anything else: EFLA_ERR_UNSUPPORTED.
  */
 efla_status efla_fwd_chunked(const void* q, const void* k, const void* v, const void* beta,
                              const float* s0, void* o, float* s_final, void* workspace,

@@ -110,11 +110,15 @@ def test_workspace_query():
     # two segments: no maps, only the start states
     assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4133, 128, 128, 64, 1) == \
         2 * 2 * 128 * 128 * 4
-    # fp32 with d = 128 and chunk 64 runs (and plans its segments) with chunk 32
-    for T in (1000, 8229, 65536):
-        assert lib.efla_fwd_chunked_workspace_bytes(1, 2, T, 128, 128, 64, 0) == \
-            lib.efla_fwd_chunked_workspace_bytes(1, 2, T, 128, 128, 32, 0)
-    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 8229, 128, 128, 32, 0) > 0
+    # fp32 with chunk 64 runs (and plans its segments) with chunk 16 when one
+    # pass would leave the GPU idle (< 128 workgroups), else with chunk 32
+    for d in (16, 64, 128):
+        for T in (1000, 8229, 65536):
+            assert lib.efla_fwd_chunked_workspace_bytes(1, 2, T, d, d, 64, 0) == \
+                lib.efla_fwd_chunked_workspace_bytes(1, 2, T, d, d, 16, 0)
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 8229, 128, 128, 16, 0) > 0
+    assert lib.efla_fwd_chunked_workspace_bytes(8, 16, 9000, 128, 128, 64, 0) == \
+        lib.efla_fwd_chunked_workspace_bytes(8, 16, 9000, 128, 128, 32, 0) == 0
     # unsupported or invalid sizes report 0
     assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 48, 1) == 0
     assert lib.efla_fwd_chunked_workspace_bytes(0, 16, 65536, 128, 128, 64, 1) == 0
