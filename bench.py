@@ -3,9 +3,13 @@
 One step = one chunked EFLA forward (gate, Gram, UT solve, WY factors, state
 passing, outputs and final state) over the whole synthetic workload, with
 inputs already resident in HBM. Prints one JSON line with head-tokens/s
-(B*H*T per second), the roofline position of the kernel, the fp64 CPU oracle
-timed on this host over whole passes of the same workload (about ten
-seconds), and the single-token decode step measured on the 340M-layer shape.
+(B*H*T per second) over the timed back-to-back launches, the roofline
+position of the kernel (events on the launch stream), the same launch with
+the caches flushed before each one, measured MFMA and copy peaks, the
+single-token decode step (cache-warm and flushed), the backward and training
+step, the gated variant, the other synthetic workloads, and the fp64 CPU
+oracle timed on this host over whole passes of the same workload (about ten
+seconds) with the host CPU model and single-thread figures.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -317,6 +321,30 @@ def bench_other_workloads(efla, torch, efla_inputs, skip: str, steps=10, warmup=
     return out
 
 
+def bench_gated(efla, torch, efla_inputs, w, steps=10, warmup=3):
+    """The gated variant (efla_fwd_chunked_gated, per-token log-decays from
+    efla_inputs.log_decay) on workload w: median per-launch time and the
+    HBM fraction on its algorithmic bytes (the forward's plus 4 bytes of
+    log-decay per head-token)."""
+    x = efla_inputs.make_inputs(w)
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    lg = efla_inputs.log_decay(w.seed + 1000, (w.B, w.H, w.T)).cuda()
+    o = torch.empty_like(g["v"])
+    sT = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        efla.efla_fwd_chunked_gated(g["q"], g["k"], g["v"], g["beta"], lg, g["s0"], chunk=w.chunk, o=o,
+                                    s_final=sT)
+
+    _, per = time_launches(fwd, steps, warmup, torch.cuda.current_stream())
+    med = sorted(per)[len(per) // 2]
+    nbytes = alg_bytes_fwd(w, g["s0"] is not None) + w.head_tokens * 4
+    return {"workload": w.name, "ms_per_launch_median": med,
+            "head_tokens_per_s": w.head_tokens / (med * 1e-3),
+            "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernel": "efla_chunked_kernel (4-wave WY form, gated)"}
+
+
 def alg_bytes_bwd(w) -> int:
     """Algorithmic bytes of the backward: read q, k, v, beta, dout; write dq,
     dk, dv, dbeta (per head-token (8d + 2) elements); read S0 and dS_T and
@@ -424,6 +452,7 @@ def main():
                     help="skip the cache-flushed per-launch timing of the forward")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured MFMA and copy peaks")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated-variant timing")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -501,6 +530,8 @@ def main():
         res["decode"] = bench_decode(efla, torch, efla_inputs, flush)
     if not args.no_backward:
         res["backward"] = bench_backward(efla, torch, efla_inputs, w)
+    if not args.no_gated:
+        res["gated"] = bench_gated(efla, torch, efla_inputs, w)
     if not args.no_others:
         res["other_workloads"] = bench_other_workloads(efla, torch, efla_inputs, w.name)
     if args.copy_calibration:

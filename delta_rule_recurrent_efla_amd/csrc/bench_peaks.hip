@@ -51,11 +51,21 @@ __global__ __launch_bounds__(256) void mfma_f32_loop(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// dst[i] = src[i] over n float4 elements, grid-stride, 16-byte accesses.
+// dst[i] = src[i] over n float4 elements, 16-byte accesses: each thread
+// issues four loads before its four stores (four requests in flight), then
+// moves on by four grid strides.
 __global__ __launch_bounds__(256) void stream_copy(const floatx4* __restrict__ src, floatx4* __restrict__ dst,
                                                    long long n) {
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += 4 * stride) {
+    floatx4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * stride < n) v[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * stride < n) __builtin_nontemporal_store(v[u], &dst[i + u * stride]);
+  }
 }
 
 }  // namespace
