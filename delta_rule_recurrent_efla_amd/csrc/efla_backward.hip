@@ -223,8 +223,7 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
         for (int e = 0; e < VE; ++e) lam = fmaf((float)x[e], (float)x[e], lam);
       }
     }
-    lam += __shfl_xor(lam, 1);
-    lam += __shfl_xor(lam, 2);
+    lam = group_sum<4>(lam);
     if (r < C && part == 0) {
       float c = 0.f, db = 0.f, dl = 0.f;
       if (r < nval) {
@@ -858,8 +857,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
       const float* gr = a.gram + mb + (size_t)i * C;
       for (int j = part; j < i; j += 4) s = fmaf(sm.E[i][j], gr[j], s);
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
+    s = group_sum<4>(s);
     if (i < C && part == 0) {
       sm.dc[i] = s;
       if (i < nval) ((CT*)a.dbeta)[(size_t)h * a.T + t0 + i] = from_f32<CT>(s * a.fb[rb + i]);
@@ -1208,8 +1206,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
           e4[e] *= ci;
         }
       }
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
+      s = xor32_sum(xor16_sum(s));
       if (g == 0) sm.dcp2[16 * I + li][J] = s;
       MM::store_tp(&sm.m.dMb[16 * I + li][0], J, m);
       MM::store_tp(&sm.m.Xb[16 * I + li][0], J, e4);

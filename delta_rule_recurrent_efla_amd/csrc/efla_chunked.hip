@@ -1274,6 +1274,12 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
     constexpr int VPRV = BV / VE;
     constexpr int NLK = (C * VPR + NLT - 1) / NLT;
     constexpr int NLV = (C * VPRV + NLT - 1) / NLT;
+    // every loader thread has a piece in every slot: the slot tests drop
+    // out, so no load is conditional and the compiler's count of loads in
+    // flight is exact (a test it cannot fold makes it wait for the most
+    // recent requests as well)
+    constexpr bool KFULL = NLT * NLK == C * VPR;
+    constexpr bool VFULL = NLT * NLV == C * VPRV;
     const CT* bg = (const CT*)a.beta + tok0;
     Vec kreg[NLK], qreg[NLK], vreg[NLV];
     CT breg;
@@ -1307,7 +1313,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       const auto rk = chunk_rsrc(kg, chunk, 0);
 #pragma unroll
       for (int j = 0; j < NLK; ++j)
-        if (lt + NLT * j < C * VPR) buf_load(rk, koff[j], kreg[j]);
+        if (KFULL || lt + NLT * j < C * VPR) buf_load(rk, koff[j], kreg[j]);
       const long long tok = (long long)chunk * C;
       buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
                (unsigned)(min(arow, C - 1) * (int)sizeof(CT)), breg);
@@ -1330,10 +1336,10 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       const auto rv = chunk_rsrc(vg, chunk, v0);
 #pragma unroll
       for (int j = 0; j < NLK; ++j)
-        if (lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
+        if (KFULL || lt + NLT * j < C * VPR) buf_load(rq, koff[j], qreg[j]);
 #pragma unroll
       for (int j = 0; j < NLV; ++j)
-        if (lt + NLT * j < C * VPRV) buf_load(rv, voff[j], vreg[j]);
+        if (VFULL || lt + NLT * j < C * VPRV) buf_load(rv, voff[j], vreg[j]);
     };
     auto loader = [&](auto pwc) {
       constexpr int PW = decltype(pwc)::value;  // loader 0..3
@@ -1386,119 +1392,169 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       // Gram operands, which are these same registers), and that row's beta
       const int li0 = lane & 15, g0 = lane >> 4;
       constexpr int NKB = LGRAM ? NFK : 1;
-      Vec kb[NKB];
-      CT kbeta;
       unsigned kboff[NKB];
       if constexpr (LGRAM) {
 #pragma unroll
         for (int f = 0; f < NFK; ++f) kboff[f] = (unsigned)(((16 * PW + li0) * D + 32 * f + 8 * g0) * (int)sizeof(CT));
       }
-      auto load_kb = [&](int chunk) {
-        const auto rk = chunk_rsrc(kg, chunk, 0);
-#pragma unroll
-        for (int f = 0; f < NKB; ++f) buf_load(rk, kboff[f], kb[f]);
-        const long long tok = (long long)chunk * C;
-        buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
-                 (unsigned)((16 * PW + li0) * (int)sizeof(CT)), kbeta);
-      };
-      // a of rows 16 PW + li of `chunk` (zero past T) and the strictly lower
-      // a_r G_rc of the block's Gram matrix, stored transposed for the
-      // solvers' column-parallel forward substitution
-      auto gate_gram = [&](int chunk, float* alpha) {
-        float lam = 0.f;
-#pragma unroll
-        for (int f = 0; f < NKB; ++f) lam += sumsq(kb[f]);
-        lam += __shfl_xor(lam, 16);
-        lam += __shfl_xor(lam, 32);
-        const int row = 16 * PW + li0;
-        const float al = row < min(C, T - chunk * C) ? gate_coef(a.coef, to_f32(kbeta), lam) : 0.f;
-        if (g0 == 0) alpha[row] = al;
-        floatx4 dg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, kb[f], kb[f]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
-      };
       if constexpr (LGRAM) {
-        load_kb(0);
-        load_qv(0);
-        gate_gram(0, sm.buf[0].alpha);
-      } else {
-        load_k(0);
-        load_qv(0);
-        gate_rows(0, sm.buf[0].alpha);
-      }
-      __syncthreads();
-      for (int c = -1; c < nchunks; ++c) {
-        const int n = c + 1;  // chunk being prepared
-        const bool act = n < nchunks;
-        auto& B = sm.buf[n & 1];
-        int li = lane & 15, g = lane >> 4;
-        asm volatile("" : "+v"(li), "+v"(g));
-        // ---- phase A: stage chunk n (keys, queries, value slice)
-        if (act) {
-          // rows past T arrived as zeros
-          if constexpr (LGRAM) {
-            // kb[f] holds columns 32 f + 8 g .. + 7 of row 16 PW + li, stored
-            // in the key layout of this pass (natural, or column-permuted)
+        // Two register sets, each holding one chunk's keys (in the layout
+        // above), betas, queries and values. A chunk's data is requested in
+        // phase A two chunk steps before it is staged, and one and a half
+        // before its gate and Gram block are formed from it.
+        struct LB {
+          Vec kb[NKB];
+          CT kbeta;
+          Vec q[NLK];
+          Vec v[NLV];
+        };
+        LB b0, b1;
+        auto load_all = [&](LB& b, int chunk) {
+          const auto rk = chunk_rsrc(kg, chunk, 0);
+#pragma unroll
+          for (int f = 0; f < NKB; ++f) buf_load(rk, kboff[f], b.kb[f]);
+          const long long tok = (long long)chunk * C;
+          buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
+                   (unsigned)((16 * PW + li0) * (int)sizeof(CT)), b.kbeta);
+          const auto rq = chunk_rsrc(qg, chunk, 0);
+          const auto rv = chunk_rsrc(vg, chunk, v0);
+#pragma unroll
+          for (int j = 0; j < NLK; ++j)
+            if (KFULL || lt + NLT * j < C * VPR) buf_load(rq, koff[j], b.q[j]);
+#pragma unroll
+          for (int j = 0; j < NLV; ++j)
+            if (VFULL || lt + NLT * j < C * VPRV) buf_load(rv, voff[j], b.v[j]);
+        };
+        // a of rows 16 PW + li of `chunk` (zero past T) and the strictly
+        // lower a_r G_rc of the block's Gram matrix, stored transposed for
+        // the solvers' column-parallel forward substitution
+        auto gate_gram = [&](LB& b, int chunk, float* alpha) {
+          float lam = 0.f;
+#pragma unroll
+          for (int f = 0; f < NKB; ++f) lam += sumsq(b.kb[f]);
+          lam = xor32_sum(xor16_sum(lam));
+          const int row = 16 * PW + li0;
+          const float al = row < min(C, T - chunk * C) ? gate_coef(a.coef, to_f32(b.kbeta), lam) : 0.f;
+          if (g0 == 0) alpha[row] = al;
+          floatx4 dg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, b.kb[f], b.kb[f]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
+        };
+        // one chunk step: cur holds chunk n = c + 1, nxt holds chunk n + 1
+        auto step = [&](int c, LB& cur, LB& nxt) {
+          const int n = c + 1;
+          const bool act = n < nchunks;
+          auto& B = sm.buf[n & 1];
+          int li = lane & 15, g = lane >> 4;
+          asm volatile("" : "+v"(li), "+v"(g));
+          // ---- phase A: stage chunk n (rows past T arrived as zeros), keys
+          //      and queries in the key layout of this pass (natural, or
+          //      column-permuted)
+          if (act) {
 #pragma unroll
             for (int f = 0; f < NKB; ++f) {
-              if constexpr (SROWP) *(Vec*)&B.K[16 * PW + li][32 * f + 8 * g] = kb[f];
-              else st_perm(&B.K[16 * PW + li][0], 32 * f + 8 * g, kb[f]);
+              if constexpr (SROWP) *(Vec*)&B.K[16 * PW + li][32 * f + 8 * g] = cur.kb[f];
+              else st_perm(&B.K[16 * PW + li][0], 32 * f + 8 * g, cur.kb[f]);
             }
 #pragma unroll
             for (int j = 0; j < NLK; ++j) {
               const int idx = lt + NLT * j;
-              if (idx < C * VPR) {
+              if (KFULL || idx < C * VPR) {
                 const int r = idx / VPR, cv = idx % VPR;
-                if constexpr (SROWP) *(Vec*)&B.Q[r][cv * VE] = qreg[j];
-                else st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+                if constexpr (SROWP) *(Vec*)&B.Q[r][cv * VE] = cur.q[j];
+                else st_perm(&B.Q[r][0], cv * VE, cur.q[j]);
               }
             }
-          } else
 #pragma unroll
-          for (int j = 0; j < NLK; ++j) {
-            const int idx = lt + NLT * j;
-            if (idx < C * VPR) {
-              const int r = idx / VPR, cv = idx % VPR;
-              if constexpr (SROWP) {
-                *(Vec*)&B.K[r][cv * VE] = kreg[j];  // 16-byte aligned rows
-                *(Vec*)&B.Q[r][cv * VE] = qreg[j];
-              } else {
-                st_perm(&B.K[r][0], cv * VE, kreg[j]);
-                st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+            for (int j = 0; j < NLV; ++j) {
+              const int idx = lt + NLT * j;
+              if (VFULL || idx < C * VPRV) {
+                const int r = idx / VPRV, cv = idx % VPRV;
+                *(Vec*)&B.V[r][cv * VE] = cur.v[j];  // 16-byte aligned rows
               }
             }
           }
+          // first M job of the chunk whose state pass runs now
+          if constexpr (NA > 0) {
+            if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
+          }
+          // cur is free again: chunk n + 2 into it (clamped, never skipped)
+          load_all(cur, min(n + 2, nchunks - 1));
+          __syncthreads();
+          // ---- phase B: the rest of this wave's lower-incl-diag Q K^T tiles
+          //      of chunk n (-> M); a and the diagonal Gram block of chunk
+          //      n + 1, which the solvers invert in the next phase
+          if constexpr (NJ > NA) {
+            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
+          }
+          if (n + 1 < nchunks) gate_gram(nxt, n + 1, sm.buf[(n + 1) & 1].alpha);
+          __syncthreads();
+        };
+        load_all(b0, 0);
+        load_all(b1, min(1, nchunks - 1));
+        gate_gram(b0, 0, sm.buf[0].alpha);
+        __syncthreads();
+        // steps c = -1 .. nchunks - 1 (b0 holds the even chunks, b1 the odd),
+        // two per trip so that the register sets keep fixed names
+        int c = -1;
+        for (; c + 1 < nchunks; c += 2) {
+          step(c, b0, b1);
+          step(c + 1, b1, b0);
+        }
+        if (c < nchunks) step(c, b0, b1);
+      } else {
+        load_k(0);
+        load_qv(0);
+        gate_rows(0, sm.buf[0].alpha);
+        __syncthreads();
+        for (int c = -1; c < nchunks; ++c) {
+          const int n = c + 1;  // chunk being prepared
+          const bool act = n < nchunks;
+          auto& B = sm.buf[n & 1];
+          // ---- phase A: stage chunk n (keys, queries, value slice); rows
+          //      past T arrived as zeros
+          if (act) {
 #pragma unroll
-          for (int j = 0; j < NLV; ++j) {
-            const int idx = lt + NLT * j;
-            if (idx < C * VPRV) {
-              const int r = idx / VPRV, cv = idx % VPRV;
-              *(Vec*)&B.V[r][cv * VE] = vreg[j];  // 16-byte aligned rows
+            for (int j = 0; j < NLK; ++j) {
+              const int idx = lt + NLT * j;
+              if (KFULL || idx < C * VPR) {
+                const int r = idx / VPR, cv = idx % VPR;
+                if constexpr (SROWP) {
+                  *(Vec*)&B.K[r][cv * VE] = kreg[j];  // 16-byte aligned rows
+                  *(Vec*)&B.Q[r][cv * VE] = qreg[j];
+                } else {
+                  st_perm(&B.K[r][0], cv * VE, kreg[j]);
+                  st_perm(&B.Q[r][0], cv * VE, qreg[j]);
+                }
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < NLV; ++j) {
+              const int idx = lt + NLT * j;
+              if (VFULL || idx < C * VPRV) {
+                const int r = idx / VPRV, cv = idx % VPRV;
+                *(Vec*)&B.V[r][cv * VE] = vreg[j];  // 16-byte aligned rows
+              }
             }
           }
+          // first M job of the chunk whose state pass runs now
+          if constexpr (NA > 0) {
+            if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
+          }
+          load_k(min(n + 1, nchunks - 1));
+          __syncthreads();
+          // ---- phase B: load the queries and values of chunk n + 1; the rest
+          //      of this wave's lower-incl-diag Q K^T tiles of chunk n (-> M)
+          load_qv(min(n + 1, nchunks - 1));
+          if constexpr (NJ > NA) {
+            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
+          }
+          // a of chunk n + 1 (its keys arrived during this phase)
+          if (n + 1 < nchunks) gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
+          __syncthreads();
         }
-        // first M job of the chunk whose state pass runs now
-        if constexpr (NA > 0) {
-          if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
-        }
-        if constexpr (LGRAM) load_kb(min(n + 1, nchunks - 1));
-        else load_k(min(n + 1, nchunks - 1));
-        __syncthreads();
-        // ---- phase B: load the queries and values of chunk n + 1; the rest
-        //      of this wave's lower-incl-diag Q K^T tiles of chunk n (-> M)
-        load_qv(min(n + 1, nchunks - 1));
-        if constexpr (NJ > NA) {
-          if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
-        }
-        // a of chunk n + 1 (its keys arrived during this phase), and with
-        // LGRAM the diagonal Gram blocks the solvers invert in the next phase
-        if (n + 1 < nchunks) {
-          if constexpr (LGRAM) gate_gram(n + 1, sm.buf[(n + 1) & 1].alpha);
-          else gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
-        }
-        __syncthreads();
       }
     };
     switch (w - NSW - 2) {

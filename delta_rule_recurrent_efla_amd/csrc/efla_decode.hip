@@ -53,12 +53,23 @@ __device__ __forceinline__ void load_run(const CT* p, int e0, float (&x)[RPT]) {
 }
 
 // Sum over the lanes that share lane % CG (the row groups of one column
-// group); every lane receives its column group's total.
+// group); every lane receives its column group's total. Inside a 16-lane row
+// a DPP rotation by off (a power of two, 8 at most) adds lane i + off mod 16,
+// which keeps the lanes of one column group together; across rows the row
+// swaps. No exchange goes through the LDS.
 template <int CG>
 __device__ __forceinline__ float rowgroup_sum(float x) {
-#pragma unroll
-  for (int off = CG; off < 64; off <<= 1) x += __shfl_xor(x, off);
-  return x;
+  static_assert(CG == 1 || CG == 2 || CG == 4 || CG == 8 || CG == 16 || CG == 32, "column groups");
+  auto ror = [](float v, auto ctrl) {  // row_ror:n is DPP control 0x120 + n
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + decltype(ctrl)::value,
+                                                              0xf, 0xf, false));
+  };
+  if constexpr (CG <= 1) x += ror(x, std::integral_constant<int, 1>{});
+  if constexpr (CG <= 2) x += ror(x, std::integral_constant<int, 2>{});
+  if constexpr (CG <= 4) x += ror(x, std::integral_constant<int, 4>{});
+  if constexpr (CG <= 8) x += ror(x, std::integral_constant<int, 8>{});
+  if constexpr (CG <= 16) x = xor16_sum(x);
+  return xor32_sum(x);
 }
 
 // GATED: the gated variant, S_new = g (I - c k k^T) S + c k v^T with

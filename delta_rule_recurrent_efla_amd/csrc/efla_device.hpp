@@ -68,9 +68,30 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, unsigned off,
   v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// x plus x of lane l ^ 16 (xor16_sum) or l ^ 32 (xor32_sum), in every lane.
+// gfx950's row swaps exchange 16-lane rows (the odd rows of one operand with
+// the even rows of the other) or 32-lane halves inside the VALU, with no LDS
+// round trip: given x as both operands, the two results hold the two rows
+// (halves) that meet in each lane. The results are copied out of the returned
+// vector before the bit cast: a bit cast of a vector element reads element 0
+// with this compiler. Every lane must be active.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned lo = r[0], hi = r[1];
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned lo = r[0], hi = r[1];
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
 // every lane of a group receiving the group's sum. Within a 16-lane row the
-// exchange uses DPP (quad permutes, then half-row and row mirrors).
+// exchange uses DPP (quad permutes, then half-row and row mirrors), across
+// rows the row swap. Every lane must be active.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   auto dpp = [](float v, auto ctrl) {
@@ -82,7 +103,7 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp(x, std::integral_constant<int, 0x4E>{});   // quad_perm 2,3,0,1
   if constexpr (N >= 8) x += dpp(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
   if constexpr (N >= 16) x += dpp(x, std::integral_constant<int, 0x140>{}); // row_mirror
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 32) x = xor16_sum(x);
   static_assert(N <= 32, "group size");
   return x;
 }
