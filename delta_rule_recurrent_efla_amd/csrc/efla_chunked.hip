@@ -760,6 +760,12 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // starts at the forward substitution, with no key fetch, no Gram product
   // and no LDS round trip of their own.
   constexpr bool LGRAM = sizeof(CT) == 2 && NB == 4 && PM != 1 && D >= 32;
+  // With four 16-row blocks and outputs, the solvers form row block 3 of
+  // M = tril(Q K^T): their key fragments of blocks 0..3 are in registers
+  // for the Gram tiles, so each adds only the query fragments of block 3
+  // and two tiles, and the loaders keep the six tiles of rows 0..2.
+  constexpr bool SM3 = outs && NB == 4;
+  constexpr int NQKL = SM3 ? 6 : PrepJobs<NB>::NQK;  // Q K^T jobs the loaders form
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
   static_assert(!SUMMARY || NSW % 2 == 0, "summary state waves come in pairs");
   static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
@@ -1183,6 +1189,12 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
                 for (int f = 0; f < NFK; ++f) kf[i][f] = MM::template ldp<NKT>(&B.K[16 * i + li][0], f);
               }
             });
+            Frag q3[SM3 ? NFK : 1];
+            if constexpr (SM3) {
+              static_assert(t_first<NB>(0) == 0 && t_first<NB>(1) <= 2, "key blocks 2 PW, 2 PW + 1 in registers");
+#pragma unroll
+              for (int f = 0; f < NFK; ++f) q3[f] = MM::template ldp<NKT>(&B.Q[48 + li][0], f);
+            }
             static_for<NB>([&](auto ib) {
               constexpr int i = decltype(ib)::value;
               static_for<i>([&](auto jb) {
@@ -1253,6 +1265,21 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
                 });
               }
             });
+            if constexpr (SM3) {
+              // tiles (3, 2 PW) and (3, 2 PW + 1) of M, lower-incl-diagonal;
+              // the same fragments and product order as the loaders' tiles
+              static_for<2>([&](auto tc) {
+                constexpr int J = 2 * PW + decltype(tc)::value;
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, kf[J][f], q3[f]);
+                if constexpr (J == 3) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e <= li) ? acc[e] : 0.f;
+                }
+                MM::store_tps(&B.M[48 + li][0], J, acc);
+              });
+            }
           }
         }
         __syncthreads();
@@ -1344,11 +1371,14 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
     auto loader = [&](auto pwc) {
       constexpr int PW = decltype(pwc)::value;  // loader 0..3
       using JB = PrepJobs<NB>;
-      constexpr int NJ = JB::NQK > PW ? (JB::NQK - PW + 3) / 4 : 0;  // Q K^T jobs PW, PW + 4, ...
+      constexpr int NJ = NQKL > PW ? (NQKL - PW + 3) / 4 : 0;  // Q K^T jobs PW, PW + 4, ...
       // The first of this wave's jobs of a chunk runs in phase A of the
       // chunk's own state pass (its K and Q were staged one phase before, the
       // state reads M only in phase B); the others one chunk ahead in phase B.
-      constexpr int NA = (outs && NJ > 0) ? 1 : 0;
+      // With the solvers on row block 3, loaders 2 and 3 (which share their
+      // SIMDs with the solvers and stage the longest in phase A) keep their
+      // one job in phase B.
+      constexpr int NA = (outs && NJ > 0 && !(SM3 && PW >= 2)) ? 1 : 0;
       // jobs [J0, J1) of this wave on buffer Bm: every fragment first, then
       // the products (one exposed LDS round trip)
       auto mtiles = [&](auto& Bm, auto j0c, auto j1c) {
