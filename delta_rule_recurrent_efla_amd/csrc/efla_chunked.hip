@@ -1479,6 +1479,21 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           auto& B = sm.buf[n & 1];
           int li = lane & 15, g = lane >> 4;
           asm volatile("" : "+v"(li), "+v"(g));
+          // the fragments of this wave's phase-A M job (chunk c, the other
+          // buffer) are requested before the staging writes, so that their
+          // LDS round trip overlaps the staging
+          using JA = std::integral_constant<int, JB::NOFF + PW>;
+          Frag akf[NA > 0 ? NFK : 1], aqf[NA > 0 ? NFK : 1];
+          if constexpr (NA > 0) {
+            if (c >= 0) {
+              auto& Bc = sm.buf[c & 1];
+#pragma unroll
+              for (int f = 0; f < NFK; ++f) {
+                akf[f] = MM::template ldp<NKT>(&Bc.K[16 * JB::J(JA::value) + li][0], f);
+                aqf[f] = MM::template ldp<NKT>(&Bc.Q[16 * JB::I(JA::value) + li][0], f);
+              }
+            }
+          }
           // ---- phase A: stage chunk n (rows past T arrived as zeros), keys
           //      and queries in the key layout of this pass (natural, or
           //      column-permuted)
@@ -1508,7 +1523,18 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           }
           // first M job of the chunk whose state pass runs now
           if constexpr (NA > 0) {
-            if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
+            static_assert(NA == 1, "one phase-A job");
+            if (c >= 0) {
+              constexpr int I = JB::I(JA::value), J = JB::J(JA::value);
+              floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, akf[f], aqf[f]);
+              if constexpr (I == J) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e <= li) ? acc[e] : 0.f;
+              }
+              MM::store_tps(&sm.buf[c & 1].M[16 * I + li][0], J, acc);
+            }
           }
           // cur is free again: chunk n + 2 into it (clamped, never skipped)
           load_all(cur, min(n + 2, nchunks - 1));
