@@ -342,7 +342,7 @@ def bench_gated(efla, torch, efla_inputs, w, steps=10, warmup=3):
     return {"workload": w.name, "ms_per_launch_median": med,
             "head_tokens_per_s": w.head_tokens / (med * 1e-3),
             "hbm_frac": nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "kernel": "efla_chunked_kernel (4-wave WY form, gated)"}
+            "kernel": "efla_chunked_pipe_kernel (gated outputs pass)"}
 
 
 def alg_bytes_bwd(w) -> int:

@@ -702,7 +702,7 @@ constexpr int pipe_loaders() {
 
 // The pipelined chunk pass of one workgroup: L is its index among the
 // workgroups of the pass (head-major, column slices adjacent).
-template <typename CT, int D, int C, int BV, int NSW, int PM>
+template <typename CT, int D, int C, int BV, int NSW, int PM, bool GATED = false>
 __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, C, BV>& sm, const int L) {
   using MM = Mma<CT>;
   using Frag = typename MM::Frag;
@@ -727,8 +727,9 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   constexpr bool NEG = !SAVE;
   // the query fragments of the output products are requested in phase A,
   // except with outputs and state saving together (pass mode 3), whose plain
-  // state form holds more registers there: then in phase B, before their use
-  constexpr bool QA = outs && NEG;
+  // state form holds more registers there, and in the gated pass: then in
+  // phase B, before their use
+  constexpr bool QA = outs && NEG && !GATED;
   constexpr int NSP = SUMMARY ? NSW / 2 : NSW;  // state waves per column set
   constexpr int SW = NSP < NVT ? NSP : NVT;  // state waves holding columns
   constexpr int CPW = NVT / SW;              // 16-column tiles per state wave
@@ -766,6 +767,43 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // and two tiles, and the loaders keep the six tiles of rows 0..2.
   constexpr bool SM3 = outs && NB == 4;
   constexpr int NQKL = SM3 ? 6 : PrepJobs<NB>::NQK;  // Q K^T jobs the loaders form
+  // GATED (outputs pass, bf16, four 16-row blocks): per-token decays
+  // g = exp(log_g), S_t = g_t (I - c k k^T) S_{t-1} + c k v^T. With b_r the
+  // chunk's log-decays summed over rows 0..r, Gamma_r = exp(b_r) and
+  // E_rs = exp(b_r - b_s):
+  //   A    = strictly-lower(diag(c) K K^T * E)   (loaders: diagonal blocks;
+  //                                               solvers: the tiles below)
+  //   M    = lower-incl-diag(Q K^T) * E
+  //   Y    = V + diag(Gamma) K N,  -U' = T' Y     (N = -S, T' = -T diag(c))
+  //   -O^T = N^T Q^T diag(Gamma) + (-U')^T M^T
+  //   N   <- Gamma_C N + K^T diag(Gamma_C / Gamma) (-U')
+  // The loaders form b, Gamma and Gamma_C / Gamma = exp(b_C - b) of a chunk
+  // with its gate, two chunk steps before its state pass, and leave them in
+  // a three-slot table in LDS. E is formed per element where the recurrence
+  // carries it (never as a ratio), so no log-decay overflows it.
+  static_assert(!GATED || (PM == 0 && LGRAM && SROWP && SM3), "gated pipelined pass");
+  // the table lives in rows 0..31 of solver 1's Gram-tile copy, which that
+  // solver never touches (its tiles (i, j) have i > j >= 1)
+  static_assert(!GATED || (t_first<NB>(1) >= 1 && 9 * C * 4 <= 32 * Sm::CP * (int)sizeof(CT)), "decay table");
+  float* const gdec = (float*)&sm.An[1][0][0];
+  // [b | Gamma | Gamma_C / Gamma] of a chunk
+  auto gslot = [&](int chunk) { return gdec + (chunk % 3) * (3 * C); };
+  // tile (I, J) in accumulator layout (lane (g, li): row r = 16 I + li,
+  // columns s = 16 J + 4g + e) times E_rs, zero above the diagonal (or on it
+  // when STRICT); gb is the chunk's b
+  auto decay_tile = [&](const float* gb, int I, int J, floatx4 v, auto strictc) {
+    constexpr bool STRICT = decltype(strictc)::value;
+    const int ln = lane_id() & 15, gg = lane_id() >> 4;
+    const int r = 16 * I + ln, s0 = 16 * J + 4 * gg;
+    const float br = gb[r];
+    const floatx4 bs = *(const floatx4*)&gb[s0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool keep = STRICT ? (s0 + e < r) : (s0 + e <= r);
+      v[e] = keep ? v[e] * __expf(br - bs[e]) : 0.f;
+    }
+    return v;
+  };
   static_assert(NVT % SW == 0 && NB <= 4 && C % 16 == 0 && D % 16 == 0, "tile sizes");
   static_assert(!SUMMARY || NSW % 2 == 0, "summary state waves come in pairs");
   static_assert((Sm::DP * sizeof(CT)) % 64 == 32 && (Sm::CP * sizeof(CT)) % 64 == 32 &&
@@ -849,6 +887,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       const auto& B = sm.buf[c & 1];
       floatx4 oacc[CPW][NB];
       Frag sf[CPW][NFK], uf[CPW][NFB], kt[NKT][NFB], qf[NB][NFK];
+      const float* gb = GATED && act ? gslot(c) : nullptr;
       // ---- phase A: Y = V + K N; -U' = T' Y (T' of this chunk is ready one
       //      phase early). The K, V and T' fragments are requested first, the
       //      Q fragments (for phase B) while the K N products run
@@ -882,6 +921,15 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
           for (int f = 0; f < NFK; ++f) sf[cc][f] = MM::template acc<NKT>(sacc[cc], f);
+        if constexpr (GATED) {
+          // N <- Gamma_C N + ...: the decay of the carried state, applied
+          // once its fragments for this chunk are formed
+          const float gC = gb[2 * C - 1];
+#pragma unroll
+          for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+            for (int rt = 0; rt < NKT; ++rt) sacc[cc][rt] = sacc[cc][rt] * gC;
+        }
         Frag kf[NB][NFK];
         floatx4 al[NB], y[CPW][NB];
         // the value columns stay in their storage type until Y: converting
@@ -895,8 +943,10 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
 #pragma unroll
         for (int ut = 0; ut < NB; ++ut) {
           if constexpr (!NEG) al[ut] = *(const floatx4*)&B.alpha[16 * ut + 4 * g];
+          if constexpr (!GATED) {
 #pragma unroll
-          for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (wl * CPW + cc));
+            for (int cc = 0; cc < CPW; ++cc) vraw[cc][ut] = ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (wl * CPW + cc));
+          }
         }
         // T of this chunk is ready since phase B of the previous one: its
         // fragments are requested now so T Y finds them in registers
@@ -913,7 +963,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           // accumulator's start; else Y = diag(a) (V - K S)
 #pragma unroll
           for (int cc = 0; cc < CPW; ++cc)
-            y[cc][ut] = (!NEG || (SUMMARY && ident)) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
+            y[cc][ut] = (!NEG || (SUMMARY && ident) || GATED) ? floatx4{0.f, 0.f, 0.f, 0.f} : to_f32x4(vraw[cc][ut]);
 #pragma unroll
           for (int f = 0; f < NFK; ++f) {
 #pragma unroll
@@ -923,6 +973,15 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           if constexpr (!NEG) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc) y[cc][ut] = al[ut] * (to_f32x4(vraw[cc][ut]) - y[cc][ut]);
+          }
+          if constexpr (GATED) {
+            // Y = V + diag(Gamma) K N: rows 4g + e of tile ut are tokens
+            // 16 ut + 4g + e (the value columns are read here: kept from the
+            // start of the phase they would cost the registers of a spill)
+            const floatx4 gm = *(const floatx4*)&gb[C + 16 * ut + 4 * g];
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc)
+              y[cc][ut] = to_f32x4(ldtr4(&B.V[0][0], LDV, 16 * ut + 4 * g, 16 * (wl * CPW + cc))) + gm * y[cc][ut];
           }
         }
         Frag yf[CPW][NFB];
@@ -978,12 +1037,59 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
 #pragma unroll
               for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], sf[cc][f], qf[ut][f]);
             }
+            if constexpr (GATED) {
+              // column li of O^T tile ut is token 16 ut + li: N^T Q^T diag(Gamma)
+              const float gm = gb[C + 16 * ut + li];
+#pragma unroll
+              for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = oacc[cc][ut] * gm;
+              // this row tile's outputs now: O^T += (-U')^T M^T with -U' as
+              // formed (it is scaled for the state update afterwards), then
+              // the store; one tile's M fragments are live at a time
+              Frag mf[NFrag<CT, ut + 1>::value];
+#pragma unroll
+              for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) mf[f] = MM::template ldps<ut + 1>(&B.M[16 * ut + li][0], f);
+#pragma unroll
+              for (int f = 0; f < NFrag<CT, ut + 1>::value; ++f) {
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc) oacc[cc][ut] = MM::mma(oacc[cc][ut], uf[cc][f], mf[f]);
+              }
+              if (16 * ut + li < min(C, T - c * C)) {
+                CT* orow = (CT*)a.o + (tok0 + (size_t)c * C + 16 * ut + li) * D + v0 + 4 * g;
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc) store4(orow + 16 * (wl * CPW + cc), -oacc[cc][ut]);
+              }
+            }
           }
 #pragma unroll
           for (int rt = ut * NKT / NB; rt < (ut + 1) * NKT / NB; ++rt)
 #pragma unroll
             for (int f = 0; f < NFB; ++f) kt[rt][f] = tr_frag<NB, true>(&B.K[0][0], LDK, f, 16 * rt);
         });
+        if constexpr (GATED) {
+          // -U' with row r scaled in place by Gamma_C / Gamma_r =
+          // exp(b_C - b_r) (elements 0..3 of fragment f are rows
+          // 32 f + 4g + e, elements 4..7 rows 32 f + 16 + 4g + e), then the
+          // state update
+          static_assert(2 * NFB == NB && NEG, "whole fragments, negated form");
+#pragma unroll
+          for (int f = 0; f < NFB; ++f) {
+            const floatx4 d0 = *(const floatx4*)&gb[2 * C + 32 * f + 4 * g];
+            const floatx4 d1 = *(const floatx4*)&gb[2 * C + 32 * f + 16 + 4 * g];
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc) {
+              const Frag x = uf[cc][f];
+              const floatx4 lo = __builtin_convertvector(__builtin_shufflevector(x, x, 0, 1, 2, 3), floatx4);
+              const floatx4 hi = __builtin_convertvector(__builtin_shufflevector(x, x, 4, 5, 6, 7), floatx4);
+              uf[cc][f] = MM::cat(MM::cvt4(lo * d0), MM::cvt4(hi * d1));
+            }
+          }
+#pragma unroll
+          for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+            for (int f = 0; f < NFB; ++f)
+#pragma unroll
+              for (int cc = 0; cc < CPW; ++cc) sacc[cc][rt] = MM::mma(sacc[cc][rt], kt[rt][f], uf[cc][f]);
+        } else {
         Frag mf[NB][NFB];
 #pragma unroll
         for (int rt = 0; rt < NKT; ++rt) {
@@ -1029,6 +1135,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
             for (int cc = 0; cc < CPW; ++cc)
               store4(orow + (size_t)16 * ut * D + 16 * (wl * CPW + cc), NEG ? -oacc[cc][ut] : oacc[cc][ut]);
           }
+        }
         }
       }
       __syncthreads();
@@ -1076,8 +1183,10 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       // never computed; they are read only against zero blocks of X, so they
       // must hold zeros, not stale bits
       if constexpr (t_first<NB>(PW) > 0 && t_first<NB>(PW) < NB) {
-        constexpr int NZ = (int)(sizeof(CT) * C * Sm::CP / 16);
-        floatx4* z = (floatx4*)&sm.An[PW][0][0];
+        // (only rows of blocks below its first column tile are ever read)
+        constexpr int R0 = 16 * (t_first<NB>(PW) + 1);
+        constexpr int NZ = (int)(sizeof(CT) * (C - R0) * Sm::CP / 16);
+        floatx4* z = (floatx4*)&sm.An[PW][R0][0];
         for (int i = lane; i < NZ; i += 64) z[i] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
       __syncthreads();  // a of the first chunk
@@ -1203,6 +1312,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
                   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                   for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, kf[j][f], kf[i][f]);
+                  if constexpr (GATED) acc = decay_tile(gslot(n), i, j, acc, std::true_type{});
                   MM::store_tps(&An[16 * i + li][0], j, -acc);
                 }
               });
@@ -1273,7 +1383,9 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, kf[J][f], q3[f]);
-                if constexpr (J == 3) {
+                if constexpr (GATED) {
+                  acc = decay_tile(gslot(n), 3, J, acc, std::false_type{});
+                } else if constexpr (J == 3) {
 #pragma unroll
                   for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e <= li) ? acc[e] : 0.f;
                 }
@@ -1381,7 +1493,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       constexpr int NA = (outs && NJ > 0 && !(SM3 && PW >= 2)) ? 1 : 0;
       // jobs [J0, J1) of this wave on buffer Bm: every fragment first, then
       // the products (one exposed LDS round trip)
-      auto mtiles = [&](auto& Bm, auto j0c, auto j1c) {
+      auto mtiles = [&](auto& Bm, auto j0c, auto j1c, const float* gb) {
         constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
         if constexpr (outs && J1 > J0) {
           const int li = lane & 15, g = lane >> 4;
@@ -1408,7 +1520,9 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
             constexpr int j = JB::NOFF + PW + 4 * (J0 + decltype(jc)::value);
             constexpr int I = JB::I(j), J = JB::J(j);
             floatx4 v = acc[decltype(jc)::value];
-            if constexpr (I == J) {
+            if constexpr (GATED) {
+              v = decay_tile(gb, I, J, v, std::false_type{});
+            } else if constexpr (I == J) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = (4 * g + e <= li) ? v[e] : 0.f;
             }
@@ -1437,6 +1551,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           CT kbeta;
           Vec q[NLK];
           Vec v[NLV];
+          float lgv;  // gated: log-decay of the chunk's row `lane`
         };
         LB b0, b1;
         auto load_all = [&](LB& b, int chunk) {
@@ -1454,6 +1569,8 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
 #pragma unroll
           for (int j = 0; j < NLV; ++j)
             if (VFULL || lt + NLT * j < C * VPRV) buf_load(rv, voff[j], b.v[j]);
+          if constexpr (GATED)
+            buf_load(buf_rsrc(a.log_g + tok0 + tok, (long long)(T - tok) * 4), (unsigned)(lane * 4), b.lgv);
         };
         // a of rows 16 PW + li of `chunk` (zero past T) and the strictly
         // lower a_r G_rc of the block's Gram matrix, stored transposed for
@@ -1469,8 +1586,28 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           floatx4 dg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, b.kb[f], b.kb[f]);
+          if constexpr (GATED) {
+            // b over the chunk's rows (lane l: row l; rows past T add 0),
+            // this block's rows of [b | Gamma | Gamma_C / Gamma] into the
+            // chunk's slot of the table, then the block's Gram entries times E
+            const float bsc = wave_prefix_sum(b.lgv);
+            const float bC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bsc), C - 1));
+            float* gb = gslot(chunk);
+            if (g0 == PW) {
+              gb[lane] = bsc;
+              gb[C + lane] = __expf(bsc);
+              gb[2 * C + lane] = __expf(bC - bsc);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const floatx4 de = decay_tile(gb, PW, PW, dg, std::true_type{});
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
+            for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = al * de[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
+          }
         };
         // one chunk step: cur holds chunk n = c + 1, nxt holds chunk n + 1
         auto step = [&](int c, LB& cur, LB& nxt) {
@@ -1529,7 +1666,9 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
               floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int f = 0; f < NFK; ++f) acc = MM::mma(acc, akf[f], aqf[f]);
-              if constexpr (I == J) {
+              if constexpr (GATED) {
+                acc = decay_tile(gslot(c), I, J, acc, std::false_type{});
+              } else if constexpr (I == J) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] = (4 * g + e <= li) ? acc[e] : 0.f;
               }
@@ -1543,7 +1682,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           //      of chunk n (-> M); a and the diagonal Gram block of chunk
           //      n + 1, which the solvers invert in the next phase
           if constexpr (NJ > NA) {
-            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
+            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{}, GATED ? gslot(n) : nullptr);
           }
           if (n + 1 < nchunks) gate_gram(nxt, n + 1, sm.buf[(n + 1) & 1].alpha);
           __syncthreads();
@@ -1597,7 +1736,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           }
           // first M job of the chunk whose state pass runs now
           if constexpr (NA > 0) {
-            if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{});
+            if (c >= 0) mtiles(sm.buf[c & 1], std::integral_constant<int, 0>{}, std::integral_constant<int, NA>{}, nullptr);
           }
           load_k(min(n + 1, nchunks - 1));
           __syncthreads();
@@ -1605,7 +1744,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           //      of this wave's lower-incl-diag Q K^T tiles of chunk n (-> M)
           load_qv(min(n + 1, nchunks - 1));
           if constexpr (NJ > NA) {
-            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{});
+            if (act) mtiles(B, std::integral_constant<int, NA>{}, std::integral_constant<int, NJ>{}, nullptr);
           }
           // a of chunk n + 1 (its keys arrived during this phase)
           if (n + 1 < nchunks) gate_rows(n + 1, sm.buf[(n + 1) & 1].alpha);
@@ -1633,10 +1772,10 @@ __device__ __forceinline__ int xcd_slot(int nvt) {
   return blockIdx.x;
 }
 
-template <typename CT, int D, int C, int BV, int NSW, int PM>
+template <typename CT, int D, int C, int BV, int NSW, int PM, bool GATED = false>
 __global__ __launch_bounds__(64 * (NSW + 2 + pipe_loaders<PM>()), 1) void efla_chunked_pipe_kernel(ChunkedArgs a) {
   __shared__ PipeSmem<CT, D, C, BV> sm;
-  pipe_body<CT, D, C, BV, NSW, PM>(a, sm, xcd_slot(a.nvt));
+  pipe_body<CT, D, C, BV, NSW, PM, GATED>(a, sm, xcd_slot(a.nvt));
 }
 
 // First launch of the time-segmented forward: the summaries of segments
@@ -1877,14 +2016,22 @@ static hipError_t dispatch_chunk(const ChunkedArgs& a, int NH, int chunk, void* 
   }
 }
 
-// Gated variant: the 4-wave kernel with the decay terms (GATED). Slices of
-// 16 state columns when 64-column slices would leave CUs idle.
+// Gated variant. bf16 with 64-token chunks and d >= 32 runs the pipelined
+// kernel's gated outputs pass (one pass per head and 64-column slice, no
+// time segments); the other shapes the 4-wave kernel with the decay terms,
+// in slices of 16 state columns when 64-column slices would leave CUs idle.
 template <typename CT, int D, int C>
 static hipError_t launch_chunked_gated(const ChunkedArgs& in, int NH, hipStream_t stream) {
   constexpr int BV = D < 64 ? D : 64;
   static_assert(chunked_smem_bytes<CT, D, C, BV>() <= 160 * 1024, "LDS budget");
   ChunkedArgs a = in;
   a.nvt = D / BV;
+  if constexpr (sizeof(CT) == 2 && C == 64 && D >= 32 && pipelined<CT, D, C>()) {
+    constexpr int NSW = EFLA_PIPE_STATE_WAVES;
+    hipLaunchKernelGGL((efla_chunked_pipe_kernel<CT, D, C, BV, NSW, 0, true>), dim3((unsigned)(NH * a.nvt)),
+                       dim3(64 * (NSW + 6)), 0, stream, a);
+    return hipGetLastError();
+  }
   if (NH * a.nvt < 256 && BV > 16) {
     a.nvt = D / 16;
     hipLaunchKernelGGL((efla_chunked_kernel<CT, D, C, 16, EFLA_STATE_WAVES, true>), dim3((unsigned)(NH * a.nvt)),

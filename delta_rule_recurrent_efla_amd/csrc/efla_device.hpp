@@ -88,6 +88,27 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
+// Inclusive prefix sum over the 64 lanes (lane l receives x_0 + ... + x_l):
+// DPP right shifts by 1, 2, 4, 8 inside each 16-lane row (lanes shifted in
+// from outside the row add 0), then the totals of the rows below, read from
+// lanes 15, 31 and 47. Every lane must be active.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  auto shr = [](float v, auto n) {  // row_shr:n is DPP control 0x110 + n
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 0x110 + decltype(n)::value, 0xf, 0xf, false));
+  };
+  x += shr(x, std::integral_constant<int, 1>{});
+  x += shr(x, std::integral_constant<int, 2>{});
+  x += shr(x, std::integral_constant<int, 4>{});
+  x += shr(x, std::integral_constant<int, 8>{});
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 15));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 47));
+  const int row = lane_id() >> 4;
+  const float below = row == 0 ? 0.f : (row == 1 ? t0 : (row == 2 ? t0 + t1 : (t0 + t1) + t2));
+  return x + below;
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
 // every lane of a group receiving the group's sum. Within a 16-lane row the
 // exchange uses DPP (quad permutes, then half-row and row mirrors), across

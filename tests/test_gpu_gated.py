@@ -106,14 +106,32 @@ def test_zero_log_decay_matches_ungated(efla):
     assert normwise(o, o_ref) <= 2e-2 and normwise(s, s_ref) <= 2e-2
 
 
+@pytest.mark.parametrize("dt,d,c", [("f32", 64, 32), ("bf16", 128, 64)])
 @pytest.mark.parametrize("rule", ["euler", "rk4", "order2"])
-def test_gated_step_rules(efla, rule):
+def test_gated_step_rules(efla, rule, dt, d, c):
+    """Every step rule, on the 4-wave kernel (fp32) and on the pipelined
+    kernel's gated pass (bf16, 64-token chunks)."""
     modes = {"euler": oracle.EULER, "rk4": oracle.RK4, "order2": oracle.ORDER2}
-    x = efla_inputs.random_case(90, B=1, H=3, T=150, d=64, dtype="f32", k_lo=0.3, k_hi=1.3, s0_std=0.3)
+    x = efla_inputs.random_case(90, B=1, H=3, T=150, d=d, dtype=dt, k_lo=0.3, k_hi=1.3, s0_std=0.3)
     lg = efla_inputs.log_decay(91, (1, 3, 150))
-    o, s = run_gated(efla, x, lg, 32, coef=rule)
+    note(f"[gated rule] {rule} dtype={dt} d={d} chunk={c}")
+    o, s = run_gated(efla, x, lg, c, coef=rule)
     o_ref, s_ref = oracle.fwd_gated(x["q"], x["k"], x["v"], x["beta"], lg, x["s0"], mode=modes[rule])
-    assert normwise(o, o_ref) <= 1e-4 and normwise(s, s_ref) <= 1e-4
+    assert normwise(o, o_ref) <= TOL[dt] and normwise(s, s_ref) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_gated_growth(efla, dt, d):
+    """Log-decays of both signs (g up to e^0.05 > 1): the decay factors the
+    kernels form then exceed 1 below the diagonal and must not be clamped."""
+    T = 200
+    x = efla_inputs.random_case(61, B=1, H=2, T=T, d=d, dtype=dt, s0_std=0.5)
+    lg = -0.3 + 0.35 * torch.rand((1, 2, T), generator=torch.Generator().manual_seed(62))
+    note(f"[gated growth] dtype={dt} d={d}")
+    o, s = run_gated(efla, x, lg, 64)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    o_ref, s_ref = oracle.fwd_gated(x["q"], x["k"], x["v"], x["beta"], lg, x["s0"])
+    assert normwise(o, o_ref) <= TOL[dt] and normwise(s, s_ref) <= TOL[dt]
 
 
 def test_gated_full_size_layer(efla):
