@@ -239,8 +239,9 @@ def efla_fwd_chunked_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, be
                            return_state: bool = True, stream=None, coef="exact"
                            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Gated EFLA forward: S_t = g_t (I - c_t k_t k_t^T) S_{t-1} + c_t k_t v_t^T
-    with g_t = exp(log_g_t); log_g [B,H,T] fp32 (values <= 0). Everything else
-    as efla_fwd_chunked."""
+    with g_t = exp(log_g_t); log_g [B,H,T] fp32 (values <= 0 keep every decay
+    factor at most 1; positive values are allowed). Everything else as
+    efla_fwd_chunked, s_final aliasing s0 included."""
     lib = load_library()
     dev = q.device
     if q.dim() != 4:

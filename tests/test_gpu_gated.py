@@ -134,6 +134,37 @@ def test_gated_growth(efla, dt, d):
     assert normwise(o, o_ref) <= TOL[dt] and normwise(s, s_ref) <= TOL[dt]
 
 
+def test_gated_in_place_state(efla):
+    """s_final aliasing s0 (the state advanced in place) gives the same bits
+    as separate buffers, and both match the oracle."""
+    T, d = 333, 128
+    x = efla_inputs.random_case(81, B=2, H=3, T=T, d=d, dtype="bf16", s0_std=0.4)
+    lg = efla_inputs.log_decay(82, (2, 3, T))
+    g = dev(x)
+    lgd = lg.cuda()
+    o1, s1 = efla.efla_fwd_chunked_gated(g["q"], g["k"], g["v"], g["beta"], lgd, g["s0"], chunk=64)
+    st = g["s0"].clone()
+    o2, s2 = efla.efla_fwd_chunked_gated(g["q"], g["k"], g["v"], g["beta"], lgd, st, chunk=64, s_final=st)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+    o_ref, s_ref = oracle.fwd_gated(x["q"], x["k"], x["v"], x["beta"], lg, x["s0"])
+    assert normwise(o2.float().cpu(), o_ref) <= 2e-2 and normwise(st.cpu(), s_ref) <= 2e-2
+
+
+def test_gated_deterministic_bitwise(efla):
+    """Two launches of the gated forward on the same inputs give identical
+    bits (no atomics, fixed reduction order)."""
+    T, d = 1000, 128
+    x = efla_inputs.random_case(83, B=2, H=8, T=T, d=d, dtype="bf16", s0_std=0.2)
+    lg = efla_inputs.log_decay(84, (2, 8, T)).cuda()
+    g = dev(x)
+    o1, s1 = efla.efla_fwd_chunked_gated(g["q"], g["k"], g["v"], g["beta"], lg, g["s0"], chunk=64)
+    o2, s2 = efla.efla_fwd_chunked_gated(g["q"], g["k"], g["v"], g["beta"], lg, g["s0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
 def test_gated_full_size_layer(efla):
     """The 1.3B-layer shape (128 heads x T = 4096, bf16, random S0) with
     per-token decays, every head against the oracle."""
