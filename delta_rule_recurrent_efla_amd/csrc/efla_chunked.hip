@@ -614,17 +614,21 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 // state waves run chunk c:
 //   state waves    A: K S, Y, U' = T Y           B: S^T Q^T, K^T U', U'^T M^T;
 //                                                    store O
-//   prep 0, 1      A: diagonal Gram blocks of    B: Gram tiles below the diagonal
-//   ("solvers")       c+1 from registers,            and the column tiles of T
-//                     (I+A_bb)^-1                    of c+1
+//   prep 0, 1      A: (I+A_bb)^-1 of c+1 (with   B: Gram tiles below the diagonal,
+//   ("solvers")       four 16-row blocks the         the column tiles of T and
+//                     loaders formed A_bb)           (four blocks) row block 3 of
+//                                                    M, of c+1
 //   prep 2..5      A: stage K, Q, V of c+1;      B: the other Q K^T tiles of
-//   ("loaders")       one Q K^T tile of c;           c+1; a of c+2; load Q, V
-//                     load the keys of c+2           of c+2
+//   ("loaders")       one Q K^T tile of c;           c+1; a (and with four
+//                     load the keys of c+2 (with     blocks the diagonal Gram
+//                     four blocks: keys, betas,      blocks) of c+2; load Q, V
+//                     queries and values of c+3)     of c+2
 // Waves are placed on the SIMDs round robin: the two state waves and the two
 // solvers get a SIMD each, and every SIMD also runs one loader. Every global
 // load is issued as soon as its registers are free and consumed one chunk
-// later; loads are never conditional (the last chunk is fetched again), so
-// the compiler keeps no copy at the loop latch.
+// (with four blocks two chunk steps) later; loads are never conditional (the
+// last chunk is fetched again), so the compiler keeps no copy at the loop
+// latch.
 // K, Q, V, T, M and a are double-buffered in LDS; K^T and the columns of V
 // are read with ds_read_b64_tr_b16 straight from the row-major tiles.
 template <typename CT, int D, int C, int BV>
