@@ -708,6 +708,195 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
   }
 }
 
+// The same dS recurrence with the chunk operands staged by four loader waves
+// into a double-buffered copy of the LDS tiles: the four column waves compute
+// chunk ch from one buffer while the loaders stage chunk ch - 1 into the
+// other, from registers fetched one chunk step earlier, and then fetch chunk
+// ch - 2. One workgroup barrier per chunk; the column waves' arithmetic is
+// that of efla_bwd_state_kernel_bf, bit for bit.
+template <int D, int C, int BV>
+__global__ __launch_bounds__(512) void efla_bwd_state_kernel_bfp(BwdArgs a) {
+  using Sm = StateSmemBf<D, C, BV>;
+  static_assert((Sm::LD * 2) % 64 == 32 && (Sm::LO * 2) % 64 == 32, "row strides");
+  __shared__ __attribute__((aligned(16))) Sm sm[2];
+  constexpr int NKT = D / 16, NB = C / 16, NW = BV / 16;
+  static_assert(NW <= 4, "four column waves");
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nvt = D / BV;
+  const int L = bwd_xcd_slot(nvt);
+  const int h = L / nvt, v0 = (L % nvt) * BV;
+  const bf16* kg = (const bf16*)a.k + (size_t)h * a.T * D;
+  const bf16* qg = (const bf16*)a.q + (size_t)h * a.T * D;
+  const bf16* dog = (const bf16*)a.dout + (size_t)h * a.T * D;
+  if (w >= 4) {
+    // ======== loaders (waves 4..7): loader thread lt = tid - 256
+    const int lt = tid - 256;
+    constexpr int NLK = (C * D / 8 + 255) / 256, NLO = (C * BV / 8 + 255) / 256, NLM = (C * C / 4 + 255) / 256;
+    bf16x8 rk[NLK], rq[NLK], ro[NLO];
+    bf16x4 rm[NLM], rt4[NLM];
+    float ral = 0.f;
+    auto fetch = [&](int ch) {
+      const int t0 = ch * C, nval = min(C, a.T - t0);
+      const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+      const bf16x8 z8 = {};
+#pragma unroll
+      for (int j = 0; j < NLK; ++j) {
+        const int i = lt + 256 * j, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+        const bool ok = i < C * D / 8 && r < nval;
+        rk[j] = ok ? *(const bf16x8*)(kg + (size_t)(t0 + r) * D + c8) : z8;
+        rq[j] = ok ? *(const bf16x8*)(qg + (size_t)(t0 + r) * D + c8) : z8;
+      }
+#pragma unroll
+      for (int j = 0; j < NLO; ++j) {
+        const int i = lt + 256 * j, r = i / (BV / 8), c8 = 8 * (i % (BV / 8));
+        ro[j] = (i < C * BV / 8 && r < nval) ? *(const bf16x8*)(dog + (size_t)(t0 + r) * D + v0 + c8) : z8;
+      }
+#pragma unroll
+      for (int j = 0; j < NLM; ++j) {
+        const int i = lt + 256 * j;
+        if (i < C * C / 4) {
+          rm[j] = *(const bf16x4*)((const bf16*)a.mt + mb + 4 * (size_t)i);
+          rt4[j] = *(const bf16x4*)((const bf16*)a.tt + mb + 4 * (size_t)i);
+        }
+      }
+      if (lt < C) ral = a.al[(size_t)h * a.nc * C + t0 + lt];
+    };
+    auto stage = [&](Sm& S) {
+#pragma unroll
+      for (int j = 0; j < NLK; ++j) {
+        const int i = lt + 256 * j, r = i / (D / 8), c8 = 8 * (i % (D / 8));
+        if (i < C * D / 8) {
+          *(bf16x8*)&S.Kf[r][c8] = rk[j];
+          *(bf16x8*)&S.Qf[r][c8] = rq[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NLO; ++j) {
+        const int i = lt + 256 * j, r = i / (BV / 8), c8 = 8 * (i % (BV / 8));
+        if (i < C * BV / 8) *(bf16x8*)&S.dOf[r][c8] = ro[j];
+      }
+#pragma unroll
+      for (int j = 0; j < NLM; ++j) {
+        const int i = lt + 256 * j, r = i / (C / 4), c4 = 4 * (i % (C / 4));
+        if (i < C * C / 4) {
+          *(bf16x4*)&S.MT[r][c4] = rm[j];
+          *(bf16x4*)&S.TT[r][c4] = rt4[j];
+        }
+      }
+      if (lt < C) S.al[lt] = ral;
+    };
+    fetch(a.nc - 1);
+    stage(sm[(a.nc - 1) & 1]);
+    fetch(a.nc > 1 ? a.nc - 2 : 0);  // always issued (the last one repeats)
+    __syncthreads();
+    for (int ch = a.nc - 1; ch >= 0; --ch) {
+      if (ch > 0) {
+        stage(sm[(ch - 1) & 1]);
+        fetch(ch > 1 ? ch - 2 : 0);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  // ======== column waves (0..3): wave w < BV / 16 owns columns v0 + 16 w ..
+  const int col = v0 + 16 * w + li;
+  const bool owner = w < NW;
+  floatx4 ds[NKT];
+#pragma unroll
+  for (int rt = 0; rt < NKT; ++rt) ds[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (owner && a.dsT) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ds[rt][e] = a.dsT[((size_t)h * D + 16 * rt + 4 * g + e) * D + col];
+  }
+  auto ld_a = [&](const bf16* row, int kb) {  // A(row, 32 kb + 4 g + ..) and (.. + 16)
+    return pk8(*(const bf16x4*)(row + 32 * kb + 4 * g), *(const bf16x4*)(row + 32 * kb + 16 + 4 * g));
+  };
+  __syncthreads();  // the last chunk is staged
+  for (int ch = a.nc - 1; ch >= 0; --ch) {
+    const int t0 = ch * C, nval = min(C, a.T - t0);
+    Sm& S = sm[ch & 1];
+    if (owner) {
+      bf16* dst = (bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * rt + 4 * g + e) * D + col] = (bf16)ds[rt][e];
+    }
+    if (owner) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      // dO columns of this wave as B fragments (k = tokens)
+      bf16x8 dof[NB / 2];
+#pragma unroll
+      for (int kb = 0; kb < NB / 2; ++kb) dof[kb] = tr_frag<NB>(&S.dOf[0][0], Sm::LO, kb, 16 * w);
+      // Q^T dO: no dependence on dS', so it runs ahead of the chain
+      floatx4 qd[NKT];
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) {
+        floatx4 acc = ds[rt];
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_frag<NB>(&S.Qf[0][0], Sm::LD, kb, 16 * rt), dof[kb], acc,
+                                                        0, 0, 0);
+        qd[rt] = acc;
+      }
+      // dU = M^T dO + K dS'
+      floatx4 du[NB];
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = z;
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&S.MT[16 * I + li][0], kb), dof[kb], acc, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < NKT / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&S.Kf[16 * I + li][0], kb),
+                                                        pk8(cv4(ds[2 * kb]), cv4(ds[2 * kb + 1])), acc, 0, 0, 0);
+        du[I] = acc;
+      }
+      // G = T^T dU; D G is dV
+      floatx4 dy[NB];
+      float* grow = a.gw + ((size_t)h * a.nc * C + t0) * D;
+      bf16* dvg = (bf16*)a.dv + ((size_t)h * a.T + t0) * D;
+#pragma unroll
+      for (int I = 0; I < NB; ++I) {
+        floatx4 acc = z;
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_a(&S.TT[16 * I + li][0], kb),
+                                                        pk8(cv4(du[2 * kb]), cv4(du[2 * kb + 1])), acc, 0, 0, 0);
+        const floatx4 al4 = *(const floatx4*)&S.al[16 * I + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * I + 4 * g + e;
+          grow[(size_t)r * D + col] = acc[e];
+          dy[I][e] = al4[e] * acc[e];
+          if (r < nval) dvg[(size_t)r * D + col] = (bf16)dy[I][e];
+        }
+      }
+      // dS = dS' + Q^T dO - K^T D G
+#pragma unroll
+      for (int rt = 0; rt < NKT; ++rt) {
+        floatx4 acc = qd[rt];
+#pragma unroll
+        for (int kb = 0; kb < NB / 2; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_frag<NB>(&S.Kf[0][0], Sm::LD, kb, 16 * rt),
+                                                        pk8(cv4(-dy[2 * kb]), cv4(-dy[2 * kb + 1])), acc, 0, 0, 0);
+        ds[rt] = acc;
+      }
+    }
+    __syncthreads();
+  }
+  if (owner && a.ds0) {
+#pragma unroll
+    for (int rt = 0; rt < NKT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.ds0[((size_t)h * D + 16 * rt + 4 * g + e) * D + col] = ds[rt][e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 4. Per (head, chunk): dq, dk, dbeta from S, dS', G and the chunk's inputs.
 // Every MFMA operand is a 16-byte read: rows of K, dO, V, G and of the two
@@ -1277,8 +1466,13 @@ static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
   constexpr int BV = D < 64 ? D : 64;
   hipLaunchKernelGGL((efla_bwd_prep_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(256), 0, stream, a);
   if constexpr (sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0) {
-    hipLaunchKernelGGL((efla_bwd_state_kernel_bf<D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
-                       stream, a);
+    if constexpr (2 * sizeof(StateSmemBf<D, C, BV>) <= 160 * 1024) {
+      hipLaunchKernelGGL((efla_bwd_state_kernel_bfp<D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(512), 0,
+                         stream, a);
+    } else {
+      hipLaunchKernelGGL((efla_bwd_state_kernel_bf<D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
+                         stream, a);
+    }
   } else {
     hipLaunchKernelGGL((efla_bwd_state_kernel<CT, D, C, BV>), dim3((unsigned)(NH * (D / BV))), dim3(256), 0,
                        stream, a);
