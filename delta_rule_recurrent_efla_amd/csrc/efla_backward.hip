@@ -1189,9 +1189,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel(BwdArgs a) {
 // column a pair of ds_read_b64_tr_b16. Each product is formed in the
 // orientation whose accumulator holds 4 consecutive columns of one row of the
 // tile it is stored to (8-byte writes). dc is summed from the fp32
-// accumulators of Yh and E as they are formed. With X = D E:
-//   Yh^T tiles  = (V - K S)^T         A = rows of K, B = -S^T rows
-//   U^T tiles   = Yh^T (T D)^T        A = rows of Yh^T, B = rows of T D
+// accumulators of Yh and E as they are formed. Every global read is 8 or 16
+// bytes per lane: the state is staged whole and its columns are read from LDS
+// (with 2-byte column reads from global memory instead, the kernel took
+// 1.5x as long). With X = D E:
+//   Yh tiles    = V - (S^T K^T)^T     A = rows of S^T (as stored), B = rows of K
+//   U^T tiles   = Yh^T (T D)^T        A = columns of Yh, B = rows of T D
 //   dM, E       from U dO^T, -U G^T   A = rows of U, B = rows of dO, G
 //   dQ = dO S^T + dM K
 //   dK = dM^T Q + U dS'^T - D (G S^T) + X K + X^T K
@@ -1203,8 +1206,9 @@ struct GradSmemBf {
   bf16 dOb[C][LD];
   bf16 Gb[C][LD];
   bf16 Ub[C][LD];  // U = T D Yh
+  bf16 Sb[D][LD];  // the chunk-start state as stored, [v][k]
   union {
-    bf16 YTb[D][LC];  // Yh^T, until U is formed
+    bf16 Yb[C][LD];  // Yh, until U is formed
     struct {
       bf16 dMb[C][LC];  // lower-incl-diag(dO U^T)
       bf16 Xb[C][LC];   // D E
@@ -1239,7 +1243,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   auto mma = [](bf16x8 x, bf16x8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0); };
 
-  static_assert(NKT <= NWV, "one v tile per wave in the Yh^T and dQ/dK phases");
+  static_assert(NKT <= NWV, "one v tile per wave in the Yh and dQ/dK phases");
   // ---- K, Q, dO and G rows (zero past T), c: every load is issued before
   //      the first LDS write
   constexpr int NIT = (C * D / 8 + 64 * NWV - 1) / (64 * NWV);
@@ -1258,33 +1262,34 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       gx1[it] = ld4(G + (size_t)r * D + c8 + 4);
     }
   }
+  // ---- the chunk-start state, staged whole (16-byte row reads; its columns
+  //      are read from LDS, transposed, where a fragment runs along v)
+  constexpr int NIS = (D * D / 8 + 64 * NWV - 1) / (64 * NWV);
+  bf16x8 sx[NIS];
+#pragma unroll
+  for (int it = 0; it < NIS; ++it) {
+    const int i = tid + 64 * NWV * it;
+    sx[it] = i < D * D / 8 ? *(const bf16x8*)(St + (size_t)8 * i) : bf16x8{};
+  }
   // ---- the global operands of every later phase, requested now so that
   //      their latency overlaps the staging instead of following a barrier:
-  //      Yh^T phase (v tile w): rows of -S^T, and V, G at (token, v);
-  //      U^T phase (token tile w % NB): rows of T; dM/E phase: Gram tiles;
-  //      dQ/dK phase (key tile w): rows of S and of dS'
+  //      Yh phase (v tile w): V and G at (token 16 J + li, v 16 w + 4g ..
+  //      + 3), 8 and 16 bytes per lane; U^T phase (token tile w % NB): rows
+  //      of T; dM/E phase: Gram tiles; dQ/dK phase (key tile w): rows of dS'
   const bool vt = w < NKT;
   const int I1 = w, I2 = w % NB;
-  bf16x8 stf[KD], snf[KD], dsf[KD];
-  float vpre[NB][4], gpre[NB][4];
+  bf16x8 dsf[KD];
+  bf16x4 vq[NB];
+  floatx4 gq[NB];
   if (vt) {
-    bf_frags<D>(stf, [&](int k0) { return -ld4(&St[(size_t)(16 * I1 + li) * D + k0]); });
 #pragma unroll
-    for (int J = 0; J < NB; ++J)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * J + 4 * g + e, v = 16 * I1 + li;
-        const bool ok = r < nval;
-        vpre[J][e] = ok ? (float)vg[(size_t)r * D + v] : 0.f;
-        gpre[J][e] = ok ? G[(size_t)r * D + v] : 0.f;
-      }
+    for (int J = 0; J < NB; ++J) {
+      const int r = 16 * J + li;
+      const bool ok = r < nval;
+      vq[J] = ok ? *(const bf16x4*)(vg + (size_t)r * D + 16 * I1 + 4 * g) : bf16x4{};
+      gq[J] = ok ? ld4(G + (size_t)r * D + 16 * I1 + 4 * g) : z;
+    }
     const int cj = 16 * I1 + li;
-    bf_frags<D>(snf, [&](int k0) {
-      floatx4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = ld1(&St[(size_t)(k0 + e) * D + cj]);
-      return x;
-    });
     bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
   }
   floatx4 tpre[2 * KC];
@@ -1313,6 +1318,11 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       st_perm(&sm.Gb[r][0], c8, pk8(cv4(gx0[it]), cv4(gx1[it])));
     }
   }
+#pragma unroll
+  for (int it = 0; it < NIS; ++it) {
+    const int i = tid + 64 * NWV * it;
+    if (i < D * D / 8) st_perm(&sm.Sb[i / (D / 8)][0], 8 * (i % (D / 8)), sx[it]);
+  }
   float fbt = 0.f;
   if (tid < C) {
     sm.al[tid] = a.al[rb + tid];
@@ -1321,23 +1331,27 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- Yh^T tiles (v tile I, token tile J): acc[e] = -(K S)[16 J + 4g + e][16 I + li];
-  //      then + V, rowsum(G * Yh) over the tile's 16 v, stored as rows of Yh^T
+  // ---- Yh tiles (token tile J, v tile I), formed transposed (S as the
+  //      first operand): acc[e] = (K S)[16 J + li][16 I + 4g + e], so a lane
+  //      holds 4 consecutive v of one token; Yh = V - K S, rowsum(G * Yh)
+  //      over the tile's 16 v, stored as rows of Yh
   if (vt) {
     const int I = I1;
+    bf16x8 stf[KD];
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) stf[kb] = MM::template ldp<NKT>(&sm.Sb[16 * I + li][0], kb);
 #pragma unroll
     for (int J = 0; J < NB; ++J) {
       floatx4 acc = z;
 #pragma unroll
-      for (int kb = 0; kb < KD; ++kb) acc = mma(MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), stf[kb], acc);
-      floatx4 gy;
+      for (int kb = 0; kb < KD; ++kb) acc = mma(stf[kb], MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), acc);
+      acc = __builtin_convertvector(vq[J], floatx4) - acc;
+      float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += vpre[J][e];
-        gy[e] = group_sum<16>(gpre[J][e] * acc[e]);
-      }
-      if (li < 4) sm.dcp[16 * J + 4 * g + li][I] = gy[li];
-      MM::store_tp(&sm.YTb[16 * I + li][0], J, acc);
+      for (int e = 0; e < 4; ++e) p += gq[J][e] * acc[e];
+      p = xor32_sum(xor16_sum(p));
+      if (g == 0) sm.dcp[16 * J + li][I] = p;
+      MM::store_tp(&sm.Yb[16 * J + li][0], I, acc);
     }
   }
   __syncthreads();
@@ -1354,7 +1368,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
     for (int J = w / NB; J < NKT; J += NWV / NB) {
       floatx4 acc = z;
 #pragma unroll
-      for (int kb = 0; kb < KC; ++kb) acc = mma(MM::template ldp<NB>(&sm.YTb[16 * J + li][0], kb), tdf[kb], acc);
+      for (int kb = 0; kb < KC; ++kb) acc = mma(tr_frag<NB, true>(&sm.Yb[0][0], Sm::LD, kb, 16 * J), tdf[kb], acc);
       MM::store_tp(&sm.Ub[16 * I + li][0], J, acc);
     }
   }
@@ -1422,12 +1436,15 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
   if (vt) {
     const int J = I1;
-    bf16x8 ktf[KC], qtf[KC];
+    bf16x8 ktf[KC], qtf[KC], snf[KD];
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
       ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
       qtf[kb] = tr_frag<NB, true>(&sm.Qb[0][0], Sm::LD, kb, 16 * J);
     }
+    // row J of S over v: column 16 J + li of the stored [v][k] tile
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) snf[kb] = tr_frag<NKT, true>(&sm.Sb[0][0], Sm::LD, kb, 16 * J);
     // the products are formed transposed (operands swapped): lane (g, li)
     // holds token 16 I + li, keys 16 J + 4g .. + 3, stored as 8 bytes
     for (int I = 0; I < NB; ++I) {
