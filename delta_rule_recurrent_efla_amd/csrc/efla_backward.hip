@@ -27,9 +27,11 @@
 // Numerics: fp32 inputs run every product as v_mfma_f32_16x16x4_f32 with fp32
 // storage. bf16 inputs with C and d multiples of 32 (the "bf16 form":
 // efla_bwd_state_kernel_bf, efla_bwd_grad_kernel_bf) take bf16 MFMA operands
-// (v_mfma_f32_16x16x32_bf16) and keep the chunk-start states, T^T, M^T and
-// dS' as bf16 in the workspace, accumulating in fp32; the other bf16 shapes
-// run the fp32 form. The gate and its derivatives are fp32 everywhere.
+// (v_mfma_f32_16x16x32_bf16) and keep the chunk-start states, T^T, M^T, dS'
+// and G as bf16 in the workspace, accumulating in fp32 (G's one fp32 use, the
+// row sum of G * Yh in dc, then takes the rounded G); the gradient kernel
+// forms K K^T itself instead of reading it. The other bf16 shapes run the
+// fp32 form. The gate and its derivatives are fp32 everywhere.
 
 #include <hip/hip_runtime.h>
 
@@ -160,14 +162,14 @@ struct BwdArgs {
   void *dq, *dk, *dv, *dbeta;
   float* ds0;
   int T, nc, coef;
-  // workspace (fp32, except sc and dsc in the bf16 form: bf16 inputs with C
-  // and d multiples of 32, where every use of them is a bf16 MFMA operand)
+  // workspace (fp32, except sc, dsc and gw in the bf16 form: bf16 inputs with
+  // C and d multiples of 32)
   const float* sc;  // [head][chunk][d_v][d_k] state at the start of each chunk
   const float* scn; // the same states, [head][chunk][d_k][d_v]
   float* dsc;       // [head][chunk][d_k][d_v] gradient of the state at each chunk's end
   float* gw;        // [head][nc C][d_v] G rows
   float *al, *fb, *fl;        // [head][nc C] c, dc/dbeta, dc/dlambda (0 past T)
-  float *gram, *tn, *tt, *mt;  // [head][chunk][C][C]: K K^T, T, T^T, M^T
+  float *gram, *tn, *tt, *mt;  // [head][chunk][C][C]: K K^T (fp32 form only), T, T^T, M^T
 };
 
 // ---------------------------------------------------------------------------
@@ -265,7 +267,9 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
     const floatx4 gk = mmk<D, sizeof(CT) == 2>(z, [&](int k0) { return ld4(&Kf[16 * J + li][k0]); },
                                                [&](int k0) { return ld4(&Kf[16 * I + li][k0]); });
     const int i = 16 * I + li, j0 = 16 * J + 4 * g;
-    *(floatx4*)&a.gram[mb + (size_t)i * C + j0] = gk;
+    // the bf16 form's gradient kernel forms these tiles itself from the same
+    // bf16 keys, with the same products in the same order
+    if constexpr (!MBF) *(floatx4*)&a.gram[mb + (size_t)i * C + j0] = gk;
     const float ci = cs[i];
     floatx4 am;
 #pragma unroll
@@ -668,9 +672,10 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
                                                         pk8(cv4(ds[2 * kb]), cv4(ds[2 * kb + 1])), acc, 0, 0, 0);
         du[I] = acc;
       }
-      // G = T^T dU; D G is dV
+      // G = T^T dU; D G is dV. G is stored as bf16: the gradient kernel
+      // takes it as a bf16 MFMA operand, and in one fp32 row sum (dc)
       floatx4 dy[NB];
-      float* grow = a.gw + ((size_t)h * a.nc * C + t0) * D;
+      bf16* grow = (bf16*)a.gw + ((size_t)h * a.nc * C + t0) * D;
       bf16* dvg = (bf16*)a.dv + ((size_t)h * a.T + t0) * D;
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(256) void efla_bwd_state_kernel_bf(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * I + 4 * g + e;
-          grow[(size_t)r * D + col] = acc[e];
+          grow[(size_t)r * D + col] = (bf16)acc[e];
           dy[I][e] = al4[e] * acc[e];
           if (r < nval) dvg[(size_t)r * D + col] = (bf16)dy[I][e];
         }
@@ -856,9 +861,10 @@ __global__ __launch_bounds__(512) void efla_bwd_state_kernel_bfp(BwdArgs a) {
                                                         pk8(cv4(ds[2 * kb]), cv4(ds[2 * kb + 1])), acc, 0, 0, 0);
         du[I] = acc;
       }
-      // G = T^T dU; D G is dV
+      // G = T^T dU; D G is dV. G is stored as bf16: the gradient kernel
+      // takes it as a bf16 MFMA operand, and in one fp32 row sum (dc)
       floatx4 dy[NB];
-      float* grow = a.gw + ((size_t)h * a.nc * C + t0) * D;
+      bf16* grow = (bf16*)a.gw + ((size_t)h * a.nc * C + t0) * D;
       bf16* dvg = (bf16*)a.dv + ((size_t)h * a.T + t0) * D;
 #pragma unroll
       for (int I = 0; I < NB; ++I) {
@@ -871,7 +877,7 @@ __global__ __launch_bounds__(512) void efla_bwd_state_kernel_bfp(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * I + 4 * g + e;
-          grow[(size_t)r * D + col] = acc[e];
+          grow[(size_t)r * D + col] = (bf16)acc[e];
           dy[I][e] = al4[e] * acc[e];
           if (r < nval) dvg[(size_t)r * D + col] = (bf16)dy[I][e];
         }
@@ -1235,7 +1241,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   const size_t rb = (size_t)h * a.nc * C + t0;
   const bf16* St = (const bf16*)a.sc + ((size_t)h * a.nc + ch) * D * D;   // [v][k]
   const bf16* dS = (const bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
-  const float* G = a.gw + rb * D;                                         // [row][v]
+  const bf16* G = (const bf16*)a.gw + rb * D;                             // [row][v]
   const bf16* kg = (const bf16*)a.k + ((size_t)h * a.T + t0) * D;
   const bf16* qg = (const bf16*)a.q + ((size_t)h * a.T + t0) * D;
   const bf16* vg = (const bf16*)a.v + ((size_t)h * a.T + t0) * D;
@@ -1247,19 +1253,16 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   // ---- K, Q, dO and G rows (zero past T), c: every load is issued before
   //      the first LDS write
   constexpr int NIT = (C * D / 8 + 64 * NWV - 1) / (64 * NWV);
-  bf16x8 kx[NIT], qx[NIT], ox[NIT];
-  floatx4 gx0[NIT], gx1[NIT];
+  bf16x8 kx[NIT], qx[NIT], ox[NIT], gx[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
-    kx[it] = qx[it] = ox[it] = bf16x8{};
-    gx0[it] = gx1[it] = z;
+    kx[it] = qx[it] = ox[it] = gx[it] = bf16x8{};
     if (i < C * D / 8 && r < nval) {
       kx[it] = *(const bf16x8*)(kg + (size_t)r * D + c8);
       qx[it] = *(const bf16x8*)(qg + (size_t)r * D + c8);
       ox[it] = *(const bf16x8*)(dog + (size_t)r * D + c8);
-      gx0[it] = ld4(G + (size_t)r * D + c8);
-      gx1[it] = ld4(G + (size_t)r * D + c8 + 4);
+      gx[it] = *(const bf16x8*)(G + (size_t)r * D + c8);
     }
   }
   // ---- the chunk-start state, staged whole (16-byte row reads; its columns
@@ -1275,7 +1278,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   //      their latency overlaps the staging instead of following a barrier:
   //      Yh phase (v tile w): V and G at (token 16 J + li, v 16 w + 4g ..
   //      + 3), 8 and 16 bytes per lane; U^T phase (token tile w % NB): rows
-  //      of T; dM/E phase: Gram tiles; dQ/dK phase (key tile w): rows of dS'
+  //      of T; dQ/dK phase (key tile w): rows of dS'
   const bool vt = w < NKT;
   const int I1 = w, I2 = w % NB;
   bf16x8 dsf[KD];
@@ -1302,12 +1305,6 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
     }
   }
   constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
-  floatx4 grp[NJ3];
-#pragma unroll
-  for (int m = 0; m < NJ3; ++m) {
-    const int J = w / NB + JS * m;
-    grp[m] = (J < NB && J <= I2) ? ld4(a.gram + mb + (size_t)(16 * I2 + li) * C + 16 * J + 4 * g) : z;
-  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
@@ -1315,7 +1312,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       st_perm(&sm.Kb[r][0], c8, kx[it]);
       st_perm(&sm.Qb[r][0], c8, qx[it]);
       st_perm(&sm.dOb[r][0], c8, ox[it]);
-      st_perm(&sm.Gb[r][0], c8, pk8(cv4(gx0[it]), cv4(gx1[it])));
+      st_perm(&sm.Gb[r][0], c8, gx[it]);
     }
   }
 #pragma unroll
@@ -1376,7 +1373,8 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
 
   // ---- dM and E tiles (token tiles I >= J; the others are zero): acc[e] =
   //      (dO U^T)[16 I + li][16 J + 4g + e], and the same with -G; X = D E;
-  //      rowsum(E * K K^T) over the tile's 16 columns
+  //      rowsum(E * K K^T) over the tile's 16 columns, with the K K^T tile
+  //      formed here in the same orientation
   {
     const int I = I2;
     const float ci = sm.al[16 * I + li];
@@ -1399,7 +1397,10 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
           m = mma(u, dof[kb], m);
           e4 = mma(u, gf[kb], e4);
         }
-        const floatx4 gr = grp[jm];
+        floatx4 gr = z;
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb)
+          gr = mma(MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), MM::template ldp<NKT>(&sm.Kb[16 * I + li][0], kb), gr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 16 * I + li, j = 16 * J + 4 * g + e;
