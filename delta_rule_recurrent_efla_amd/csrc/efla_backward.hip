@@ -322,10 +322,17 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
   }
-  // T and T^T to the workspace
+  // T (in the bf16 form T D, the only form its reader takes: rounded to bf16,
+  // columns permuted so a fragment is one 16-byte read) and T^T to the
+  // workspace
   for (int i = tid; i < C * C / 4; i += 256) {
     const int r = i / (C / 4), c4 = 4 * (i % (C / 4));
-    *(floatx4*)&a.tn[mb + (size_t)r * C + c4] = *(const floatx4*)&Ts(r, c4);
+    if constexpr (MBF) {
+      const floatx4 td = *(const floatx4*)&Ts(r, c4) * *(const floatx4*)&cs[c4];
+      *(bf16x4*)&((bf16*)a.tn)[mb + (size_t)r * C + Mma<bf16>::pcol(c4)] = __builtin_convertvector(td, bf16x4);
+    } else {
+      *(floatx4*)&a.tn[mb + (size_t)r * C + c4] = *(const floatx4*)&Ts(r, c4);
+    }
     floatx4 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = Ts(c4 + e, r);
@@ -1295,14 +1302,13 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
     const int cj = 16 * I1 + li;
     bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
   }
-  floatx4 tpre[2 * KC];
+  // row 16 I2 + li of T D as fragments (bf16, column-permuted by the prep
+  // kernel): B(j, i) = T[i][j] c_j of the U^T products
+  bf16x8 tdf[KC];
   {
-    const float* Tn = a.tn + mb;
+    const bf16* Tn = (const bf16*)a.tn + mb;
 #pragma unroll
-    for (int kb = 0; kb < KC; ++kb) {
-      tpre[2 * kb] = ld4(&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 4 * g]);
-      tpre[2 * kb + 1] = ld4(&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 16 + 4 * g]);
-    }
+    for (int kb = 0; kb < KC; ++kb) tdf[kb] = *(const bf16x8*)&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 8 * g];
   }
   constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
 #pragma unroll
@@ -1354,14 +1360,9 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   __syncthreads();
 
   // ---- U^T tiles (token tile I, v tile J): acc[e] = U[16 I + li][16 J + 4g + e];
-  //      B(j, i) = T[i][j] c_j, row i of T D, formed once per wave
+  //      B(j, i) = T[i][j] c_j, row i of T D (read once per wave)
   {
     const int I = I2;
-    bf16x8 tdf[KC];
-#pragma unroll
-    for (int kb = 0; kb < KC; ++kb)
-      tdf[kb] = pk8(cv4(tpre[2 * kb] * *(const floatx4*)&sm.al[32 * kb + 4 * g]),
-                    cv4(tpre[2 * kb + 1] * *(const floatx4*)&sm.al[32 * kb + 16 + 4 * g]));
     for (int J = w / NB; J < NKT; J += NWV / NB) {
       floatx4 acc = z;
 #pragma unroll
