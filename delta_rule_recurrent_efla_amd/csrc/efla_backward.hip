@@ -1257,81 +1257,76 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   auto mma = [](bf16x8 x, bf16x8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0); };
 
   static_assert(NKT <= NWV, "one v tile per wave in the Yh and dQ/dK phases");
-  // ---- K, Q, dO and G rows (zero past T), c: every load is issued before
-  //      the first LDS write
+  // ---- every global operand is requested here, in the order the phases
+  //      first need it; each is staged or used only where that phase starts,
+  //      so the later ones arrive while the earlier phases compute:
+  //      Yh phase: K rows, the chunk-start state (staged whole: its columns
+  //      are read from LDS, transposed, where a fragment runs along v), V and
+  //      G at (token 16 J + li, v 16 w + 4g .. + 3); U^T phase (token tile
+  //      w % NB): row 16 I2 + li of T D; dM/E phase: dO and G rows; dQ/dK
+  //      phase (key tile w): Q rows and rows of dS'.
+  //      No load sits behind a branch: rows past T are read clamped to the
+  //      last row and zeroed where they are used, so every wave issues the
+  //      same loads and each wait counts exactly the loads it needs.
   constexpr int NIT = (C * D / 8 + 64 * NWV - 1) / (64 * NWV);
-  bf16x8 kx[NIT], qx[NIT], ox[NIT], gx[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
-    kx[it] = qx[it] = ox[it] = gx[it] = bf16x8{};
-    if (i < C * D / 8 && r < nval) {
-      kx[it] = *(const bf16x8*)(kg + (size_t)r * D + c8);
-      qx[it] = *(const bf16x8*)(qg + (size_t)r * D + c8);
-      ox[it] = *(const bf16x8*)(dog + (size_t)r * D + c8);
-      gx[it] = *(const bf16x8*)(G + (size_t)r * D + c8);
-    }
-  }
-  // ---- the chunk-start state, staged whole (16-byte row reads; its columns
-  //      are read from LDS, transposed, where a fragment runs along v)
   constexpr int NIS = (D * D / 8 + 64 * NWV - 1) / (64 * NWV);
-  bf16x8 sx[NIS];
+  // when the threads cover a tile exactly, its staging has no bounds test
+  // (the compiler would otherwise move the guarded row loads behind it)
+  constexpr bool EXR = NIT * 64 * NWV == C * D / 8, EXS = NIS * 64 * NWV == D * D / 8;
+  const int rlast = nval - 1;
+  auto load_rows = [&](bf16x8* x, const bf16* src) {
 #pragma unroll
-  for (int it = 0; it < NIS; ++it) {
-    const int i = tid + 64 * NWV * it;
-    sx[it] = i < D * D / 8 ? *(const bf16x8*)(St + (size_t)8 * i) : bf16x8{};
-  }
-  // ---- the global operands of every later phase, requested now so that
-  //      their latency overlaps the staging instead of following a barrier:
-  //      Yh phase (v tile w): V and G at (token 16 J + li, v 16 w + 4g ..
-  //      + 3), 8 and 16 bytes per lane; U^T phase (token tile w % NB): rows
-  //      of T; dQ/dK phase (key tile w): rows of dS'
+    for (int it = 0; it < NIT; ++it) {
+      const int i = min(tid + 64 * NWV * it, C * D / 8 - 1), r = i / (D / 8), c8 = 8 * (i % (D / 8));
+      x[it] = *(const bf16x8*)(src + (size_t)min(r, rlast) * D + c8);
+    }
+  };
+  auto stage_rows = [&](bf16 (*dst)[Sm::LD], const bf16x8* x) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int i = tid + 64 * NWV * it, r = i / (D / 8);
+      if (EXR || i < C * D / 8) st_perm(&dst[r][0], 8 * (i % (D / 8)), r < nval ? x[it] : bf16x8{});
+    }
+  };
   const bool vt = w < NKT;
   const int I1 = w, I2 = w % NB;
-  bf16x8 dsf[KD];
-  bf16x4 vq[NB];
-  floatx4 gq[NB];
-  if (vt) {
+  const int vw = 16 * (w % NKT) + 4 * g;  // v columns of this lane in the Yh phase
+  bf16x8 kx[NIT], qx[NIT], ox[NIT], gx[NIT], sx[NIS], dsf[KD], tdf[KC];
+  bf16x4 vq[NB], gq[NB];
+  load_rows(kx, kg);
 #pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      const int r = 16 * J + li;
-      const bool ok = r < nval;
-      vq[J] = ok ? *(const bf16x4*)(vg + (size_t)r * D + 16 * I1 + 4 * g) : bf16x4{};
-      gq[J] = ok ? ld4(G + (size_t)r * D + 16 * I1 + 4 * g) : z;
-    }
-    const int cj = 16 * I1 + li;
-    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+  for (int it = 0; it < NIS; ++it) sx[it] = *(const bf16x8*)(St + (size_t)8 * min(tid + 64 * NWV * it, D * D / 8 - 1));
+  const int tc = min(tid, C - 1);
+  const float alt = a.al[rb + tc], flt = a.fl[rb + tc], fbt = a.fb[rb + tc];
+#pragma unroll
+  for (int J = 0; J < NB; ++J) {
+    const size_t r = (size_t)min(16 * J + li, rlast) * D + vw;
+    vq[J] = *(const bf16x4*)(vg + r);
+    gq[J] = *(const bf16x4*)(G + r);
   }
-  // row 16 I2 + li of T D as fragments (bf16, column-permuted by the prep
-  // kernel): B(j, i) = T[i][j] c_j of the U^T products
-  bf16x8 tdf[KC];
   {
-    const bf16* Tn = (const bf16*)a.tn + mb;
+    const bf16* Tn = (const bf16*)a.tn + mb;  // column-permuted by the prep kernel
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) tdf[kb] = *(const bf16x8*)&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 8 * g];
   }
-  constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int i = tid + 64 * NWV * it, r = i / (D / 8), c8 = 8 * (i % (D / 8));
-    if (i < C * D / 8) {
-      st_perm(&sm.Kb[r][0], c8, kx[it]);
-      st_perm(&sm.Qb[r][0], c8, qx[it]);
-      st_perm(&sm.dOb[r][0], c8, ox[it]);
-      st_perm(&sm.Gb[r][0], c8, gx[it]);
-    }
+  load_rows(ox, dog);
+  load_rows(gx, G);
+  load_rows(qx, qg);
+  {
+    const int cj = 16 * (w % NKT) + li;
+    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
   }
+  constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
+  stage_rows(sm.Kb, kx);
 #pragma unroll
   for (int it = 0; it < NIS; ++it) {
     const int i = tid + 64 * NWV * it;
-    if (i < D * D / 8) st_perm(&sm.Sb[i / (D / 8)][0], 8 * (i % (D / 8)), sx[it]);
+    if (EXS || i < D * D / 8) st_perm(&sm.Sb[i / (D / 8)][0], 8 * (i % (D / 8)), sx[it]);
   }
-  float fbt = 0.f;
-  if (tid < C) {
-    sm.al[tid] = a.al[rb + tid];
-    sm.fl[tid] = a.fl[rb + tid];
-    fbt = a.fb[rb + tid];
-  }
+  // every thread stores (those past C repeat row C - 1 with its own values):
+  // behind a tid < C test the compiler would move these loads after the rest
+  sm.al[tc] = alt;
+  sm.fl[tc] = flt;
   __syncthreads();
 
   // ---- Yh tiles (token tile J, v tile I), formed transposed (S as the
@@ -1348,10 +1343,12 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       floatx4 acc = z;
 #pragma unroll
       for (int kb = 0; kb < KD; ++kb) acc = mma(stf[kb], MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), acc);
-      acc = __builtin_convertvector(vq[J], floatx4) - acc;
+      const bool ok = 16 * J + li < nval;
+      acc = (ok ? __builtin_convertvector(vq[J], floatx4) : z) - acc;
+      const floatx4 gg = ok ? __builtin_convertvector(gq[J], floatx4) : z;
       float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) p += gq[J][e] * acc[e];
+      for (int e = 0; e < 4; ++e) p += gg[e] * acc[e];
       p = xor32_sum(xor16_sum(p));
       if (g == 0) sm.dcp[16 * J + li][I] = p;
       MM::store_tp(&sm.Yb[16 * J + li][0], I, acc);
@@ -1370,6 +1367,8 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
       MM::store_tp(&sm.Ub[16 * I + li][0], J, acc);
     }
   }
+  stage_rows(sm.dOb, ox);
+  stage_rows(sm.Gb, gx);
   __syncthreads();
 
   // ---- dM and E tiles (token tiles I >= J; the others are zero): acc[e] =
@@ -1429,6 +1428,7 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
     sm.dc[tid] = s;
     if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * fbt);
   }
+  stage_rows(sm.Qb, qx);
   __syncthreads();
 
   // ---- dQ and dK tiles (token tile I, key tile J): acc[e] at row 16 I + 4g + e,
