@@ -199,16 +199,31 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
   const CT* qg = (const CT*)a.q + ((size_t)h * a.T + t0) * D;
   constexpr int VE = 16 / (int)sizeof(LT);  // elements per 16-byte piece
   using Piece = std::conditional_t<MBF, bf16x8, floatx4>;
-  for (int i = tid; i < C * D / VE; i += 256) {
-    const int r = i / (D / VE), c = VE * (i % (D / VE));
+  // every load is issued before the first LDS write (rows past T are read
+  // clamped to the last row and staged as zeros; no load behind a branch,
+  // which would make the compiler wait for each in turn); beta of row
+  // tid / 4 with them
+  constexpr int NP = C * D / VE, NPT = (NP + 255) / 256;
+  constexpr bool EXP = NPT * 256 == NP;
+  Piece kx[NPT], qx[NPT];
+#pragma unroll
+  for (int it = 0; it < NPT; ++it) {
+    const int i = min(tid + 256 * it, NP - 1), r = min(i / (D / VE), nval - 1), c = VE * (i % (D / VE));
     if constexpr (MBF) {
-      const bf16x8 z8 = {};
-      *(bf16x8*)&Kf[r][c] = r < nval ? *(const bf16x8*)(kg + (size_t)r * D + c) : z8;
-      *(bf16x8*)&Qf[r][c] = r < nval ? *(const bf16x8*)(qg + (size_t)r * D + c) : z8;
+      kx[it] = *(const bf16x8*)(kg + (size_t)r * D + c);
+      qx[it] = *(const bf16x8*)(qg + (size_t)r * D + c);
     } else {
-      const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
-      *(floatx4*)&Kf[r][c] = r < nval ? ld4(kg + (size_t)r * D + c) : z4;
-      *(floatx4*)&Qf[r][c] = r < nval ? ld4(qg + (size_t)r * D + c) : z4;
+      kx[it] = ld4(kg + (size_t)r * D + c);
+      qx[it] = ld4(qg + (size_t)r * D + c);
+    }
+  }
+  const float bq = ld1((const CT*)a.beta + (size_t)h * a.T + t0 + min(tid >> 2, nval - 1));
+#pragma unroll
+  for (int it = 0; it < NPT; ++it) {
+    const int i = tid + 256 * it, r = i / (D / VE), c = VE * (i % (D / VE));
+    if (EXP || i < NP) {
+      *(Piece*)&Kf[r][c] = r < nval ? kx[it] : Piece{};
+      *(Piece*)&Qf[r][c] = r < nval ? qx[it] : Piece{};
     }
   }
   __syncthreads();
@@ -229,9 +244,8 @@ __global__ __launch_bounds__(256) void efla_bwd_prep_kernel(BwdArgs a) {
     if (r < C && part == 0) {
       float c = 0.f, db = 0.f, dl = 0.f;
       if (r < nval) {
-        const float b = ld1((const CT*)a.beta + (size_t)h * a.T + t0 + r);
-        c = gate_coef(a.coef, b, lam);
-        gate_coef_grad(a.coef, b, lam, db, dl);
+        c = gate_coef(a.coef, bq, lam);
+        gate_coef_grad(a.coef, bq, lam, db, dl);
       }
       cs[r] = c;
       a.al[rb + r] = c;
