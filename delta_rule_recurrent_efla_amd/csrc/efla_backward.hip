@@ -161,7 +161,7 @@ struct BwdArgs {
   const float *s0, *dsT;
   void *dq, *dk, *dv, *dbeta;
   float* ds0;
-  int T, nc, coef;
+  int T, nc, coef, nh;
   // workspace (fp32, except sc, dsc and gw in the bf16 form: bf16 inputs with
   // C and d multiples of 32)
   const float* sc;  // [head][chunk][d_v][d_k] state at the start of each chunk
@@ -1254,243 +1254,321 @@ __global__ __launch_bounds__(512) void efla_bwd_grad_kernel_bf(BwdArgs a) {
   static_assert((Sm::LD * 2) % 64 == 32 && (Sm::LC * 2) % 64 == 32, "row strides");
   __shared__ __attribute__((aligned(16))) Sm sm;
   constexpr int NKT = D / 16, NB = C / 16, NWV = 8, KD = D / 32, KC = C / 32;
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  // lane indices: passed through an empty asm at every item (step below),
+  // so the addresses formed from them are recomputed per item rather than
+  // held in registers across the whole loop
+  int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x / a.nc, ch = blockIdx.x % a.nc;
-  const int t0 = ch * C, nval = min(C, a.T - t0);
-  const size_t mb = ((size_t)h * a.nc + ch) * C * C;
-  const size_t rb = (size_t)h * a.nc * C + t0;
-  const bf16* St = (const bf16*)a.sc + ((size_t)h * a.nc + ch) * D * D;   // [v][k]
-  const bf16* dS = (const bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
-  const bf16* G = (const bf16*)a.gw + rb * D;                             // [row][v]
-  const bf16* kg = (const bf16*)a.k + ((size_t)h * a.T + t0) * D;
-  const bf16* qg = (const bf16*)a.q + ((size_t)h * a.T + t0) * D;
-  const bf16* vg = (const bf16*)a.v + ((size_t)h * a.T + t0) * D;
-  const bf16* dog = (const bf16*)a.dout + ((size_t)h * a.T + t0) * D;
   const floatx4 z = {0.f, 0.f, 0.f, 0.f};
   auto mma = [](bf16x8 x, bf16x8 y, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0); };
 
   static_assert(NKT <= NWV, "one v tile per wave in the Yh and dQ/dK phases");
-  // ---- every global operand is requested here, in the order the phases
-  //      first need it; each is staged or used only where that phase starts,
-  //      so the later ones arrive while the earlier phases compute:
-  //      Yh phase: K rows, the chunk-start state (staged whole: its columns
-  //      are read from LDS, transposed, where a fragment runs along v), V and
-  //      G at (token 16 J + li, v 16 w + 4g .. + 3); U^T phase (token tile
-  //      w % NB): row 16 I2 + li of T D; dM/E phase: dO and G rows; dQ/dK
-  //      phase (key tile w): Q rows and rows of dS'.
-  //      No load sits behind a branch: rows past T are read clamped to the
-  //      last row and zeroed where they are used, so every wave issues the
-  //      same loads and each wait counts exactly the loads it needs.
+  // The workgroups are persistent: each takes the (head, chunk) items
+  // blockIdx.x, blockIdx.x + gridDim.x, ... and requests the operands that
+  // open its next item (K rows, the state, V and G at (token, v), the
+  // scalars) during the current one, right after its Yh phase, so their
+  // latency overlaps most of an item's products (one workgroup fills a CU's
+  // LDS, so no second workgroup could). The rest of an item's operands are requested when the
+  // item starts: its first phases run while they arrive. (Holding all of
+  // the next item's operands would take more registers than a wave has.)
+  //
+  // The operands of an item are requested in the order its phases first need
+  // them, and each is staged or used only where that phase starts:
+  // Yh phase: K rows, the chunk-start state (staged whole: its columns are
+  // read from LDS, transposed, where a fragment runs along v), V and G at
+  // (token 16 J + li, v 16 w + 4g .. + 3); U^T phase (token tile w % NB): row
+  // 16 I2 + li of T D; dM/E phase: dO and G rows; dQ/dK phase (key tile w): Q
+  // rows and rows of dS'.
+  // No load sits behind a branch: rows past T are read clamped to the last
+  // row and zeroed where they are used, and the last round requests its own
+  // item again instead of none, so every wave issues the same loads and each
+  // wait counts exactly the loads it needs.
   constexpr int NIT = (C * D / 8 + 64 * NWV - 1) / (64 * NWV);
   constexpr int NIS = (D * D / 8 + 64 * NWV - 1) / (64 * NWV);
   // when the threads cover a tile exactly, its staging has no bounds test
   // (the compiler would otherwise move the guarded row loads behind it)
   constexpr bool EXR = NIT * 64 * NWV == C * D / 8, EXS = NIS * 64 * NWV == D * D / 8;
-  const int rlast = nval - 1;
-  auto load_rows = [&](bf16x8* x, const bf16* src) {
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int i = min(tid + 64 * NWV * it, C * D / 8 - 1), r = i / (D / 8), c8 = 8 * (i % (D / 8));
-      x[it] = *(const bf16x8*)(src + (size_t)min(r, rlast) * D + c8);
-    }
-  };
-  auto stage_rows = [&](bf16 (*dst)[Sm::LD], const bf16x8* x) {
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int i = tid + 64 * NWV * it, r = i / (D / 8);
-      if (EXR || i < C * D / 8) st_perm(&dst[r][0], 8 * (i % (D / 8)), r < nval ? x[it] : bf16x8{});
-    }
-  };
+  constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
   const bool vt = w < NKT;
   const int I1 = w, I2 = w % NB;
-  const int vw = 16 * (w % NKT) + 4 * g;  // v columns of this lane in the Yh phase
-  bf16x8 kx[NIT], qx[NIT], ox[NIT], gx[NIT], sx[NIS], dsf[KD], tdf[KC];
-  bf16x4 vq[NB], gq[NB];
-  load_rows(kx, kg);
+  int vw = 16 * (w % NKT) + 4 * g;  // v columns of this lane in the Yh phase
+  int tc = min(tid, C - 1);
+  struct Ops {  // requested one item ahead
+    bf16x8 kx[NIT], sx[NIS];
+    bf16x4 vq[NB], gq[NB];
+    float alt, flt, fbt;
+  };
+  struct Late {  // requested when the item starts
+    bf16x8 qx[NIT], ox[NIT], gx[NIT], dsf[KD], tdf[KC];
+  };
+  auto item_rows = [&](int item, auto f) {
+    const int h = item / a.nc, ch = item % a.nc;
+    const int t0 = ch * C, rlast = min(C, a.T - t0) - 1;
+    auto load_rows = [&](bf16x8* x, const bf16* src) {
 #pragma unroll
-  for (int it = 0; it < NIS; ++it) sx[it] = *(const bf16x8*)(St + (size_t)8 * min(tid + 64 * NWV * it, D * D / 8 - 1));
-  const int tc = min(tid, C - 1);
-  const float alt = a.al[rb + tc], flt = a.fl[rb + tc], fbt = a.fb[rb + tc];
-#pragma unroll
-  for (int J = 0; J < NB; ++J) {
-    const size_t r = (size_t)min(16 * J + li, rlast) * D + vw;
-    vq[J] = *(const bf16x4*)(vg + r);
-    gq[J] = *(const bf16x4*)(G + r);
-  }
-  {
-    const bf16* Tn = (const bf16*)a.tn + mb;  // column-permuted by the prep kernel
-#pragma unroll
-    for (int kb = 0; kb < KC; ++kb) tdf[kb] = *(const bf16x8*)&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 8 * g];
-  }
-  load_rows(ox, dog);
-  load_rows(gx, G);
-  load_rows(qx, qg);
-  {
-    const int cj = 16 * (w % NKT) + li;
-    bf_frags<D>(dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
-  }
-  constexpr int JS = NWV / NB, NJ3 = (NB + JS - 1) / JS;
-  stage_rows(sm.Kb, kx);
-#pragma unroll
-  for (int it = 0; it < NIS; ++it) {
-    const int i = tid + 64 * NWV * it;
-    if (EXS || i < D * D / 8) st_perm(&sm.Sb[i / (D / 8)][0], 8 * (i % (D / 8)), sx[it]);
-  }
-  // every thread stores (those past C repeat row C - 1 with its own values):
-  // behind a tid < C test the compiler would move these loads after the rest
-  sm.al[tc] = alt;
-  sm.fl[tc] = flt;
-  __syncthreads();
-
-  // ---- Yh tiles (token tile J, v tile I), formed transposed (S as the
-  //      first operand): acc[e] = (K S)[16 J + li][16 I + 4g + e], so a lane
-  //      holds 4 consecutive v of one token; Yh = V - K S, rowsum(G * Yh)
-  //      over the tile's 16 v, stored as rows of Yh
-  if (vt) {
-    const int I = I1;
-    bf16x8 stf[KD];
-#pragma unroll
-    for (int kb = 0; kb < KD; ++kb) stf[kb] = MM::template ldp<NKT>(&sm.Sb[16 * I + li][0], kb);
-#pragma unroll
-    for (int J = 0; J < NB; ++J) {
-      floatx4 acc = z;
-#pragma unroll
-      for (int kb = 0; kb < KD; ++kb) acc = mma(stf[kb], MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), acc);
-      const bool ok = 16 * J + li < nval;
-      acc = (ok ? __builtin_convertvector(vq[J], floatx4) : z) - acc;
-      const floatx4 gg = ok ? __builtin_convertvector(gq[J], floatx4) : z;
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p += gg[e] * acc[e];
-      p = xor32_sum(xor16_sum(p));
-      if (g == 0) sm.dcp[16 * J + li][I] = p;
-      MM::store_tp(&sm.Yb[16 * J + li][0], I, acc);
-    }
-  }
-  __syncthreads();
-
-  // ---- U^T tiles (token tile I, v tile J): acc[e] = U[16 I + li][16 J + 4g + e];
-  //      B(j, i) = T[i][j] c_j, row i of T D (read once per wave)
-  {
-    const int I = I2;
-    for (int J = w / NB; J < NKT; J += NWV / NB) {
-      floatx4 acc = z;
-#pragma unroll
-      for (int kb = 0; kb < KC; ++kb) acc = mma(tr_frag<NB, true>(&sm.Yb[0][0], Sm::LD, kb, 16 * J), tdf[kb], acc);
-      MM::store_tp(&sm.Ub[16 * I + li][0], J, acc);
-    }
-  }
-  stage_rows(sm.dOb, ox);
-  stage_rows(sm.Gb, gx);
-  __syncthreads();
-
-  // ---- dM and E tiles (token tiles I >= J; the others are zero): acc[e] =
-  //      (dO U^T)[16 I + li][16 J + 4g + e], and the same with -G; X = D E;
-  //      rowsum(E * K K^T) over the tile's 16 columns, with the K K^T tile
-  //      formed here in the same orientation
-  {
-    const int I = I2;
-    const float ci = sm.al[16 * I + li];
-    bf16x8 dof[KD], gf[KD];
-#pragma unroll
-    for (int kb = 0; kb < KD; ++kb) {
-      dof[kb] = MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb);
-      gf[kb] = MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb);
-    }
-#pragma unroll
-    for (int jm = 0; jm < NJ3; ++jm) {
-      const int J = w / NB + JS * jm;
-      if (J >= NB) break;
-      floatx4 m = z, e4 = z;
-      float s = 0.f;
-      if (J <= I) {
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb) {
-          const bf16x8 u = MM::template ldp<NKT>(&sm.Ub[16 * J + li][0], kb);
-          m = mma(u, dof[kb], m);
-          e4 = mma(u, gf[kb], e4);
-        }
-        floatx4 gr = z;
-#pragma unroll
-        for (int kb = 0; kb < KD; ++kb)
-          gr = mma(MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), MM::template ldp<NKT>(&sm.Kb[16 * I + li][0], kb), gr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + li, j = 16 * J + 4 * g + e;
-          m[e] = j <= i ? m[e] : 0.f;
-          e4[e] = j < i ? -e4[e] : 0.f;
-          s += e4[e] * gr[e];
-          e4[e] *= ci;
-        }
+      for (int it = 0; it < NIT; ++it) {
+        const int i = min(tid + 64 * NWV * it, C * D / 8 - 1), r = i / (D / 8), c8 = 8 * (i % (D / 8));
+        x[it] = *(const bf16x8*)(src + (size_t)min(r, rlast) * D + c8);
       }
-      s = xor32_sum(xor16_sum(s));
-      if (g == 0) sm.dcp2[16 * I + li][J] = s;
-      MM::store_tp(&sm.m.dMb[16 * I + li][0], J, m);
-      MM::store_tp(&sm.m.Xb[16 * I + li][0], J, e4);
+    };
+    f(h, ch, t0, rlast, load_rows);
+  };
+  auto request_late = [&](int item, Late& o) {
+    item_rows(item, [&](int h, int ch, int t0, int rlast, auto load_rows) {
+      const size_t mb = ((size_t)h * a.nc + ch) * C * C;
+      const size_t rb = (size_t)h * a.nc * C + t0;
+      const size_t tok = ((size_t)h * a.T + t0) * D;
+      const bf16* Tn = (const bf16*)a.tn + mb;  // column-permuted by the prep kernel
+#pragma unroll
+      for (int kb = 0; kb < KC; ++kb) o.tdf[kb] = *(const bf16x8*)&Tn[(size_t)(16 * I2 + li) * C + 32 * kb + 8 * g];
+      load_rows(o.ox, (const bf16*)a.dout + tok);
+      load_rows(o.gx, (const bf16*)a.gw + rb * D);
+      load_rows(o.qx, (const bf16*)a.q + tok);
+      const bf16* dS = (const bf16*)a.dsc + ((size_t)h * a.nc + ch) * D * D;  // [k][v]
+      const int cj = 16 * (w % NKT) + li;
+      bf_frags<D>(o.dsf, [&](int k0) { return ld4(&dS[(size_t)cj * D + k0]); });
+    });
+  };
+  auto request = [&](int item, Ops& o) {
+    item_rows(item, [&](int h, int ch, int t0, int rlast, auto load_rows) {
+      const size_t rb = (size_t)h * a.nc * C + t0;
+      const bf16* St = (const bf16*)a.sc + ((size_t)h * a.nc + ch) * D * D;  // [v][k]
+      const size_t tok = ((size_t)h * a.T + t0) * D;
+      load_rows(o.kx, (const bf16*)a.k + tok);
+#pragma unroll
+      for (int it = 0; it < NIS; ++it)
+        o.sx[it] = *(const bf16x8*)(St + (size_t)8 * min(tid + 64 * NWV * it, D * D / 8 - 1));
+      o.alt = a.al[rb + tc];
+      o.flt = a.fl[rb + tc];
+      o.fbt = a.fb[rb + tc];
+#pragma unroll
+      for (int J = 0; J < NB; ++J) {
+        const size_t r = (size_t)min(16 * J + li, rlast) * D + vw;
+        o.vq[J] = *(const bf16x4*)((const bf16*)a.v + tok + r);
+        o.gq[J] = *(const bf16x4*)((const bf16*)a.gw + rb * D + r);
+      }
+    });
+  };
+  auto process = [&](int item, const Ops& o, const Late& l, auto after_yh) {
+    const int h = item / a.nc, ch = item % a.nc;
+    const int t0 = ch * C, nval = min(C, a.T - t0);
+    const auto& vq = o.vq;
+    const auto& gq = o.gq;
+    const auto& tdf = l.tdf;
+    const auto& dsf = l.dsf;
+    const float fbt = o.fbt;
+    auto stage_rows = [&](bf16 (*dst)[Sm::LD], const bf16x8* x) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i = tid + 64 * NWV * it, r = i / (D / 8);
+        if (EXR || i < C * D / 8) st_perm(&dst[r][0], 8 * (i % (D / 8)), r < nval ? x[it] : bf16x8{});
+      }
+    };
+    const auto& ox = l.ox;
+    const auto& gx = l.gx;
+    const auto& qx = l.qx;
+    stage_rows(sm.Kb, o.kx);
+#pragma unroll
+    for (int it = 0; it < NIS; ++it) {
+      const int i = tid + 64 * NWV * it;
+      if (EXS || i < D * D / 8) st_perm(&sm.Sb[i / (D / 8)][0], 8 * (i % (D / 8)), o.sx[it]);
     }
-  }
-  __syncthreads();
+    // every thread stores (those past C repeat row C - 1 with its own
+    // values): behind a tid < C test the compiler would move these loads
+    // after the rest
+    sm.al[tc] = o.alt;
+    sm.fl[tc] = o.flt;
+    __syncthreads();
 
-  // ---- dc, dbeta
-  if (tid < C) {
-    float s = 0.f;
+    // ---- Yh tiles (token tile J, v tile I), formed transposed (S as the
+    //      first operand): acc[e] = (K S)[16 J + li][16 I + 4g + e], so a lane
+    //      holds 4 consecutive v of one token; Yh = V - K S, rowsum(G * Yh)
+    //      over the tile's 16 v, stored as rows of Yh
+    if (vt) {
+      const int I = I1;
+      bf16x8 stf[KD];
 #pragma unroll
-    for (int I = 0; I < NKT; ++I) s += sm.dcp[tid][I];
+      for (int kb = 0; kb < KD; ++kb) stf[kb] = MM::template ldp<NKT>(&sm.Sb[16 * I + li][0], kb);
 #pragma unroll
-    for (int J = 0; J < NB; ++J) s += sm.dcp2[tid][J];
-    sm.dc[tid] = s;
-    if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * fbt);
-  }
-  stage_rows(sm.Qb, qx);
-  __syncthreads();
-
-  // ---- dQ and dK tiles (token tile I, key tile J): acc[e] at row 16 I + 4g + e,
-  //      column 16 J + li; wave w takes key tile J and forms the fragments of
-  //      row J of S, dS' (over v) and of columns J of K, Q (over tokens) once
-  bf16* dqg = (bf16*)a.dq + ((size_t)h * a.T + t0) * D;
-  bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
-  if (vt) {
-    const int J = I1;
-    bf16x8 ktf[KC], qtf[KC], snf[KD];
+      for (int J = 0; J < NB; ++J) {
+        floatx4 acc = z;
 #pragma unroll
-    for (int kb = 0; kb < KC; ++kb) {
-      ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
-      qtf[kb] = tr_frag<NB, true>(&sm.Qb[0][0], Sm::LD, kb, 16 * J);
+        for (int kb = 0; kb < KD; ++kb) acc = mma(stf[kb], MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), acc);
+        const bool ok = 16 * J + li < nval;
+        acc = (ok ? __builtin_convertvector(vq[J], floatx4) : z) - acc;
+        const floatx4 gg = ok ? __builtin_convertvector(gq[J], floatx4) : z;
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p += gg[e] * acc[e];
+        p = xor32_sum(xor16_sum(p));
+        if (g == 0) sm.dcp[16 * J + li][I] = p;
+        MM::store_tp(&sm.Yb[16 * J + li][0], I, acc);
+      }
     }
-    // row J of S over v: column 16 J + li of the stored [v][k] tile
+    __syncthreads();
+    after_yh();  // this item's opening registers are free now
+
+    // ---- U^T tiles (token tile I, v tile J): acc[e] = U[16 I + li][16 J + 4g + e];
+    //      B(j, i) = T[i][j] c_j, row i of T D (read once per wave)
+    {
+      const int I = I2;
+      for (int J = w / NB; J < NKT; J += NWV / NB) {
+        floatx4 acc = z;
 #pragma unroll
-    for (int kb = 0; kb < KD; ++kb) snf[kb] = tr_frag<NKT, true>(&sm.Sb[0][0], Sm::LD, kb, 16 * J);
-    // the products are formed transposed (operands swapped): lane (g, li)
-    // holds token 16 I + li, keys 16 J + 4g .. + 3, stored as 8 bytes
-    for (int I = 0; I < NB; ++I) {
-      floatx4 dq = z, dk = z, dg = z;
+        for (int kb = 0; kb < KC; ++kb) acc = mma(tr_frag<NB, true>(&sm.Yb[0][0], Sm::LD, kb, 16 * J), tdf[kb], acc);
+        MM::store_tp(&sm.Ub[16 * I + li][0], J, acc);
+      }
+    }
+    stage_rows(sm.dOb, ox);
+    stage_rows(sm.Gb, gx);
+    __syncthreads();
+
+    // ---- dM and E tiles (token tiles I >= J; the others are zero): acc[e] =
+    //      (dO U^T)[16 I + li][16 J + 4g + e], and the same with -G; X = D E;
+    //      rowsum(E * K K^T) over the tile's 16 columns, with the K K^T tile
+    //      formed here in the same orientation
+    {
+      const int I = I2;
+      const float ci = sm.al[16 * I + li];
+      bf16x8 dof[KD], gf[KD];
 #pragma unroll
       for (int kb = 0; kb < KD; ++kb) {
-        dq = mma(snf[kb], MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb), dq);
-        dk = mma(dsf[kb], MM::template ldp<NKT>(&sm.Ub[16 * I + li][0], kb), dk);
-        dg = mma(snf[kb], MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb), dg);
+        dof[kb] = MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb);
+        gf[kb] = MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb);
       }
 #pragma unroll
-      for (int kb = 0; kb < KC; ++kb) {
-        dq = mma(ktf[kb], MM::template ldp<NB>(&sm.m.dMb[16 * I + li][0], kb), dq);
-        dk = mma(qtf[kb], tr_frag<NB, true>(&sm.m.dMb[0][0], Sm::LC, kb, 16 * I), dk);
-        dk = mma(ktf[kb], MM::template ldp<NB>(&sm.m.Xb[16 * I + li][0], kb), dk);
-        dk = mma(ktf[kb], tr_frag<NB, true>(&sm.m.Xb[0][0], Sm::LC, kb, 16 * I), dk);
-      }
-      const int r = 16 * I + li, k4 = 16 * J + 4 * g;
-      if (r < nval) {
-        // pcol keeps 4-aligned runs of 4 columns together
-        const floatx4 kv = __builtin_convertvector(*(const bf16x4*)&sm.Kb[r][MM::pcol(k4)], floatx4);
-        const float ar = sm.al[r], fr = 2.f * sm.dc[r] * sm.fl[r];
-        floatx4 dkr;
+      for (int jm = 0; jm < NJ3; ++jm) {
+        const int J = w / NB + JS * jm;
+        if (J >= NB) break;
+        floatx4 m = z, e4 = z;
+        float s = 0.f;
+        if (J <= I) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dkr[e] = dk[e] - ar * dg[e] + fr * kv[e];
-        *(bf16x4*)&dqg[(size_t)r * D + k4] = cv4(dq);
-        *(bf16x4*)&dkg[(size_t)r * D + k4] = cv4(dkr);
+          for (int kb = 0; kb < KD; ++kb) {
+            const bf16x8 u = MM::template ldp<NKT>(&sm.Ub[16 * J + li][0], kb);
+            m = mma(u, dof[kb], m);
+            e4 = mma(u, gf[kb], e4);
+          }
+          floatx4 gr = z;
+#pragma unroll
+          for (int kb = 0; kb < KD; ++kb)
+            gr = mma(MM::template ldp<NKT>(&sm.Kb[16 * J + li][0], kb), MM::template ldp<NKT>(&sm.Kb[16 * I + li][0], kb), gr);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + li, j = 16 * J + 4 * g + e;
+            m[e] = j <= i ? m[e] : 0.f;
+            e4[e] = j < i ? -e4[e] : 0.f;
+            s += e4[e] * gr[e];
+            e4[e] *= ci;
+          }
+        }
+        s = xor32_sum(xor16_sum(s));
+        if (g == 0) sm.dcp2[16 * I + li][J] = s;
+        MM::store_tp(&sm.m.dMb[16 * I + li][0], J, m);
+        MM::store_tp(&sm.m.Xb[16 * I + li][0], J, e4);
       }
     }
+    __syncthreads();
+
+    // ---- dc, dbeta
+    if (tid < C) {
+      float s = 0.f;
+#pragma unroll
+      for (int I = 0; I < NKT; ++I) s += sm.dcp[tid][I];
+#pragma unroll
+      for (int J = 0; J < NB; ++J) s += sm.dcp2[tid][J];
+      sm.dc[tid] = s;
+      if (tid < nval) ((bf16*)a.dbeta)[(size_t)h * a.T + t0 + tid] = (bf16)(s * fbt);
+    }
+    stage_rows(sm.Qb, qx);
+    __syncthreads();
+
+    // ---- dQ and dK tiles (token tile I, key tile J): acc[e] at row 16 I + 4g + e,
+    //      column 16 J + li; wave w takes key tile J and forms the fragments of
+    //      row J of S, dS' (over v) and of columns J of K, Q (over tokens) once
+    bf16* dqg = (bf16*)a.dq + ((size_t)h * a.T + t0) * D;
+    bf16* dkg = (bf16*)a.dk + ((size_t)h * a.T + t0) * D;
+    if (vt) {
+      const int J = I1;
+      bf16x8 ktf[KC], qtf[KC], snf[KD];
+#pragma unroll
+      for (int kb = 0; kb < KC; ++kb) {
+        ktf[kb] = tr_frag<NB, true>(&sm.Kb[0][0], Sm::LD, kb, 16 * J);
+        qtf[kb] = tr_frag<NB, true>(&sm.Qb[0][0], Sm::LD, kb, 16 * J);
+      }
+      // row J of S over v: column 16 J + li of the stored [v][k] tile
+#pragma unroll
+      for (int kb = 0; kb < KD; ++kb) snf[kb] = tr_frag<NKT, true>(&sm.Sb[0][0], Sm::LD, kb, 16 * J);
+      // the products are formed transposed (operands swapped): lane (g, li)
+      // holds token 16 I + li, keys 16 J + 4g .. + 3, stored as 8 bytes
+      for (int I = 0; I < NB; ++I) {
+        floatx4 dq = z, dk = z, dg = z;
+#pragma unroll
+        for (int kb = 0; kb < KD; ++kb) {
+          dq = mma(snf[kb], MM::template ldp<NKT>(&sm.dOb[16 * I + li][0], kb), dq);
+          dk = mma(dsf[kb], MM::template ldp<NKT>(&sm.Ub[16 * I + li][0], kb), dk);
+          dg = mma(snf[kb], MM::template ldp<NKT>(&sm.Gb[16 * I + li][0], kb), dg);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KC; ++kb) {
+          dq = mma(ktf[kb], MM::template ldp<NB>(&sm.m.dMb[16 * I + li][0], kb), dq);
+          dk = mma(qtf[kb], tr_frag<NB, true>(&sm.m.dMb[0][0], Sm::LC, kb, 16 * I), dk);
+          dk = mma(ktf[kb], MM::template ldp<NB>(&sm.m.Xb[16 * I + li][0], kb), dk);
+          dk = mma(ktf[kb], tr_frag<NB, true>(&sm.m.Xb[0][0], Sm::LC, kb, 16 * I), dk);
+        }
+        const int r = 16 * I + li, k4 = 16 * J + 4 * g;
+        if (r < nval) {
+          // pcol keeps 4-aligned runs of 4 columns together
+          const floatx4 kv = __builtin_convertvector(*(const bf16x4*)&sm.Kb[r][MM::pcol(k4)], floatx4);
+          const float ar = sm.al[r], fr = 2.f * sm.dc[r] * sm.fl[r];
+          floatx4 dkr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dkr[e] = dk[e] - ar * dg[e] + fr * kv[e];
+          *(bf16x4*)&dqg[(size_t)r * D + k4] = cv4(dq);
+          *(bf16x4*)&dkg[(size_t)r * D + k4] = cv4(dkr);
+        }
+      }
+    }
+  };
+  const int nitems = a.nh * a.nc;
+  int item = blockIdx.x;  // the grid holds at most nitems workgroups
+  // one item: its late operands, its products, and after its Yh phase (when
+  // its own opening registers are dead) the next item's opening operands;
+  // false after the last item. Two register sets alternate (the loop body
+  // takes two items), so nothing is copied and no wait covers this item's
+  // stores
+  auto step = [&](const Ops& cur, Ops& nx) {
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(li), "+v"(g), "+v"(vw), "+v"(tc));
+    const int nxt = item + (int)gridDim.x;
+    Late late;
+    request_late(item, late);
+    process(item, cur, late, [&] { request(nxt < nitems ? nxt : item, nx); });
+    if (nxt >= nitems) return false;
+    __syncthreads();  // the LDS reads of this item are done before the next staging
+    item = nxt;
+    return true;
+  };
+  Ops A, B;
+  request(item, A);
+  while (step(A, B) && step(B, A)) {
   }
+  // the last round's requests (its own item again) are drained before the
+  // waves end
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Compute units of the current device (the persistent gradient kernel runs
+// one workgroup per CU), cached per device.
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 // ---------------------------------------------------------------------------
@@ -1511,7 +1589,8 @@ static hipError_t launch_bwd(const BwdArgs& a, int NH, hipStream_t stream) {
                        stream, a);
   }
   if constexpr (sizeof(CT) == 2 && C % 32 == 0 && D % 32 == 0) {
-    hipLaunchKernelGGL((efla_bwd_grad_kernel_bf<D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
+    const int items = NH * a.nc;
+    hipLaunchKernelGGL((efla_bwd_grad_kernel_bf<D, C>), dim3((unsigned)min(items, device_cus())), dim3(512), 0, stream, a);
   } else {
     hipLaunchKernelGGL((efla_bwd_grad_kernel<CT, D, C>), dim3((unsigned)(NH * a.nc)), dim3(512), 0, stream, a);
   }
@@ -1616,6 +1695,7 @@ hipError_t efla_internal_launch_bwd(const void* q, const void* k, const void* v,
   a.ds0 = ds0;
   a.T = T;
   a.nc = (int)nc;
+  a.nh = NH;
   a.coef = coef;
   float* sc = p;
   p += (size_t)NH * nc * d * d;
