@@ -23,7 +23,8 @@
 //   3. efla_bwd_state_kernel, one workgroup per (head, 64-column slice),
 //      chunks last to first: the dS recurrence (the only serial part), dV,
 //      G and the dS' of every chunk;
-//   4. efla_bwd_grad_kernel, one workgroup per (head, chunk): dq, dk, dbeta.
+//   4. efla_bwd_grad_kernel, one workgroup per (head, chunk) (in the bf16
+//      form one persistent workgroup per CU over those items): dq, dk, dbeta.
 // Numerics: fp32 inputs run every product as v_mfma_f32_16x16x4_f32 with fp32
 // storage. bf16 inputs with C and d multiples of 32 (the "bf16 form":
 // efla_bwd_state_kernel_bf, efla_bwd_grad_kernel_bf) take bf16 MFMA operands

@@ -229,10 +229,11 @@ size_t efla_bwd_chunked_workspace_bytes(int B, int H, int T, int d_k, int d_v, i
  * The forward is recomputed inside (the chunk-start states go to the
  * workspace). Numerics: for fp32 inputs every product is fp32 MFMA with fp32
  * storage. For bf16 inputs with chunk and d multiples of 32, the products
- * take bf16 MFMA operands (the saved chunk-start states, T^T, M^T and the
- * state gradients are stored as bf16, which is exactly the rounding their
- * consumers apply) and accumulate in fp32; other bf16 shapes run the fp32
- * form. The gate, its derivatives and every accumulator are fp32. Supported sizes are
+ * take bf16 MFMA operands (the saved chunk-start states, T^T, M^T, T diag(c)
+ * and the state gradients are stored as bf16, which is exactly the rounding
+ * their consumers apply; so is G = T^T dU, whose one fp32 use, a row sum in
+ * dc, then takes the rounded value) and accumulate in fp32; other bf16
+ * shapes run the fp32 form. The gate, its derivatives and every accumulator are fp32. Supported sizes are
  * the forward's; where the forward's pipelined kernel does not serve the
  * chunk size, the backward runs with chunk 32 (same result up to rounding).
  * Errors as for efla_fwd_chunked; a missing or short workspace is
