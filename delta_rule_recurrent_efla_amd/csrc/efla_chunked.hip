@@ -619,10 +619,11 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 //                     loaders formed A_bb)           (four blocks) row block 3 of
 //                                                    M, of c+1
 //   prep 2..5      A: stage K, Q, V of c+1;      B: the other Q K^T tiles of
-//   ("loaders")       one Q K^T tile of c;           c+1; a (and with four
-//                     load the keys of c+2 (with     blocks the diagonal Gram
-//                     four blocks: keys, betas,      blocks) of c+2; load Q, V
-//                     queries and values of c+3)     of c+2
+//   ("loaders")       one Q K^T tile of c (with      c+1 (with four blocks:
+//                     four blocks: loaders 0, 1);    loaders 2, 3); a (and with
+//                     load the keys of c+2 (with     four blocks the diagonal
+//                     four blocks: keys, betas,      Gram blocks) of c+2; load
+//                     queries and values of c+3)     Q, V of c+2
 // Waves are placed on the SIMDs round robin: the two state waves and the two
 // solvers get a SIMD each, and every SIMD also runs one loader. Every global
 // load is issued as soon as its registers are free and consumed one chunk
@@ -1487,13 +1488,19 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
     auto loader = [&](auto pwc) {
       constexpr int PW = decltype(pwc)::value;  // loader 0..3
       using JB = PrepJobs<NB>;
-      constexpr int NJ = NQKL > PW ? (NQKL - PW + 3) / 4 : 0;  // Q K^T jobs PW, PW + 4, ...
-      // The first of this wave's jobs of a chunk runs in phase A of the
-      // chunk's own state pass (its K and Q were staged one phase before, the
-      // state reads M only in phase B); the others one chunk ahead in phase B.
-      // With the solvers on row block 3, loaders 2 and 3 (which share their
-      // SIMDs with the solvers and stage the longest in phase A) keep their
-      // one job in phase B.
+      // Q K^T jobs of this wave, in the order of PrepJobs (jobs 0..5 of rows
+      // 0..2 are tiles (0,0) (1,0) (1,1) (2,0) (2,1) (2,2)). The first of a
+      // wave's jobs runs in phase A of the chunk's own state pass (its K and
+      // Q were staged one phase before, the state reads M only in phase B);
+      // the others one chunk ahead in phase B. With the solvers on row block
+      // 3 (six jobs left), loaders 0 and 1, which share their SIMDs with the
+      // state waves, take one job each, (0,0) and (1,0), in phase A and leave
+      // phase B to the state waves' products; loaders 2 and 3 take (1,1),
+      // (2,1) and (2,0), (2,2) in phase B (measured, same box: 1.3B layer
+      // 149 -> 144 us, 340M layer 73 -> 70 us). Otherwise jobs PW, PW + 4, ...
+      constexpr bool XJ = NQKL == 6 && outs;
+      constexpr int NJ = XJ ? (PW < 2 ? 1 : 2) : (NQKL > PW ? (NQKL - PW + 3) / 4 : 0);
+      auto ljob = [](int t) constexpr { return XJ ? (PW < 2 ? PW : PW + 2 * t) : PW + 4 * t; };
       constexpr int NA = (outs && NJ > 0 && !(SM3 && PW >= 2)) ? 1 : 0;
       // jobs [J0, J1) of this wave on buffer Bm: every fragment first, then
       // the products (one exposed LDS round trip)
@@ -1503,7 +1510,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           const int li = lane & 15, g = lane >> 4;
           Frag kfr[J1 - J0][NFK], qfr[J1 - J0][NFK];
           static_for<J1 - J0>([&](auto jc) {
-            constexpr int j = JB::NOFF + PW + 4 * (J0 + decltype(jc)::value);
+            constexpr int j = JB::NOFF + ljob(J0 + decltype(jc)::value);
             constexpr int I = JB::I(j), J = JB::J(j);
 #pragma unroll
             for (int f = 0; f < NFK; ++f) {
@@ -1521,7 +1528,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
                   MM::mma(acc[decltype(jc)::value], kfr[decltype(jc)::value][f], qfr[decltype(jc)::value][f]);
           });
           static_for<J1 - J0>([&](auto jc) {
-            constexpr int j = JB::NOFF + PW + 4 * (J0 + decltype(jc)::value);
+            constexpr int j = JB::NOFF + ljob(J0 + decltype(jc)::value);
             constexpr int I = JB::I(j), J = JB::J(j);
             floatx4 v = acc[decltype(jc)::value];
             if constexpr (GATED) {
@@ -1623,7 +1630,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           // the fragments of this wave's phase-A M job (chunk c, the other
           // buffer) are requested before the staging writes, so that their
           // LDS round trip overlaps the staging
-          using JA = std::integral_constant<int, JB::NOFF + PW>;
+          using JA = std::integral_constant<int, JB::NOFF + ljob(0)>;
           Frag akf[NA > 0 ? NFK : 1], aqf[NA > 0 ? NFK : 1];
           if constexpr (NA > 0) {
             if (c >= 0) {
