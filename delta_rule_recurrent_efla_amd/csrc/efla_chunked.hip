@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256, 1) void efla_chunked_kernel(ChunkedArgs a) {
 //                                                    M, of c+1
 //   prep 2..5      A: stage K, Q, V of c+1;      B: the other Q K^T tiles of
 //   ("loaders")       one Q K^T tile of c (with      c+1 (with four blocks:
-//                     four blocks: loaders 0, 1);    loaders 2, 3); a (and with
+//                     four blocks: loaders 2, 3);    loaders 2, 3); a (and with
 //                     load the keys of c+2 (with     four blocks the diagonal
 //                     four blocks: keys, betas,      Gram blocks) of c+2; load
 //                     queries and values of c+3)     Q, V of c+2
@@ -1494,14 +1494,16 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
       // Q were staged one phase before, the state reads M only in phase B);
       // the others one chunk ahead in phase B. With the solvers on row block
       // 3 (six jobs left), loaders 0 and 1, which share their SIMDs with the
-      // state waves, take one job each, (0,0) and (1,0), in phase A and leave
-      // phase B to the state waves' products; loaders 2 and 3 take (1,1),
-      // (2,1) and (2,0), (2,2) in phase B (measured, same box: 1.3B layer
-      // 149 -> 144 us, 340M layer 73 -> 70 us). Otherwise jobs PW, PW + 4, ...
+      // state waves, form no tile: the state waves' products have those
+      // SIMDs' MFMA pipes to themselves. Loaders 2 and 3 take (0,0), (1,1),
+      // (2,1) and (1,0), (2,0), (2,2), the first in phase A (measured, same
+      // box: 1.3B layer 149 -> 141 us, 340M layer 73 -> 68 us against one
+      // tile per loader). Otherwise jobs PW, PW + 4, ... with the first in
+      // phase A except on loaders 2 and 3 next to the solvers' row block 3.
       constexpr bool XJ = NQKL == 6 && outs;
-      constexpr int NJ = XJ ? (PW < 2 ? 1 : 2) : (NQKL > PW ? (NQKL - PW + 3) / 4 : 0);
-      auto ljob = [](int t) constexpr { return XJ ? (PW < 2 ? PW : PW + 2 * t) : PW + 4 * t; };
-      constexpr int NA = (outs && NJ > 0 && !(SM3 && PW >= 2)) ? 1 : 0;
+      constexpr int NJ = XJ ? (PW < 2 ? 0 : 3) : (NQKL > PW ? (NQKL - PW + 3) / 4 : 0);
+      auto ljob = [](int t) constexpr { return XJ ? PW - 2 + 2 * t : PW + 4 * t; };
+      constexpr int NA = XJ ? (PW < 2 ? 0 : 1) : ((outs && NJ > 0 && !(SM3 && PW >= 2)) ? 1 : 0);
       // jobs [J0, J1) of this wave on buffer Bm: every fragment first, then
       // the products (one exposed LDS round trip)
       auto mtiles = [&](auto& Bm, auto j0c, auto j1c, const float* gb) {
