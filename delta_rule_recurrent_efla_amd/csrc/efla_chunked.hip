@@ -765,7 +765,7 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // a_r (K_L K_L^T)_{rc}, c < r, and leaves it in LDS: the solvers' phase A
   // starts at the forward substitution, with no key fetch, no Gram product
   // and no LDS round trip of their own.
-  constexpr bool LGRAM = sizeof(CT) == 2 && NB == 4 && PM != 1 && D >= 32;
+  constexpr bool LGRAM = sizeof(CT) == 2 && NB == 4 && D >= 32;
   // With four 16-row blocks and outputs, the solvers form row block 3 of
   // M = tril(Q K^T): their key fragments of blocks 0..3 are in registers
   // for the Gram tiles, so each adds only the query fragments of block 3
@@ -1543,16 +1543,25 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           });
         }
       };
-      // LGRAM: this loader's block PW of key rows in MFMA operand layout:
-      // lane (g, li) holds row 16 PW + li, 16-byte pieces at columns
-      // 32 f + 8 g (the pieces' k order only has to agree between the two
-      // Gram operands, which are these same registers), and that row's beta
+      // LGRAM: this loader's blocks PW, PW + NLW, ... of key rows (one with
+      // four loaders, two with the summaries' two) in MFMA operand layout:
+      // lane (g, li) holds row 16 b + li of block b, 16-byte pieces at
+      // columns 32 f + 8 g (the pieces' k order only has to agree between
+      // the two Gram operands, which are these same registers), and that
+      // row's beta
       const int li0 = lane & 15, g0 = lane >> 4;
+      constexpr int NLW = pipe_loaders<PM>();
       constexpr int NKB = LGRAM ? NFK : 1;
-      unsigned kboff[NKB];
+      constexpr int NBL = LGRAM ? NB / NLW : 1;  // key blocks of this loader
+      static_assert(!LGRAM || NB % NLW == 0, "key blocks per loader");
+      static_assert(!GATED || NBL == 1, "gated pass: one key block per loader");
+      unsigned kboff[NBL][NKB];
       if constexpr (LGRAM) {
 #pragma unroll
-        for (int f = 0; f < NFK; ++f) kboff[f] = (unsigned)(((16 * PW + li0) * D + 32 * f + 8 * g0) * (int)sizeof(CT));
+        for (int i = 0; i < NBL; ++i)
+#pragma unroll
+          for (int f = 0; f < NFK; ++f)
+            kboff[i][f] = (unsigned)(((16 * (PW + NLW * i) + li0) * D + 32 * f + 8 * g0) * (int)sizeof(CT));
       }
       if constexpr (LGRAM) {
         // Two register sets, each holding one chunk's keys (in the layout
@@ -1560,8 +1569,8 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         // phase A two chunk steps before it is staged, and one and a half
         // before its gate and Gram block are formed from it.
         struct LB {
-          Vec kb[NKB];
-          CT kbeta;
+          Vec kb[NBL][NKB];
+          CT kbeta[NBL];
           Vec q[NLK];
           Vec v[NLV];
           float lgv;  // gated: log-decay of the chunk's row `lane`
@@ -1570,10 +1579,13 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
         auto load_all = [&](LB& b, int chunk) {
           const auto rk = chunk_rsrc(kg, chunk, 0);
 #pragma unroll
-          for (int f = 0; f < NKB; ++f) buf_load(rk, kboff[f], b.kb[f]);
+          for (int i = 0; i < NBL; ++i)
+#pragma unroll
+            for (int f = 0; f < NKB; ++f) buf_load(rk, kboff[i][f], b.kb[i][f]);
           const long long tok = (long long)chunk * C;
-          buf_load(buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT)),
-                   (unsigned)((16 * PW + li0) * (int)sizeof(CT)), b.kbeta);
+          const auto rb = buf_rsrc(bg + tok, (long long)(T - tok) * (long long)sizeof(CT));
+#pragma unroll
+          for (int i = 0; i < NBL; ++i) buf_load(rb, (unsigned)((16 * (PW + NLW * i) + li0) * (int)sizeof(CT)), b.kbeta[i]);
           const auto rq = chunk_rsrc(qg, chunk, 0);
           const auto rv = chunk_rsrc(vg, chunk, v0);
 #pragma unroll
@@ -1585,20 +1597,24 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           if constexpr (GATED)
             buf_load(buf_rsrc(a.log_g + tok0 + tok, (long long)(T - tok) * 4), (unsigned)(lane * 4), b.lgv);
         };
-        // a of rows 16 PW + li of `chunk` (zero past T) and the strictly
-        // lower a_r G_rc of the block's Gram matrix, stored transposed for
-        // the solvers' column-parallel forward substitution
+        // a of rows 16 b + li of `chunk` (zero past T) and the strictly
+        // lower a_r G_rc of the Gram matrix of each of this loader's blocks
+        // b, stored transposed for the solvers' column-parallel forward
+        // substitution
         auto gate_gram = [&](LB& b, int chunk, float* alpha) {
+#pragma unroll
+         for (int i = 0; i < NBL; ++i) {
+          const int blk = PW + NLW * i;
           float lam = 0.f;
 #pragma unroll
-          for (int f = 0; f < NKB; ++f) lam += sumsq(b.kb[f]);
+          for (int f = 0; f < NKB; ++f) lam += sumsq(b.kb[i][f]);
           lam = xor32_sum(xor16_sum(lam));
-          const int row = 16 * PW + li0;
-          const float al = row < min(C, T - chunk * C) ? gate_coef(a.coef, to_f32(b.kbeta), lam) : 0.f;
+          const int row = 16 * blk + li0;
+          const float al = row < min(C, T - chunk * C) ? gate_coef(a.coef, to_f32(b.kbeta[i]), lam) : 0.f;
           if (g0 == 0) alpha[row] = al;
           floatx4 dg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, b.kb[f], b.kb[f]);
+          for (int f = 0; f < NKB; ++f) dg = MM::mma(dg, b.kb[i][f], b.kb[i][f]);
           if constexpr (GATED) {
             // b over the chunk's rows (lane l: row l; rows past T add 0),
             // this block's rows of [b | Gamma | Gamma_C / Gamma] into the
@@ -1619,8 +1635,9 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
             for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = al * de[e];
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Adt[PW][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
+            for (int e = 0; e < 4; ++e) sm.Adt[blk][4 * g0 + e][li0] = (4 * g0 + e < li0) ? al * dg[e] : 0.f;
           }
+         }
         };
         // one chunk step: cur holds chunk n = c + 1, nxt holds chunk n + 1
         auto step = [&](int c, LB& cur, LB& nxt) {
@@ -1649,10 +1666,12 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
           //      column-permuted)
           if (act) {
 #pragma unroll
-            for (int f = 0; f < NKB; ++f) {
-              if constexpr (SROWP) *(Vec*)&B.K[16 * PW + li][32 * f + 8 * g] = cur.kb[f];
-              else st_perm(&B.K[16 * PW + li][0], 32 * f + 8 * g, cur.kb[f]);
-            }
+            for (int i = 0; i < NBL; ++i)
+#pragma unroll
+              for (int f = 0; f < NKB; ++f) {
+                if constexpr (SROWP) *(Vec*)&B.K[16 * (PW + NLW * i) + li][32 * f + 8 * g] = cur.kb[i][f];
+                else st_perm(&B.K[16 * (PW + NLW * i) + li][0], 32 * f + 8 * g, cur.kb[i][f]);
+              }
 #pragma unroll
             for (int j = 0; j < NLK; ++j) {
               const int idx = lt + NLT * j;
