@@ -1931,7 +1931,15 @@ static SegPlan seg_plan(int NH, int T, int d, int C, bool pipelined) {
   const long long W = (long long)NH * (d / (d < 64 ? d : 64));  // workgroups of one pass
   const int nchunks = (T + C - 1) / C;
   if (W >= 128 || nchunks < 64) return p;
-  const long long G = std::min<long long>(256 / W + 1, nchunks / 32);  // segments of >= 32 chunks
+  // Segments of >= 8 chunks (measured on fp32_d64, 32 heads x 128 chunks of
+  // 16 tokens: at least 32 chunks per segment gave 4 segments and 162.7 us,
+  // at least 16 gave 8 and 95 us, at least 8 gave 9 and 89.5 us), and at
+  // most sqrt(nchunks) + 1 of them: the two big launches take about
+  // 2 nchunks / G chunk steps, the carry G steps of its own (each about
+  // 1.5 chunk steps), which this bound balances for very few heads.
+  long long rt = 1;
+  while ((rt + 1) * (rt + 1) <= nchunks) ++rt;
+  const long long G = std::min<long long>(std::min<long long>(256 / W + 1, nchunks / 8), rt + 1);
   if (G < 2) return p;
   const int cps = (int)((nchunks + G - 1) / G);  // chunks per segment
   p.seg_len = cps * C;

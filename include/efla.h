@@ -94,7 +94,8 @@ typedef EFLA_ENUM(efla_status_e) {
  * Bytes of device workspace efla_fwd_chunked needs for these sizes. It is 0
  * when one pass over the sequence fills the GPU. For few heads and long
  * sequences (fewer than 128 workgroups of 64 state columns, and at least 64
- * chunks; segments of at least 32 chunks) the forward runs over nseg time
+ * chunks; segments of at least 8 chunks, at most sqrt(chunks) + 1 of
+ * them) the forward runs over nseg time
  * segments: the first segment from S0 beside the affine maps S -> P S + R of
  * segments 1 .. nseg - 2, then their composition, then every later segment
  * from its true start state (the chunk recurrence is affine in S, section

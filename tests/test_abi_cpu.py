@@ -107,9 +107,16 @@ def test_workspace_query():
     nseg = 9
     assert lib.efla_fwd_chunked_workspace_bytes(1, 16, 65536, 128, 128, 64, 1) == \
         16 * (2 * (nseg - 2) + nseg) * 128 * 128 * 4
-    # two segments: no maps, only the start states
+    # 2 heads x 2 slices = 4 workgroups: up to 65 segments fill the GPU, but
+    # segments are at least 8 chunks long, so 65 chunks give 8 segments of 9
+    # chunks (the last one 2); maps of segments 1 .. 6 and 8 start states
+    nseg = 8
     assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4133, 128, 128, 64, 1) == \
-        2 * 2 * 128 * 128 * 4
+        2 * (2 * (nseg - 2) + nseg) * 128 * 128 * 4
+    # 64 chunks, the shortest sequence that takes segments: 8 of 8 chunks
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4096, 128, 128, 64, 1) == \
+        2 * (2 * (nseg - 2) + nseg) * 128 * 128 * 4
+    assert lib.efla_fwd_chunked_workspace_bytes(1, 2, 4032, 128, 128, 64, 1) == 0  # 63 chunks
     # fp32 with chunk 64 runs (and plans its segments) with chunk 16 when one
     # pass would leave the GPU idle (< 128 workgroups), else with chunk 32
     for d in (16, 64, 128):
