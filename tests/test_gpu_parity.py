@@ -119,7 +119,8 @@ def test_fp32_fallback_slices(efla, d, B, H):
 # bound: 33 segments of 32 chunks with a last segment of one chunk (bf16), and
 # 36 segments of 35 sixteen-token chunks (fp32).
 SEG_CASES = [("bf16", 128, 64, 1, 2, 8229), ("bf16", 64, 32, 1, 3, 4000), ("f32", 32, 16, 1, 2, 3000),
-             ("bf16", 16, 16, 2, 1, 2100), ("bf16", 64, 64, 1, 1, 65600), ("f32", 32, 16, 1, 1, 20000)]
+             ("bf16", 16, 16, 2, 1, 2100), ("bf16", 64, 64, 1, 1, 65600), ("f32", 32, 16, 1, 1, 20000),
+             ("bf16", 32, 64, 1, 2, 9000)]
 
 
 @pytest.mark.parametrize("dt,d,c,B,H,T", SEG_CASES)
