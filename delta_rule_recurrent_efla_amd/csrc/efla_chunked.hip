@@ -758,13 +758,13 @@ __device__ __forceinline__ void pipe_body(const ChunkedArgs& a, PipeSmem<CT, D, 
   // register that keeps the pass without spills.
   constexpr bool SROWP = sizeof(CT) == 2 && D >= 32 && !SAVE;
 #define skey(r) (SROWP ? MM::pcol(r) : (r))
-  // Where the chunk has four 16-row blocks and four loaders (bf16, C = 64,
-  // every pass mode but the summaries), loader L fetches the key rows of
-  // block L straight into MFMA operand layout. It then forms, one chunk
-  // ahead, the gate of those rows and the diagonal Gram block
-  // a_r (K_L K_L^T)_{rc}, c < r, and leaves it in LDS: the solvers' phase A
-  // starts at the forward substitution, with no key fetch, no Gram product
-  // and no LDS round trip of their own.
+  // Where the chunk has four 16-row blocks (bf16, C = 64, d >= 32), each
+  // loader fetches the key rows of its blocks straight into MFMA operand
+  // layout: block L for loader L of the four, blocks L and L + 2 for the
+  // summaries' two loaders. It then forms, one chunk ahead, the gate of those
+  // rows and the diagonal Gram blocks a_r (K_b K_b^T)_{rc}, c < r, and leaves
+  // them in LDS: the solvers' phase A starts at the forward substitution,
+  // with no key fetch, no Gram product and no LDS round trip of their own.
   constexpr bool LGRAM = sizeof(CT) == 2 && NB == 4 && D >= 32;
   // With four 16-row blocks and outputs, the solvers form row block 3 of
   // M = tril(Q K^T): their key fragments of blocks 0..3 are in registers
